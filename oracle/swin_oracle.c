@@ -1,0 +1,332 @@
+/*
+ * swin_oracle.c -- fp64 CPU oracle for shifted-window multi-head attention.
+ *
+ * TEST INFRASTRUCTURE ONLY (see swin_oracle.h): used by the tests, the smoke
+ * check and the CPU baseline of the benchmark, never by the product path.
+ *
+ * Every step is written as its plain definition, in the order the pages give
+ * the operations of a Swin block (NVIDIA talk "Swin Transformer training and
+ * inference optimization", section 1: window shift / partition / reverse,
+ * then attention): shift by a cyclic roll, cut into windows, attention inside
+ * each window with the relative position bias and the shift mask added to
+ * the scores, reverse the partition, roll back.  Nothing is fused or
+ * reordered; the attention is two plain triple loops around a softmax.
+ */
+#include "swin_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+static long mod_l(long a, long m) {
+  long r = a % m;
+  return r < 0 ? r + m : r;
+}
+
+/* torch.roll semantics: the element at i moves to (i + shift) mod H */
+void oracle_roll(const double* x, int B, int H, int W, int C, int sy, int sx, double* y) {
+  for (long b = 0; b < B; ++b)
+    for (long i = 0; i < H; ++i)
+      for (long j = 0; j < W; ++j) {
+        long yi = mod_l(i + sy, H), yj = mod_l(j + sx, W);
+        const double* src = x + ((b * H + i) * W + j) * (long)C;
+        double* dst = y + ((b * H + yi) * W + yj) * (long)C;
+        memcpy(dst, src, sizeof(double) * (size_t)C);
+      }
+}
+
+/* cut [B][H][W][C] into non-overlapping M x M windows, windows in row-major
+ * order over the image, tokens in row-major order inside a window */
+void oracle_window_partition(const double* x, int B, int H, int W, int C, int M, double* win) {
+  long nWy = H / M, nWx = W / M, N = (long)M * M;
+  for (long b = 0; b < B; ++b)
+    for (long wy = 0; wy < nWy; ++wy)
+      for (long wx = 0; wx < nWx; ++wx)
+        for (long ty = 0; ty < M; ++ty)
+          for (long tx = 0; tx < M; ++tx) {
+            long n = (b * nWy + wy) * nWx + wx, t = ty * M + tx;
+            const double* src = x + ((b * H + wy * M + ty) * W + wx * M + tx) * (long)C;
+            memcpy(win + (n * N + t) * (long)C, src, sizeof(double) * (size_t)C);
+          }
+}
+
+/* put window tokens back at their image positions (inverse of the above) */
+void oracle_window_reverse(const double* win, int B, int H, int W, int C, int M, double* x) {
+  long nWy = H / M, nWx = W / M, N = (long)M * M;
+  for (long b = 0; b < B; ++b)
+    for (long wy = 0; wy < nWy; ++wy)
+      for (long wx = 0; wx < nWx; ++wx)
+        for (long ty = 0; ty < M; ++ty)
+          for (long tx = 0; tx < M; ++tx) {
+            long n = (b * nWy + wy) * nWx + wx, t = ty * M + tx;
+            double* dst = x + ((b * H + wy * M + ty) * W + wx * M + tx) * (long)C;
+            memcpy(dst, win + (n * N + t) * (long)C, sizeof(double) * (size_t)C);
+          }
+}
+
+/* relative position of query i to key j, (dy, dx) = (y_i - y_j, x_i - x_j),
+ * each in [-(M-1), M-1], shifted to be non-negative and flattened row-major
+ * over a (2M-1) x (2M-1) table */
+void oracle_rel_index(int M, int32_t* idx) {
+  int N = M * M;
+  for (int i = 0; i < N; ++i)
+    for (int j = 0; j < N; ++j) {
+      int dy = i / M - j / M, dx = i % M - j % M;
+      idx[i * N + j] = (dy + M - 1) * (2 * M - 1) + (dx + M - 1);
+    }
+}
+
+static int band(int p, int L, int M, int s) {
+  if (p < L - M) return 0;
+  if (p < L - s) return 1;
+  return 2;
+}
+
+/* label every position of the shifted frame by the region it came from:
+ * after the roll, the last M rows hold two strips that were not adjacent in
+ * the image (the wrapped-around strip of s rows and the M-s rows before it);
+ * likewise for columns */
+void oracle_region_labels(int H, int W, int M, int s, int32_t* lab) {
+  for (int y = 0; y < H; ++y)
+    for (int x = 0; x < W; ++x)
+      lab[y * W + x] = s > 0 ? 3 * band(y, H, M, s) + band(x, W, M, s) : 0;
+}
+
+void oracle_shift_mask(int H, int W, int M, int s, double* mask) {
+  int N = M * M;
+  long nW = (long)(H / M) * (W / M);
+  int32_t* lab = (int32_t*)malloc(sizeof(int32_t) * (size_t)H * W);
+  double* labd = (double*)malloc(sizeof(double) * (size_t)H * W);
+  double* labw = (double*)malloc(sizeof(double) * (size_t)H * W);
+  oracle_region_labels(H, W, M, s, lab);
+  for (long k = 0; k < (long)H * W; ++k) labd[k] = lab[k];
+  /* partition the label image exactly like the features */
+  oracle_window_partition(labd, 1, H, W, 1, M, labw);
+  for (long w = 0; w < nW; ++w)
+    for (int i = 0; i < N; ++i)
+      for (int j = 0; j < N; ++j)
+        mask[(w * N + i) * N + j] = labw[w * N + i] == labw[w * N + j] ? 0.0 : -100.0;
+  free(lab);
+  free(labd);
+  free(labw);
+}
+
+/* ---------------------------------------------------------------------- */
+/* attention inside one window                                              */
+
+typedef struct {
+  const double* win_qkv;
+  const float* table;
+  const double* mask;
+  const int32_t* rel;
+  long nWin, begin, end;
+  int nW, M, nh, d, npad;
+  double* win_out;
+} attn_job;
+
+/* one window, every head: S = Q K^T * (1/sqrt d) + bias + mask, row softmax,
+ * O = P V.  Padded tokens (index >= N) are zero; padded keys score -inf. */
+static void attend_window(const attn_job* J, long n, double* q, double* k, double* v, double* S,
+                          double* P) {
+  const int M = J->M, N = M * M, nh = J->nh, d = J->d, Np = J->npad;
+  const long C = (long)nh * d;
+  const double scale = 1.0 / sqrt((double)d);
+  const double* base = J->win_qkv + n * N * 3 * C;
+  const double* mk = J->mask ? J->mask + (n % J->nW) * (long)N * N : NULL;
+  for (int h = 0; h < nh; ++h) {
+    for (int t = 0; t < Np; ++t)
+      for (int e = 0; e < d; ++e) {
+        int in = t < N;
+        q[t * d + e] = in ? base[(t * 3 + 0) * C + h * d + e] : 0.0;
+        k[t * d + e] = in ? base[(t * 3 + 1) * C + h * d + e] : 0.0;
+        v[t * d + e] = in ? base[(t * 3 + 2) * C + h * d + e] : 0.0;
+      }
+    for (int i = 0; i < Np; ++i)
+      for (int j = 0; j < Np; ++j) {
+        if (j >= N) {
+          S[i * Np + j] = -INFINITY;
+          continue;
+        }
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e) dot += q[i * d + e] * k[j * d + e];
+        double sc = dot * scale;
+        if (i < N) {
+          sc += (double)J->table[(long)J->rel[i * N + j] * nh + h];
+          if (mk) sc += mk[i * N + j];
+        }
+        S[i * Np + j] = sc;
+      }
+    for (int i = 0; i < Np; ++i) {
+      double m = -INFINITY;
+      for (int j = 0; j < Np; ++j) m = S[i * Np + j] > m ? S[i * Np + j] : m;
+      double sum = 0.0;
+      for (int j = 0; j < Np; ++j) {
+        P[i * Np + j] = exp(S[i * Np + j] - m);
+        sum += P[i * Np + j];
+      }
+      for (int j = 0; j < Np; ++j) P[i * Np + j] /= sum;
+    }
+    for (int i = 0; i < N; ++i)
+      for (int e = 0; e < d; ++e) {
+        double acc = 0.0;
+        for (int j = 0; j < Np; ++j) acc += P[i * Np + j] * v[j * d + e];
+        J->win_out[(n * N + i) * C + h * d + e] = acc;
+      }
+  }
+}
+
+static void* attn_worker(void* arg) {
+  const attn_job* J = (const attn_job*)arg;
+  const int Np = J->npad, d = J->d;
+  double* q = (double*)malloc(sizeof(double) * (size_t)Np * d);
+  double* k = (double*)malloc(sizeof(double) * (size_t)Np * d);
+  double* v = (double*)malloc(sizeof(double) * (size_t)Np * d);
+  double* S = (double*)malloc(sizeof(double) * (size_t)Np * Np);
+  double* P = (double*)malloc(sizeof(double) * (size_t)Np * Np);
+  for (long n = J->begin; n < J->end; ++n) attend_window(J, n, q, k, v, S, P);
+  free(q);
+  free(k);
+  free(v);
+  free(S);
+  free(P);
+  return NULL;
+}
+
+static int resolve_threads(int nthreads, long work) {
+  if (nthreads <= 0) {
+    long c = sysconf(_SC_NPROCESSORS_ONLN);
+    nthreads = c > 0 ? (int)c : 1;
+  }
+  if (nthreads > work) nthreads = work > 0 ? (int)work : 1;
+  return nthreads;
+}
+
+int oracle_window_attention(const double* win_qkv, const float* table, const double* mask,
+                            long nWin, int nW, int M, int nh, int d, int npad, int nthreads,
+                            double* win_out) {
+  const int N = M * M;
+  if (npad < N) npad = N;
+  int32_t* rel = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * N);
+  oracle_rel_index(M, rel);
+  nthreads = resolve_threads(nthreads, nWin);
+  attn_job* jobs = (attn_job*)calloc((size_t)nthreads, sizeof(attn_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int t = 0; t < nthreads; ++t) {
+    attn_job* J = &jobs[t];
+    J->win_qkv = win_qkv;
+    J->table = table;
+    J->mask = mask;
+    J->rel = rel;
+    J->nWin = nWin;
+    J->begin = nWin * t / nthreads;
+    J->end = nWin * (t + 1) / nthreads;
+    J->nW = nW;
+    J->M = M;
+    J->nh = nh;
+    J->d = d;
+    J->npad = npad;
+    J->win_out = win_out;
+    if (t > 0) pthread_create(&th[t], NULL, attn_worker, J);
+  }
+  attn_worker(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+  free(rel);
+  return nthreads;
+}
+
+/* ---------------------------------------------------------------------- */
+
+static double load_elem(const void* p, int dtype, long i) {
+  if (dtype == ORACLE_F32) return (double)((const float*)p)[i];
+  if (dtype == ORACLE_BF16) {
+    /* a bf16 pattern is the upper half of the fp32 with the same value */
+    uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+  }
+  return ((const double*)p)[i];
+}
+
+static int bad_args(int B, int H, int W, int nh, int d, int M, int s, int dtype) {
+  return B < 0 || H <= 0 || W <= 0 || nh <= 0 || d <= 0 || M <= 0 || H % M || W % M || s < 0 ||
+         s >= M || dtype < ORACLE_F64 || dtype > ORACLE_BF16;
+}
+
+int oracle_swin_wattn_fwd(const void* qkv, int dtype, const float* table, int B, int H, int W,
+                          int nh, int d, int M, int s, int npad, int nthreads, double* out) {
+  if (bad_args(B, H, W, nh, d, M, s, dtype)) return -1;
+  const long C = (long)nh * d, C3 = 3 * C, HW = (long)H * W;
+  const long N = (long)M * M, nW = (long)(H / M) * (W / M), nWin = (long)B * nW;
+  double* x = (double*)malloc(sizeof(double) * (size_t)(B * HW * C3));
+  double* xr = (double*)malloc(sizeof(double) * (size_t)(B * HW * C3));
+  for (long i = 0; i < B * HW * C3; ++i) x[i] = load_elem(qkv, dtype, i);
+  /* 1. cyclic shift towards the top-left */
+  oracle_roll(x, B, H, W, (int)C3, -s, -s, xr);
+  /* 2. window partition */
+  oracle_window_partition(xr, B, H, W, (int)C3, M, x);
+  free(xr);
+  /* 3. attention inside every window, mask only for shifted windows */
+  double* mask = NULL;
+  if (s > 0) {
+    mask = (double*)malloc(sizeof(double) * (size_t)(nW * N * N));
+    oracle_shift_mask(H, W, M, s, mask);
+  }
+  double* wo = (double*)malloc(sizeof(double) * (size_t)(B * HW * C));
+  int used = oracle_window_attention(x, table, mask, nWin, (int)nW, M, nh, d, npad, nthreads, wo);
+  free(x);
+  free(mask);
+  /* 4. window reverse, 5. roll back */
+  double* o = (double*)malloc(sizeof(double) * (size_t)(B * HW * C));
+  oracle_window_reverse(wo, B, H, W, (int)C, M, o);
+  oracle_roll(o, B, H, W, (int)C, s, s, out);
+  free(wo);
+  free(o);
+  return used;
+}
+
+int oracle_swin_wattn_windows(const void* qkv, int dtype, const float* table, int B, int H,
+                              int W, int nh, int d, int M, int s, long nsel, const int64_t* sel,
+                              int nthreads, double* out, int64_t* pos) {
+  if (bad_args(B, H, W, nh, d, M, s, dtype)) return -1;
+  const long C = (long)nh * d, C3 = 3 * C, N = (long)M * M;
+  const long nWx = W / M, nW = (long)(H / M) * nWx;
+  for (long k = 0; k < nsel; ++k)
+    if (sel[k] < 0 || sel[k] >= (long)B * nW) return -1;
+  /* gather the selected windows: token t of window w sits at (wy*M+ty,
+   * wx*M+tx) of the frame rolled by (-s,-s), whose position p holds the
+   * image position (p + s) mod H -- the two index maps of steps 1 and 2 */
+  double* win = (double*)malloc(sizeof(double) * (size_t)(nsel * N * C3));
+  for (long k = 0; k < nsel; ++k) {
+    long b = sel[k] / nW, w = sel[k] % nW, wy = w / nWx, wx = w % nWx;
+    for (long t = 0; t < N; ++t) {
+      long yr = wy * M + t / M, xr = wx * M + t % M;
+      long y = mod_l(yr + s, H), x = mod_l(xr + s, W);
+      long p = (b * H + y) * W + x;
+      pos[k * N + t] = p;
+      for (long c = 0; c < C3; ++c) win[(k * N + t) * C3 + c] = load_elem(qkv, dtype, p * C3 + c);
+    }
+  }
+  double* mask = NULL;
+  if (s > 0) {
+    mask = (double*)malloc(sizeof(double) * (size_t)(nW * N * N));
+    oracle_shift_mask(H, W, M, s, mask);
+  }
+  /* attention with each selected window's own mask slice */
+  double* msel = NULL;
+  if (mask) {
+    msel = (double*)malloc(sizeof(double) * (size_t)(nsel * N * N));
+    for (long k = 0; k < nsel; ++k)
+      memcpy(msel + k * N * N, mask + (sel[k] % nW) * N * N, sizeof(double) * (size_t)(N * N));
+  }
+  int used = oracle_window_attention(win, table, msel, nsel, (int)(nsel > 0 ? nsel : 1), M, nh, d,
+                                     (int)N, nthreads, out);
+  free(win);
+  free(mask);
+  free(msel);
+  return used;
+}

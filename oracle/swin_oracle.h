@@ -1,0 +1,99 @@
+/*
+ * swin_oracle.h -- plain, slow, fp64 CPU oracle for shifted-window
+ * multi-head attention (Swin Transformer window attention with cyclic shift).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this library: only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no code, header, table or
+ * constant with the HIP implementation.
+ *
+ * What it computes, and where the pages state it:
+ *  - NVIDIA talk "Swin Transformer training and inference optimization"
+ *    (uticex.com article 1598), section 1 "Swin Transformer introduction":
+ *    attention is taken only among the patches of one window; a window shift
+ *    fixes the window-boundary problem; a relative position bias is added
+ *    inside attention; query and key through softmax give the attention map
+ *    that weights value; several heads form multi-head attention; a block is
+ *    window shift/partition/reverse, then attention, then FFN.
+ *  - same talk, section 2 "training optimization": the window shift is a roll,
+ *    the partition/shift/merge operations are pure index mapping, and the
+ *    fused attention receives the mask and the bias as tensors.
+ *  - same talk, section 3 "inference optimization": the position-bias lookup
+ *    is moved to preprocessing; batch GEMM, softmax, batch GEMM form the
+ *    attention.
+ *  - Baidu AIAK-Training talk (jxzklqfsx.com article 743345), section 2,
+ *    WindowAttention fusion case: two matrix products and a softmax.
+ * The formula figure of the WindowAttention case did not survive extraction;
+ * the oracle takes softmax(Q K^T / sqrt(d) + bias + mask) V, and every other
+ * reading where the pages are silent is listed in the design doc.
+ *
+ * Conventions (all arrays dense, row-major, no padding):
+ *   image tensors  [B][H][W][Cx]
+ *   qkv            [B][H][W][3][nh][d]     (0 = query, 1 = key, 2 = value)
+ *   table          [(2M-1)^2][nh]          relative position bias, fp32
+ *   rel_index      [N][N], N = M*M         int32
+ *   mask           [nW][N][N]              0 or -100 (natural-log units)
+ *   windows        [B][nWy][nWx][N][Cx]    token t = ty*M + tx in a window
+ *   out            [B][H][W][nh*d]
+ */
+#ifndef SWIN_ORACLE_H
+#define SWIN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type codes of the qkv input accepted by the forward functions */
+enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_BF16 = 2 /* raw 16-bit patterns */ };
+
+/* cyclic roll with torch.roll semantics on dims (1,2) of [B][H][W][C]:
+ * y[b][(i+sy) mod H][(j+sx) mod W][c] = x[b][i][j][c] */
+void oracle_roll(const double* x, int B, int H, int W, int C, int sy, int sx, double* y);
+
+/* window partition: win[b][wy][wx][ty*M+tx][c] = x[b][wy*M+ty][wx*M+tx][c] */
+void oracle_window_partition(const double* x, int B, int H, int W, int C, int M, double* win);
+
+/* window reverse, the inverse map of oracle_window_partition */
+void oracle_window_reverse(const double* win, int B, int H, int W, int C, int M, double* x);
+
+/* relative position index of query i and key j inside an M x M window */
+void oracle_rel_index(int M, int32_t* idx);
+
+/* region label image [H][W] of the shifted frame: three bands per axis,
+ * [0,H-M), [H-M,H-s), [H-s,H); label = 3*band_y + band_x; all zero if s == 0 */
+void oracle_region_labels(int H, int W, int M, int s, int32_t* lab);
+
+/* shifted-window mask [nW][N][N]: 0 where query and key carry the same
+ * region label, -100 elsewhere (all zero when s == 0) */
+void oracle_shift_mask(int H, int W, int M, int s, double* mask);
+
+/* attention inside windows.  win_qkv [nWin][N][3][nh][d]; window n uses
+ * mask[n mod nW] (mask may be NULL = no mask).  npad >= N pads every window
+ * to npad tokens: padded keys get score -inf, padded tokens are zero and
+ * padded query rows are dropped.  win_out [nWin][N][nh*d].
+ * nthreads <= 0 uses every online CPU.  Returns the thread count used. */
+int oracle_window_attention(const double* win_qkv, const float* table, const double* mask,
+                            long nWin, int nW, int M, int nh, int d, int npad, int nthreads,
+                            double* win_out);
+
+/* the whole forward: roll(-s,-s) -> partition -> window attention with bias
+ * and mask -> reverse -> roll(+s,+s).  qkv of type dtype, out fp64
+ * [B][H][W][nh*d].  Returns the thread count used, or -1 on bad arguments. */
+int oracle_swin_wattn_fwd(const void* qkv, int dtype, const float* table, int B, int H, int W,
+                          int nh, int d, int M, int s, int npad, int nthreads, double* out);
+
+/* the same forward restricted to selected windows, for spot checks at sizes
+ * too large for the whole forward.  sel[k] = b*nW + w.  out [nsel][N][nh*d]
+ * in window token order; pos[k*N+t] = (b*H + y)*W + x is the image position
+ * that token t of window sel[k] is read from and written back to.
+ * Returns the thread count used, or -1 on bad arguments. */
+int oracle_swin_wattn_windows(const void* qkv, int dtype, const float* table, int B, int H,
+                              int W, int nh, int d, int M, int s, long nsel, const int64_t* sel,
+                              int nthreads, double* out, int64_t* pos);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs shared by the oracle side and the HIP side.
+
+This module holds no step of the attention method: it only draws numbers.
+Both sides of every parity check read the very same arrays produced here.
+
+Generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014) used in counter form -- draw k of a stream is
+the SplitMix64 output for state ``key + (k+1) * golden`` -- so any slice of a
+stream can be produced independently.  Uniforms take the top 53 bits; normals
+come from the Box-Muller transform (Box and Muller, 1958), one pair of normals
+per pair of uniforms, computed in float64, scaled by the std, then rounded to
+float32 (and, for bfloat16 tensors, rounded again to nearest-even bfloat16).
+
+Workload shapes are Swin stage shapes: qkv ``[B, H, W, 3, heads, head_dim]``
+~ N(0, 1) and a relative position bias table ``[(2M-1)^2, heads]`` ~ N(0, 0.02).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_CHUNK = 1 << 22
+
+
+def _mix(z: np.ndarray) -> np.ndarray:
+    z = (z ^ (z >> np.uint64(30))) * _M1
+    z = (z ^ (z >> np.uint64(27))) * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def stream_key(seed: int, stream: int) -> int:
+    """Independent 64-bit key for sub-stream ``stream`` of ``seed``."""
+    z = np.array([(seed * 0x100000001B3 + stream) & 0xFFFFFFFFFFFFFFFF], dtype=np.uint64)
+    return int(_mix(z + _GOLDEN)[0])
+
+
+def splitmix64(key: int, start: int, n: int) -> np.ndarray:
+    """Draws ``start .. start+n-1`` of the SplitMix64 stream with state ``key``."""
+    k = np.arange(start + 1, start + n + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return _mix(np.uint64(key) + k * _GOLDEN)
+
+
+def uniform53(key: int, start: int, n: int) -> np.ndarray:
+    """Uniform doubles in [0, 1) from the top 53 bits of each draw."""
+    return (splitmix64(key, start, n) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+def normal(key: int, n: int, std: float = 1.0) -> np.ndarray:
+    """``n`` normal float32 values; normal 2p and 2p+1 use draws 2p and 2p+1."""
+    out = np.empty(n, dtype=np.float32)
+    pairs = (n + 1) // 2
+    for p0 in range(0, pairs, _CHUNK):
+        p1 = min(pairs, p0 + _CHUNK)
+        u = uniform53(key, 2 * p0, 2 * (p1 - p0))
+        u1 = 1.0 - u[0::2]  # (0, 1]: keeps the log finite
+        u2 = u[1::2]
+        r = np.sqrt(-2.0 * np.log(u1))
+        z = np.empty(2 * (p1 - p0), dtype=np.float64)
+        z[0::2] = r * np.cos(2.0 * np.pi * u2)
+        z[1::2] = r * np.sin(2.0 * np.pi * u2)
+        lo, hi = 2 * p0, min(n, 2 * p1)
+        out[lo:hi] = (z[: hi - lo] * std).astype(np.float32)
+    return out
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to nearest-even bfloat16; returns the 16-bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 value of bfloat16 patterns."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Workloads: Swin stage shapes.  Each carries its own seed.
+
+WORKLOADS = {
+    "tiny-f32": dict(B=1, H=14, W=14, heads=2, head_dim=32, window=7, shifts=(3,), dtype="f32",
+                     seed=1001, desc="tiny fp32 check, 14x14 tokens, window 7, shift 3"),
+    "swin-t-s1": dict(B=32, H=56, W=56, heads=3, head_dim=32, window=7, shifts=(3,), dtype="bf16",
+                      seed=1002, desc="Swin-T stage 1, B=32, 56x56, C=96"),
+    "swin-t-s3": dict(B=64, H=14, W=14, heads=12, head_dim=32, window=7, shifts=(0, 3), dtype="bf16",
+                      seed=1003, desc="Swin-T stage 3, B=64, 14x14, C=384, shift 0 and 3"),
+    "swin-l-s1": dict(B=64, H=56, W=56, heads=6, head_dim=32, window=7, shifts=(3,), dtype="bf16",
+                      seed=1004, desc="Swin-L stage 1, B=64, 56x56, C=192"),
+    "swin-l-384": dict(B=16, H=96, W=96, heads=6, head_dim=32, window=12, shifts=(6,), dtype="bf16",
+                       seed=1005, desc="Swin-L at 384px, B=16, 96x96, C=192, window 12"),
+}
+
+
+def make_inputs(B: int, H: int, W: int, heads: int, head_dim: int, window: int, seed: int,
+                dtype: str = "bf16", qkv_std: float = 1.0, table_std: float = 0.02):
+    """Returns ``(qkv, table)`` as numpy arrays.
+
+    ``qkv`` is ``[B, H, W, 3, heads, head_dim]``: float32 values for ``dtype='f32'``,
+    uint16 bfloat16 patterns for ``dtype='bf16'``.  ``table`` is float32
+    ``[(2*window-1)**2, heads]``.
+    """
+    n = B * H * W * 3 * heads * head_dim
+    q = normal(stream_key(seed, 0), n, qkv_std).reshape(B, H, W, 3, heads, head_dim)
+    T = (2 * window - 1) ** 2
+    table = normal(stream_key(seed, 1), T * heads, table_std).reshape(T, heads)
+    if dtype == "bf16":
+        q = bf16_bits(q)
+    elif dtype != "f32":
+        raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
+    return q, table
+
+
+def workload_inputs(name: str, batch: int | None = None):
+    """Inputs of a named workload (optionally with a smaller batch)."""
+    w = WORKLOADS[name]
+    B = w["B"] if batch is None else batch
+    return make_inputs(B, w["H"], w["W"], w["heads"], w["head_dim"], w["window"], w["seed"],
+                       w["dtype"])

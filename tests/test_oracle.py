@@ -1,0 +1,317 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Every function of the oracle is checked against at least one of: a value
+worked out by hand from the definition (tests/golden), a closed form, a
+library routine that computes the same thing for a special case (torch.roll,
+a reshape, torch's scaled_dot_product_attention in float64), brute force on a
+tiny input, or an exact invariance.  Each test names the mistake it catches.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name, dtype=np.float64):
+    return np.loadtxt(os.path.join(GOLDEN, name), comments="#", dtype=dtype)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- index maps
+
+@pytest.mark.parametrize("shape,shifts", [((2, 6, 8, 3), [(1, 2), (-3, -3), (0, 5), (-7, 4)]),
+                                          ((1, 14, 14, 5), [(-3, -3), (3, 3)])])
+def test_roll_matches_torch_roll(oracle_lib, shape, shifts):
+    # catches a reversed shift direction or a wrong axis
+    x = _rng(1).standard_normal(shape)
+    for sy, sx in shifts:
+        ref = torch.roll(torch.from_numpy(x), shifts=(sy, sx), dims=(1, 2)).numpy()
+        assert np.array_equal(oracle.roll(x, sy, sx), ref)
+
+
+@pytest.mark.parametrize("B,H,W,C,M", [(2, 14, 21, 3, 7), (1, 24, 12, 2, 12), (3, 4, 4, 1, 2)])
+def test_partition_matches_reshape_and_reverses(oracle_lib, B, H, W, C, M):
+    # catches transposed window or token order
+    x = _rng(2).standard_normal((B, H, W, C))
+    ref = (torch.from_numpy(x).view(B, H // M, M, W // M, M, C).permute(0, 1, 3, 2, 4, 5)
+           .reshape(B, H // M, W // M, M * M, C).numpy())
+    win = oracle.window_partition(x, M)
+    assert np.array_equal(win, ref)
+    assert np.array_equal(oracle.window_reverse(win, H, W, M), x)
+
+
+def test_shift_then_partition_golden(oracle_lib):
+    # hand-worked 4x4 example: pins the shift direction of the whole gather
+    img = np.arange(16, dtype=np.float64).reshape(1, 4, 4, 1)
+    win = oracle.window_partition(oracle.roll(img, -1, -1), 2)
+    assert np.array_equal(win.reshape(4, 4), _golden("shift_partition_h4w4_m2_s1.txt"))
+
+
+def test_shift_and_reverse_roundtrip(oracle_lib):
+    x = _rng(3).standard_normal((2, 14, 14, 4))
+    for s in range(7):
+        back = oracle.roll(oracle.window_reverse(oracle.window_partition(oracle.roll(x, -s, -s), 7),
+                                                 14, 14, 7), s, s)
+        assert np.array_equal(back, x)
+
+
+# --------------------------------------------------------- relative position
+
+def test_rel_index_golden_m2(oracle_lib):
+    assert np.array_equal(oracle.rel_index(2), _golden("rel_index_m2.txt", np.int32))
+
+
+@pytest.mark.parametrize("M", range(1, 13))
+def test_rel_index_closed_forms(oracle_lib, M):
+    idx = oracle.rel_index(M)
+    N, T = M * M, (2 * M - 1) ** 2
+    assert idx.min() >= 0 and idx.max() <= T - 1
+    # the diagonal (zero offset) sits at the centre of the table: 84 for M=7, 264 for M=12
+    assert np.all(np.diag(idx) == (M - 1) * (2 * M - 1) + (M - 1))
+    # opposite offsets mirror through the centre
+    assert np.all(idx + idx.T == T - 1)
+    # every one of the (2M-1)^2 offsets appears, and only offsets decide the index
+    assert len(np.unique(idx)) == T
+    ty, tx = np.divmod(np.arange(N), M)
+    off = (ty[:, None] - ty[None, :]) * 100 + (tx[:, None] - tx[None, :])
+    pairs = set(zip(off.ravel().tolist(), idx.ravel().tolist()))
+    assert len(pairs) == T
+
+
+def test_rel_index_known_values(oracle_lib):
+    assert oracle.rel_index(7)[0, 0] == 84
+    assert oracle.rel_index(12)[0, 0] == 264
+    # query one row below the key: dy = +1, dx = 0
+    idx = oracle.rel_index(7)
+    assert idx[7, 0] == (1 + 6) * 13 + 6
+
+
+@pytest.mark.parametrize("M", [2, 7, 12])
+def test_rel_index_rank_one_difference(oracle_lib, M):
+    # idx[i][j] = idx[i][0] + idx[0][j] - idx[0][0]: the index is a difference
+    # of per-token codes, a structure the GPU kernel relies on
+    idx = oracle.rel_index(M).astype(np.int64)
+    assert np.array_equal(idx, idx[:, :1] + idx[:1, :] - idx[0, 0])
+
+
+# --------------------------------------------------------------------- mask
+
+def test_mask_golden_h4w4(oracle_lib):
+    m = oracle.shift_mask(4, 4, 2, 1)
+    assert np.array_equal(m.reshape(16, 4), _golden("shift_mask_h4w4_m2_s1.txt"))
+
+
+@pytest.mark.parametrize("H,W,M,s", [(56, 56, 7, 3), (14, 14, 7, 3), (96, 96, 12, 6),
+                                     (28, 14, 7, 2), (12, 24, 12, 5)])
+def test_mask_closed_form_counts(oracle_lib, H, W, M, s):
+    m = oracle.shift_mask(H, W, M, s)
+    nWy, nWx, N = H // M, W // M, M * M
+    assert set(np.unique(m).tolist()) <= {0.0, -100.0}
+    cnt = (m == -100.0).reshape(nWy, nWx, N * N).sum(-1)
+    edge = 2 * (M - s) * M * s * M
+    corner = N * N - ((M - s) ** 4 + 2 * (M - s) ** 2 * s ** 2 + s ** 4)
+    expect = np.zeros((nWy, nWx), dtype=np.int64)
+    expect[-1, :] = edge
+    expect[:, -1] = edge
+    expect[-1, -1] = corner
+    assert np.array_equal(cnt, expect)
+    if (M, s) == (7, 3):
+        assert (edge, corner) == (1176, 1776)
+    if (M, s) == (12, 6):
+        assert (edge, corner) == (10368, 15552)
+    # the mask is symmetric and never masks a token from itself
+    assert np.array_equal(m, m.transpose(0, 2, 1))
+    assert np.all(np.diagonal(m, axis1=1, axis2=2) == 0.0)
+
+
+def test_mask_zero_without_shift(oracle_lib):
+    assert np.all(oracle.shift_mask(56, 56, 7, 0) == 0.0)
+
+
+# --------------------------------------------------------------- attention
+
+def _torch_reference(qkv, table, M, s):
+    """Library composition in float64: torch.roll, reshape partition,
+    torch scaled_dot_product_attention with the additive bias+mask, reverse,
+    roll back.  Index and mask come from the separately pinned oracle maps."""
+    x = torch.from_numpy(np.asarray(qkv, dtype=np.float64))
+    B, H, W, _, nh, d = x.shape
+    N, nWy, nWx = M * M, H // M, W // M
+    xr = torch.roll(x, shifts=(-s, -s), dims=(1, 2))
+    win = xr.view(B, nWy, M, nWx, M, 3, nh, d).permute(0, 1, 3, 2, 4, 5, 6, 7)
+    win = win.reshape(B * nWy * nWx, N, 3, nh, d)
+    q, k, v = (win[:, :, i].permute(0, 2, 1, 3) for i in range(3))  # [nWin, nh, N, d]
+    idx = torch.from_numpy(oracle.rel_index(M).astype(np.int64))
+    bias = torch.from_numpy(np.asarray(table, dtype=np.float64))[idx]  # [N, N, nh]
+    bias = bias.permute(2, 0, 1)[None]  # [1, nh, N, N]
+    mask = torch.from_numpy(oracle.shift_mask(H, W, M, s)) if s > 0 else torch.zeros(1, N, N,
+                                                                                     dtype=torch.float64)
+    mask = mask.repeat(B, 1, 1)[:, None] if s > 0 else mask[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=bias + mask)
+    o = o.permute(0, 2, 1, 3).reshape(B, nWy, nWx, M, M, nh * d).permute(0, 1, 3, 2, 4, 5)
+    o = o.reshape(B, H, W, nh * d)
+    return torch.roll(o, shifts=(s, s), dims=(1, 2)).numpy()
+
+
+@pytest.mark.parametrize("B,H,W,nh,d,M,s", [(2, 14, 14, 2, 32, 7, 3), (1, 14, 28, 3, 16, 7, 0),
+                                            (1, 24, 24, 2, 32, 12, 6), (2, 8, 12, 1, 8, 4, 1)])
+def test_forward_matches_torch_sdpa_float64(oracle_lib, B, H, W, nh, d, M, s):
+    # catches a transposed operand, a missing scale, bias or mask, a wrong
+    # softmax axis, or a wrong scatter
+    q, table = synth.make_inputs(B, H, W, nh, d, M, seed=77, dtype="f32", table_std=0.5)
+    out = oracle.swin_wattn_fwd(q, table, M, s)
+    ref = _torch_reference(q, table, M, s)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("L,nh,d", [(7, 2, 32), (4, 1, 8), (14, 1, 4)])
+def test_window_equal_image_is_global_attention(oracle_lib, L, nh, d):
+    # brute force: one window covering the whole image, no shift, zero bias
+    rng = _rng(4)
+    q = rng.standard_normal((1, L, L, 3, nh, d))
+    table = np.zeros(((2 * L - 1) ** 2, nh), dtype=np.float32)
+    out = oracle.swin_wattn_fwd(q, table, L, 0)
+    tok = q.reshape(L * L, 3, nh, d)
+    ref = np.empty((L * L, nh, d))
+    for h in range(nh):
+        Q, K, V = tok[:, 0, h], tok[:, 1, h], tok[:, 2, h]
+        S = np.array([[sum(Q[i, e] * K[j, e] for e in range(d)) / math.sqrt(d)
+                       for j in range(L * L)] for i in range(L * L)])
+        P = np.exp(S - S.max(1, keepdims=True))
+        P /= P.sum(1, keepdims=True)
+        ref[:, h] = P @ V
+    assert np.max(np.abs(out.reshape(L * L, nh, d) - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("s", [0, 3])
+def test_softmax_rows_sum_to_one(oracle_lib, s):
+    # value = 1 everywhere: each output is the sum of one softmax row
+    q, table = synth.make_inputs(2, 14, 14, 2, 32, 7, seed=5, dtype="f32", table_std=1.0)
+    q = q.astype(np.float64)
+    q[:, :, :, 2] = 1.0
+    out = oracle.swin_wattn_fwd(q, table, 7, s)
+    assert np.max(np.abs(out - 1.0)) < 1e-12
+
+
+def test_uniform_attention_is_window_mean(oracle_lib):
+    # q = k = 0 and zero bias, no shift: every token gets the mean of v over its window
+    rng = _rng(6)
+    B, H, W, nh, d, M = 2, 14, 21, 2, 4, 7
+    q = np.zeros((B, H, W, 3, nh, d))
+    q[:, :, :, 2] = rng.standard_normal((B, H, W, nh, d))
+    table = np.zeros(((2 * M - 1) ** 2, nh), dtype=np.float32)
+    out = oracle.swin_wattn_fwd(q, table, M, 0).reshape(B, H, W, nh, d)
+    v = q[:, :, :, 2]
+    for y in range(H):
+        for x in range(W):
+            wy, wx = y // M, x // M
+            mean = v[:, wy * M:(wy + 1) * M, wx * M:(wx + 1) * M].mean(axis=(1, 2))
+            assert np.max(np.abs(out[:, y, x] - mean)) < 1e-12
+
+
+def test_uniform_attention_shifted_is_region_mean(oracle_lib):
+    # 4x4 image, window 2, shift 1, q = k = 0, zero bias: every token gets the
+    # mean of v over the tokens of its own window that share its region; the
+    # regions come from the hand-worked golden labels (masked weight e^-100)
+    rng = _rng(7)
+    v = rng.standard_normal((1, 4, 4, 1, 3))
+    q = np.zeros((1, 4, 4, 3, 1, 3))
+    q[:, :, :, 2] = v
+    table = np.zeros((9, 1), dtype=np.float32)
+    out = oracle.swin_wattn_fwd(q, table, 2, 1).reshape(4, 4, 3)
+    labels = np.array([[0, 0, 1, 2], [0, 0, 1, 2], [3, 3, 4, 5], [6, 6, 7, 8]])  # rolled frame
+    vr = np.roll(v.reshape(4, 4, 3), (-1, -1), (0, 1))  # value seen at each rolled position
+    for yr in range(4):
+        for xr in range(4):
+            wy, wx = yr // 2, xr // 2
+            members = [(a, b) for a in range(wy * 2, wy * 2 + 2) for b in range(wx * 2, wx * 2 + 2)
+                       if labels[a, b] == labels[yr, xr]]
+            mean = np.mean([vr[a, b] for a, b in members], axis=0)
+            y, x = (yr + 1) % 4, (xr + 1) % 4
+            assert np.max(np.abs(out[y, x] - mean)) < 1e-12
+
+
+def test_one_hot_bias_sign(oracle_lib):
+    # bias +50 only for offset (dy, dx) = (+1, 0) (query one row below the key):
+    # every query not in its window's first row copies the value one row above
+    rng = _rng(8)
+    B, H, W, nh, d, M = 1, 14, 14, 2, 4, 7
+    q = np.zeros((B, H, W, 3, nh, d))
+    q[:, :, :, 2] = rng.standard_normal((B, H, W, nh, d))
+    table = np.zeros(((2 * M - 1) ** 2, nh), dtype=np.float32)
+    table[(1 + M - 1) * (2 * M - 1) + (M - 1)] = 50.0
+    out = oracle.swin_wattn_fwd(q, table, M, 0).reshape(B, H, W, nh, d)
+    v = q[:, :, :, 2]
+    for y in range(H):
+        for x in range(W):
+            if y % M == 0:
+                continue
+            assert np.max(np.abs(out[:, y, x] - v[:, y - 1, x])) < 1e-12
+
+
+def test_linearity_in_value(oracle_lib):
+    q, table = synth.make_inputs(2, 14, 14, 2, 32, 7, seed=9, dtype="f32")
+    q2 = q.astype(np.float64).copy()
+    q2[:, :, :, 2] *= 2.0
+    assert np.array_equal(oracle.swin_wattn_fwd(q2, table, 7, 3), 2.0 * oracle.swin_wattn_fwd(q, table, 7, 3))
+
+
+def test_table_offset_invariance(oracle_lib):
+    q, table = synth.make_inputs(1, 14, 14, 2, 32, 7, seed=10, dtype="f32")
+    # table on a 2^-16 grid so that adding 0.5 is exact in float32
+    table = (np.round(table.astype(np.float64) * 2 ** 16) / 2 ** 16).astype(np.float32)
+    a = oracle.swin_wattn_fwd(q, table, 7, 3)
+    b = oracle.swin_wattn_fwd(q, table + np.float32(0.5), 7, 3)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+@pytest.mark.parametrize("M,npad", [(7, 64), (7, 56), (12, 160), (5, 32)])
+def test_padding_is_exact(oracle_lib, M, npad):
+    # padded keys score -inf, so their weights are exactly zero
+    q, table = synth.make_inputs(2, 2 * M, 3 * M, 2, 16, M, seed=11, dtype="bf16")
+    a = oracle.swin_wattn_fwd(q, table, M, M // 2)
+    b = oracle.swin_wattn_fwd(q, table, M, M // 2, npad=npad)
+    assert np.array_equal(a, b)
+
+
+def test_unshifted_roll_equivariance(oracle_lib):
+    q, table = synth.make_inputs(1, 21, 14, 2, 8, 7, seed=12, dtype="f32")
+    a = oracle.swin_wattn_fwd(q, table, 7, 0)
+    qr = np.roll(q, (7, 7), (1, 2))
+    b = oracle.swin_wattn_fwd(qr, table, 7, 0)
+    assert np.array_equal(np.roll(a, (7, 7), (1, 2)), b)
+
+
+def test_bf16_patterns_read_exactly(oracle_lib):
+    q, table = synth.make_inputs(1, 14, 14, 2, 32, 7, seed=13, dtype="bf16")
+    a = oracle.swin_wattn_fwd(q, table, 7, 3)
+    b = oracle.swin_wattn_fwd(synth.bf16_to_f32(q).astype(np.float64), table, 7, 3)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("B,H,W,nh,M,s", [(2, 14, 14, 2, 7, 3), (1, 24, 36, 3, 12, 6), (3, 14, 14, 1, 7, 0)])
+def test_selected_windows_equal_whole_forward(oracle_lib, B, H, W, nh, M, s):
+    q, table = synth.make_inputs(B, H, W, nh, 32, M, seed=14, dtype="bf16")
+    full = oracle.swin_wattn_fwd(q, table, M, s).reshape(B * H * W, -1)
+    nW = (H // M) * (W // M)
+    sel = np.arange(B * nW)[::-1].copy()
+    out, pos = oracle.swin_wattn_windows(q, table, M, s, sel)
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(B * H * W))
+    assert np.array_equal(out.reshape(-1, out.shape[-1]), full[pos.ravel()])
+
+
+def test_thread_count_does_not_change_result(oracle_lib):
+    q, table = synth.make_inputs(2, 14, 14, 2, 32, 7, seed=15, dtype="bf16")
+    a = oracle.swin_wattn_fwd(q, table, 7, 3, nthreads=1)
+    b = oracle.swin_wattn_fwd(q, table, 7, 3, nthreads=3)
+    assert np.array_equal(a, b)
