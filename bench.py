@@ -1,0 +1,188 @@
+"""Benchmark of the fused shifted-window attention forward on one MI355X.
+
+A step is one ``swin_wattn_fwd`` over the whole batch of the workload (default:
+Swin-L stage 1, B=64, 56x56 tokens, 6 heads x 32, window 7, shift 3, bf16)
+with inputs already resident in HBM.  Input/output buffer sets rotate so that
+the working set of the timed region exceeds twice the 256 MB Infinity Cache
+(cold cache).  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "shifted-window attn fwd GB/s & TFLOP/s (Swin-L stage1, bf16, B=64); % HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 * 2 ** 20
+KERNEL_SRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc", "wattn_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(B, H, W, heads, head_dim, window, elem=2):
+    """Bytes: qkv read once + out written once.  FLOPs: two contractions of
+    N x N x head_dim per window and head over the unpadded N."""
+    T = B * H * W
+    C = heads * head_dim
+    N = window * window
+    return 4 * C * T * elem, 4 * N * C * T
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"wattn_fwd_bf16_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50):
+    """The fp64 oracle on the first `sample_batch` images of the workload, on
+    every host core, repeated until about `min_seconds` of wall time; reported
+    in the metric's unit (GB/s of algorithmic bytes)."""
+    import oracle
+    import synth
+    w = synth.WORKLOADS[name]
+    qkv, table = synth.workload_inputs(name, batch=sample_batch)
+    reps, used = 0, 0
+    t0 = time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        _, used = oracle.swin_wattn_fwd(qkv, table, w["window"], w["shifts"][0], return_threads=True)
+        reps += 1
+    dt = time.perf_counter() - t0
+    nbytes, _ = algorithmic(sample_batch, w["H"], w["W"], w["heads"], w["head_dim"], w["window"])
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{name}, first {sample_batch} of {w['B']} images, whole forward x{reps} "
+                      f"({dt:.1f} s wall, fp64, {used} threads)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="swin-l-s1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-batch", type=int, default=64)
+    ap.add_argument("--hot", action="store_true", help="one buffer set (working set may sit in cache)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the forward shards by batch with no "
+              "communication, so there is no multi-GPU run to make (--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import shifted_window_attention_swin_amd as swa
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w["dtype"] != "bf16":
+        print("bench.py: the benchmark times the bf16 path", file=sys.stderr)
+        return 2
+    B, H, W, nh, d, M = w["B"], w["H"], w["W"], w["heads"], w["head_dim"], w["window"]
+    shifts = w["shifts"]
+    dev = torch.device("cuda:0")
+
+    qkv_np, table_np = synth.workload_inputs(args.workload)
+    q0 = torch.from_numpy(qkv_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    table = torch.from_numpy(table_np).to(dev)
+    del qkv_np
+    nbytes, nflops = algorithmic(B, H, W, nh, d, M)
+    nbytes *= len(shifts)
+    nflops *= len(shifts)
+    footprint = nbytes // len(shifts)
+    sets = 1 if args.hot else 2 * MALL_BYTES // footprint + 1  # sets * footprint > 2 x MALL
+    qs = [q0] + [q0.clone() for _ in range(sets - 1)]
+    outs = [torch.empty(B, H, W, nh * d, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+    for s in shifts:
+        swa.check(swa.swin_wattn_precompute(H, W, M, s, stream), "precompute")
+    torch.cuda.synchronize()
+
+    def step(i):
+        k = i % sets
+        for s in shifts:
+            swa.check(swa.swin_wattn_fwd(qs[k], table, outs[k], B, H, W, nh, d, M, s, stream), "fwd")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_launch_s = sum(launch_ms) / K / 1e3 / len(shifts)
+    ms_per_step = total_ms / K
+    value = nbytes * K / (total_ms / 1e3) / 1e9
+
+    achieved = (nbytes / len(shifts)) / avg_launch_s / 1e9
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, qkv ~ N(0,1), bias table ~ N(0,0.02))",
+        "config": {"workload": args.workload, "desc": w["desc"], "B": B, "H": H, "W": W, "heads": nh,
+                   "head_dim": d, "window": M, "shifts": list(shifts),
+                   "buffer_sets": sets, "cache": "hot" if args.hot else "cold"},
+        "tflops": round(nflops * K / (total_ms / 1e3) / 1e12, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": f"wattn_fwd_bf16_kernel<{M}>",
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "alg_bytes_per_launch": nbytes // len(shifts),
+                     "alg_flops_per_launch": nflops // len(shifts),
+                     "mfma_tflops": round((nflops / len(shifts)) / avg_launch_s / 1e12, 3),
+                     "mfma_peak_tflops": BF16_PEAK_TFLOPS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample_batch, B))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,112 @@
+/*
+ * swinattn.h -- C ABI of libswinattn: fused shifted-window multi-head
+ * attention forward (Swin Transformer) for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, for every image of a batch:
+ *   cyclic shift by (-shift, -shift) -> cut into window x window tiles ->
+ *   per tile and head: softmax(Q K^T / sqrt(head_dim) + bias + mask) V ->
+ *   put the tiles back -> shift by (+shift, +shift).
+ * Passages that define it:
+ *   - NVIDIA talk "Swin Transformer training and inference optimization"
+ *     (uticex.com article 1598), section 1: attention restricted to windows,
+ *     the window shift, the relative position bias, multi-head attention, and
+ *     the block's split into window shift/partition/reverse plus attention.
+ *   - same talk, section 2: shift, partition and merge are pure index mapping
+ *     (here folded into the kernel's loads and stores); the fused attention
+ *     takes the mask and the bias as tensors.
+ *   - same talk, section 3: the position-bias lookup is moved to a one-time
+ *     preprocessing step (swin_wattn_precompute); batch GEMM, softmax and
+ *     batch GEMM run as one kernel whose loads and stores absorb the
+ *     transposes.
+ *   - Baidu AIAK-Training talk (jxzklqfsx.com article 743345), section 2,
+ *     WindowAttention case: the whole module as one kernel, tiles staged
+ *     through the memory hierarchy, two matrix products and a softmax.
+ *
+ * Conventions shared by every call:
+ *   - every int return value is a swin_status_t; no call aborts or prints;
+ *   - arguments are checked before any device work is queued;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *     work is queued on it and the call returns without waiting;
+ *   - device pointers are owned by the caller unless stated otherwise;
+ *   - the calls act on the HIP device that is current on the calling thread.
+ *
+ * Mask semantics: after the shift, the last `window` rows (columns) of the
+ * shifted image hold two strips that were not adjacent in the image; the
+ * shifted frame is split into bands [0,H-window), [H-window,H-shift),
+ * [H-shift,H) per axis, and a query and a key in different band pairs get
+ * -100 added to their score (natural-log units).  With shift == 0 there is
+ * no mask.  Relative position index of query (yi,xi) and key (yj,xj) inside a
+ * window: (yi-yj+window-1)*(2*window-1) + (xi-xj+window-1).
+ */
+#ifndef SWINATTN_H
+#define SWINATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SWIN_OK = 0,
+  SWIN_ERR_INVALID_ARG = -1,  /* null or misaligned pointer, bad size, shift, divisibility */
+  SWIN_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim != 32, window > 12, too many heads */
+  SWIN_ERR_NOT_PREPARED = -3, /* no swin_wattn_precompute for (device, H, W, window, shift) */
+  SWIN_ERR_HIP = -4           /* the HIP runtime reported an error (allocation, launch) */
+} swin_status_t;
+
+/* Setup, once per (device, H, W, window, shift), before swin_wattn_fwd*.
+ * Builds in library-owned device memory: the relative position index
+ * [N][N] int32 (N = window^2), the shift mask [nW][N][N] float32 (0 or -100,
+ * nW = (H/window)*(W/window)), and the compact form the kernels read
+ * (per-window region labels [nW][N] uint8 and a per-window has-mask flag).
+ * May allocate device memory (hipMalloc); the fill is queued on `stream`.
+ * Calling it again for a prepared key is a no-op returning SWIN_OK.
+ * Requires H, W > 0, 1 <= window <= 12, H % window == 0, W % window == 0,
+ * 0 <= shift < window. */
+int swin_wattn_precompute(int H, int W, int window, int shift, void* stream);
+
+/* Hot path, bfloat16.
+ *   qkv            [B][H][W][3][heads][head_dim] bf16, contiguous, image
+ *                  (un-shifted) order; index 0 = query, 1 = key, 2 = value.
+ *                  Device pointer, 16-byte aligned.
+ *   rel_bias_table [(2*window-1)^2][heads] float32, contiguous; device
+ *                  pointer, 4-byte aligned.
+ *   out            [B][H][W][heads*head_dim] bf16, contiguous, image order;
+ *                  device pointer, 16-byte aligned; must not overlap qkv.
+ * Scores and softmax in float32, products on bf16 inputs with float32
+ * accumulation, attention weights rounded to bf16 before the value product,
+ * output rounded to nearest-even bf16.  B == 0 queues nothing and returns
+ * SWIN_OK.  head_dim must be 32; heads * (2*window-1)^2 * 4 bytes must fit
+ * in 64 KiB (the bias table is staged in LDS).  No allocation, no host
+ * synchronisation; safe to call concurrently from several threads once the
+ * precompute for the key has completed. */
+int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int B, int H, int W,
+                   int heads, int head_dim, int window, int shift, void* stream);
+
+/* Same operation with float32 qkv and out (products and accumulation in
+ * float32).  Same layouts, alignment and error behaviour. */
+int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out, int B, int H,
+                       int W, int heads, int head_dim, int window, int shift, void* stream);
+
+/* Copies of the precomputed tensors into caller-owned device memory, queued
+ * on `stream` (for verification).  SWIN_ERR_NOT_PREPARED without a prior
+ * swin_wattn_precompute for the key.
+ *   index  [N][N] int32;  mask [nW][N][N] float32;
+ *   region [nW][N] uint8 region labels (label = 3*band_y + band_x). */
+int swin_wattn_copy_index(int H, int W, int window, int shift, int32_t* dst, void* stream);
+int swin_wattn_copy_mask(int H, int W, int window, int shift, float* dst, void* stream);
+int swin_wattn_copy_region(int H, int W, int window, int shift, uint8_t* dst, void* stream);
+
+/* Frees every precomputed buffer on every device (synchronises each device
+ * first).  Afterwards swin_wattn_fwd* return SWIN_ERR_NOT_PREPARED until the
+ * next precompute.  Must not run concurrently with other calls. */
+int swin_wattn_release(void);
+
+/* Static, human-readable name of a status code. */
+const char* swin_wattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWINATTN_H */

@@ -1,0 +1,218 @@
+// C-ABI front of libswinattn: argument checks, the per-device cache of
+// precomputed index/mask tensors, and kernel launches on the caller's stream.
+// The bias lookup structure is built once at setup and reused by every call
+// (talk "Swin Transformer training and inference optimization", uticex.com
+// 1598, section 3: computations needed once are hoisted to preprocessing).
+
+#include <math.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/swinattn.h"
+#include "wattn_internal.h"
+
+using namespace swinattn;
+
+namespace {
+
+struct Prepared {
+  int dev, H, W, M, s;
+  void* block;  // one allocation holding the four arrays below
+  int32_t* rel_index;
+  float* mask;
+  uint8_t* region;
+  uint8_t* has_mask;
+};
+
+std::mutex g_mu;
+std::vector<Prepared> g_cache;
+
+bool shape_ok(int H, int W, int M, int s) {
+  return H > 0 && W > 0 && M >= 1 && M <= kMaxWindow && H % M == 0 && W % M == 0 && s >= 0 &&
+         s < M;
+}
+
+// caller holds g_mu
+Prepared* find(int dev, int H, int W, int M, int s) {
+  for (auto& e : g_cache)
+    if (e.dev == dev && e.H == H && e.W == W && e.M == M && e.s == s) return &e;
+  return nullptr;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int W, int heads,
+               int head_dim, int M, int s, void* stream, size_t elem, bool bf16) {
+  if (!qkv || !table || !out) return SWIN_ERR_INVALID_ARG;
+  if (!aligned(qkv, 16) || !aligned(out, 16) || !aligned(table, 4)) return SWIN_ERR_INVALID_ARG;
+  if (B < 0 || H <= 0 || W <= 0 || heads <= 0 || head_dim <= 0 || M <= 0) return SWIN_ERR_INVALID_ARG;
+  if (H % M != 0 || W % M != 0 || s < 0 || s >= M) return SWIN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || M > kMaxWindow) return SWIN_ERR_UNSUPPORTED;
+  const long long T = (2LL * M - 1) * (2LL * M - 1);
+  if (T * heads * (long long)sizeof(float) > kMaxTableLds) return SWIN_ERR_UNSUPPORTED;
+  const long long nW = (long long)(H / M) * (W / M);
+  const long long windows = (long long)B * nW;
+  if (windows > 0x7fffffffLL) return SWIN_ERR_UNSUPPORTED;
+  const long long tokens = (long long)B * H * W;
+  const long long C = (long long)heads * head_dim;
+  if (tokens > (1LL << 40) / (3 * C)) return SWIN_ERR_UNSUPPORTED;
+  if (overlap(qkv, (size_t)(tokens * 3 * C) * elem, out, (size_t)(tokens * C) * elem))
+    return SWIN_ERR_INVALID_ARG;
+  if (B == 0) return SWIN_OK;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SWIN_ERR_HIP;
+  Prepared prep;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    Prepared* e = find(dev, H, W, M, s);
+    if (!e) return SWIN_ERR_NOT_PREPARED;
+    prep = *e;
+  }
+  FwdParams p;
+  p.qkv = qkv;
+  p.table = table;
+  p.out = out;
+  p.rel_index = prep.rel_index;
+  p.region = prep.region;
+  p.has_mask = prep.has_mask;
+  p.B = B;
+  p.H = H;
+  p.W = W;
+  p.nh = heads;
+  p.shift = s;
+  p.nWx = W / M;
+  p.nW = (int)nW;
+  p.total_windows = (int)windows;
+  const double sd = sqrt((double)head_dim);
+  p.score_scale = (float)(1.4426950408889634 / sd);
+  p.inv_scale = (float)sd;
+  p.mask_value = (float)(-100.0 * sd);
+  // heads are dealt round-robin to the waves of a workgroup: prefer 2-3
+  // heads per wave (the next head's loads overlap the current head's math)
+  int waves = 1;
+  for (int cand = 4; cand >= 1; --cand)
+    if (heads % cand == 0 && heads / cand >= 2) {
+      waves = cand;
+      break;
+    }
+  if (heads == 1) waves = 1;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err = bf16 ? launch_fwd_bf16(M, p, waves, st) : launch_fwd_f32(M, p, waves, st);
+  return err == hipSuccess ? SWIN_OK : SWIN_ERR_HIP;
+}
+
+int copy_common(int H, int W, int M, int s, void* dst, int which, void* stream) {
+  if (!dst || !shape_ok(H, W, M, s)) return SWIN_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SWIN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  Prepared* e = find(dev, H, W, M, s);
+  if (!e) return SWIN_ERR_NOT_PREPARED;
+  const size_t N = (size_t)M * M, nW = (size_t)(H / M) * (W / M);
+  const void* src = which == 0 ? (const void*)e->rel_index
+                    : which == 1 ? (const void*)e->mask
+                                 : (const void*)e->region;
+  const size_t bytes = which == 0 ? N * N * 4 : which == 1 ? nW * N * N * 4 : nW * N;
+  const hipError_t err =
+      hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? SWIN_OK : SWIN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int swin_wattn_precompute(int H, int W, int window, int shift, void* stream) {
+  if (!shape_ok(H, W, window, shift)) return SWIN_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SWIN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (find(dev, H, W, window, shift)) return SWIN_OK;
+  const size_t N = (size_t)window * window, nW = (size_t)(H / window) * (W / window);
+  const size_t b_idx = align256(N * N * 4), b_mask = align256(nW * N * N * 4),
+               b_reg = align256(nW * N), b_flag = align256(nW);
+  void* block = nullptr;
+  if (hipMalloc(&block, b_idx + b_mask + b_reg + b_flag) != hipSuccess) return SWIN_ERR_HIP;
+  Prepared e;
+  e.dev = dev;
+  e.H = H;
+  e.W = W;
+  e.M = window;
+  e.s = shift;
+  e.block = block;
+  char* base = static_cast<char*>(block);
+  e.rel_index = reinterpret_cast<int32_t*>(base);
+  e.mask = reinterpret_cast<float*>(base + b_idx);
+  e.region = reinterpret_cast<uint8_t*>(base + b_idx + b_mask);
+  e.has_mask = reinterpret_cast<uint8_t*>(base + b_idx + b_mask + b_reg);
+  const hipError_t err = launch_precompute(H, W, window, shift, e.rel_index, e.mask, e.region,
+                                           e.has_mask, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    (void)hipFree(block);
+    return SWIN_ERR_HIP;
+  }
+  g_cache.push_back(e);
+  return SWIN_OK;
+}
+
+int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int B, int H, int W,
+                   int heads, int head_dim, int window, int shift, void* stream) {
+  return fwd_common(qkv, rel_bias_table, out, B, H, W, heads, head_dim, window, shift, stream, 2,
+                    true);
+}
+
+int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out, int B, int H,
+                       int W, int heads, int head_dim, int window, int shift, void* stream) {
+  return fwd_common(qkv, rel_bias_table, out, B, H, W, heads, head_dim, window, shift, stream, 4,
+                    false);
+}
+
+int swin_wattn_copy_index(int H, int W, int window, int shift, int32_t* dst, void* stream) {
+  return copy_common(H, W, window, shift, dst, 0, stream);
+}
+
+int swin_wattn_copy_mask(int H, int W, int window, int shift, float* dst, void* stream) {
+  return copy_common(H, W, window, shift, dst, 1, stream);
+}
+
+int swin_wattn_copy_region(int H, int W, int window, int shift, uint8_t* dst, void* stream) {
+  return copy_common(H, W, window, shift, dst, 2, stream);
+}
+
+int swin_wattn_release(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int status = SWIN_OK;
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto& e : g_cache) {
+    if (hipSetDevice(e.dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+        hipFree(e.block) != hipSuccess)
+      status = SWIN_ERR_HIP;
+  }
+  g_cache.clear();
+  if (have_cur) (void)hipSetDevice(cur);
+  return status;
+}
+
+const char* swin_wattn_status_string(int status) {
+  switch (status) {
+    case SWIN_OK: return "SWIN_OK";
+    case SWIN_ERR_INVALID_ARG: return "SWIN_ERR_INVALID_ARG: invalid argument";
+    case SWIN_ERR_UNSUPPORTED: return "SWIN_ERR_UNSUPPORTED: configuration not supported";
+    case SWIN_ERR_NOT_PREPARED: return "SWIN_ERR_NOT_PREPARED: swin_wattn_precompute not called";
+    case SWIN_ERR_HIP: return "SWIN_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"
