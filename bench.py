@@ -85,6 +85,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batch", type=int, default=64)
     ap.add_argument("--hot", action="store_true", help="one buffer set (working set may sit in cache)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 4 plain device-to-device copies of BYTES bytes (calibrates the "
+                         "HBM byte counters of a profiler) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -94,6 +97,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe // 16 * 16
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+        dst = [torch.empty_like(src) for _ in range(2)]
+        for i in range(4):
+            dst[i % 2].copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 4}), flush=True)
+        return 0
 
     import shifted_window_attention_swin_amd as swa
     import synth
@@ -132,21 +145,26 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # throughput: exactly K steps between two synchronisations
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         step(i)
-        ev[i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_launch_s = sum(launch_ms) / K / 1e3 / len(shifts)
     ms_per_step = total_ms / K
     value = nbytes * K / (total_ms / 1e3) / 1e9
+    # duration of each launch, from HIP events recorded on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_launch_s = sum(launch_ms) / K / 1e3 / len(shifts)
 
     achieved = (nbytes / len(shifts)) / avg_launch_s / 1e9
     traffic = measured_traffic(args.workload)

@@ -4,7 +4,10 @@ Usage: ``python shifted_window_attention_swin_amd/build.py`` (run it by path:
 importing the package itself requires the built library).  Every HIP source
 is compiled with packed FP32 instructions disabled (``-packed-fp32-ops``);
 hipcc's host pass warns that it does not know that feature, which is
-harmless.
+harmless.  ``-fno-honor-nans``: inputs are required to be finite (NaN inputs
+give unspecified results), which lets max reductions skip NaN quieting.
+``-amdgpu-mfma-vgpr-form``: MFMA results stay in VGPRs, where the softmax
+reads them, instead of round-tripping through AGPRs.
 """
 from __future__ import annotations
 
@@ -16,7 +19,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libswinattn.so")
-SOURCES = ["swinattn_api.hip", "wattn_kernels.hip"]
+SOURCES = ["swinattn_api.hip", "wattn_kernels.hip", "wattn_persistent.hip"]
 ARCH = "gfx950"
 
 
@@ -29,6 +32,7 @@ def hipcc() -> str:
 
 def command(out: str = LIB, extra=()) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-function", *extra, "-o", out,
             *[os.path.join(CSRC, s) for s in SOURCES]]

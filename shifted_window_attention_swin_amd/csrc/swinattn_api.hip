@@ -6,6 +6,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 #include <vector>
@@ -28,6 +29,29 @@ struct Prepared {
 
 std::mutex g_mu;
 std::vector<Prepared> g_cache;
+
+// compute units per device (looked up once per device)
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+
+int compute_units(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_cus[dev] <= 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    g_cus[dev] = v;
+  }
+  return g_cus[dev];
+}
+
+// heads per unit of the persistent kernel
+int head_group(int heads) {
+  if (heads % 2 == 0) return 2;
+  if (heads % 3 == 0) return 3;
+  return 1;
+}
 
 bool shape_ok(int H, int W, int M, int s) {
   return H > 0 && W > 0 && M >= 1 && M <= kMaxWindow && H % M == 0 && W % M == 0 && s >= 0 &&
@@ -57,14 +81,12 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
   if (B < 0 || H <= 0 || W <= 0 || heads <= 0 || head_dim <= 0 || M <= 0) return SWIN_ERR_INVALID_ARG;
   if (H % M != 0 || W % M != 0 || s < 0 || s >= M) return SWIN_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || M > kMaxWindow) return SWIN_ERR_UNSUPPORTED;
-  const long long T = (2LL * M - 1) * (2LL * M - 1);
-  if (T * heads * (long long)sizeof(float) > kMaxTableLds) return SWIN_ERR_UNSUPPORTED;
+  if (fwd_lds_bytes(M, heads) > (size_t)kMaxTableLds) return SWIN_ERR_UNSUPPORTED;
   const long long nW = (long long)(H / M) * (W / M);
-  const long long windows = (long long)B * nW;
-  if (windows > 0x7fffffffLL) return SWIN_ERR_UNSUPPORTED;
-  const long long tokens = (long long)B * H * W;
   const long long C = (long long)heads * head_dim;
-  if (tokens > (1LL << 40) / (3 * C)) return SWIN_ERR_UNSUPPORTED;
+  const long long image_bytes = (long long)H * W * 3 * C * (long long)elem;
+  if (image_bytes > kMaxChunkBytes) return SWIN_ERR_UNSUPPORTED;
+  const long long tokens = (long long)B * H * W;
   if (overlap(qkv, (size_t)(tokens * 3 * C) * elem, out, (size_t)(tokens * C) * elem))
     return SWIN_ERR_INVALID_ARG;
   if (B == 0) return SWIN_OK;
@@ -79,36 +101,66 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
     prep = *e;
   }
   FwdParams p;
-  p.qkv = qkv;
   p.table = table;
-  p.out = out;
-  p.rel_index = prep.rel_index;
-  p.region = prep.region;
   p.has_mask = prep.has_mask;
-  p.B = B;
   p.H = H;
   p.W = W;
   p.nh = heads;
   p.shift = s;
   p.nWx = W / M;
   p.nW = (int)nW;
-  p.total_windows = (int)windows;
   const double sd = sqrt((double)head_dim);
   p.score_scale = (float)(1.4426950408889634 / sd);
   p.inv_scale = (float)sd;
   p.mask_value = (float)(-100.0 * sd);
-  // heads are dealt round-robin to the waves of a workgroup: prefer 2-3
-  // heads per wave (the next head's loads overlap the current head's math)
+  // 100*sqrt(d) as three bf16 pieces (each the top 8 significant bits of the
+  // remainder); their sum is the fp32 value exactly, in any order
+  {
+    float rest = (float)(100.0 * sd);
+    for (int k = 0; k < 3; ++k) {
+      uint32_t u;
+      memcpy(&u, &rest, 4);
+      u &= 0xFFFF0000u;
+      float piece;
+      memcpy(&piece, &u, 4);
+      p.mask_pieces[k] = piece;
+      rest -= piece;
+    }
+  }
+  // bf16 windows of up to 4 tiles go to the persistent LDS-staged kernel
+  const int hg = head_group(heads);
+  const bool persistent = bf16 && M <= kMaxPersistentWindow &&
+                          persistent_lds_bytes(M, hg, heads) <= (size_t)kMaxTableLds;
+  const int cus = persistent ? compute_units(dev) : 0;
+  p.nhg = heads / hg;
+  // per-window kernels: heads are dealt round-robin to the waves of a
+  // workgroup, preferably 2-3 heads per wave
   int waves = 1;
   for (int cand = 4; cand >= 1; --cand)
     if (heads % cand == 0 && heads / cand >= 2) {
       waves = cand;
       break;
     }
-  if (heads == 1) waves = 1;
+  // images per launch: keeps every in-kernel byte offset below 2^31, and the
+  // grid (windows of the launch) below 2^31
+  long long per = kMaxChunkBytes / image_bytes;
+  if (per * nW * heads > 0x7fffffffLL) per = 0x7fffffffLL / (nW * heads);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t err = bf16 ? launch_fwd_bf16(M, p, waves, st) : launch_fwd_f32(M, p, waves, st);
-  return err == hipSuccess ? SWIN_OK : SWIN_ERR_HIP;
+  const char* in = static_cast<const char*>(qkv);
+  char* o = static_cast<char*>(out);
+  for (long long b0 = 0; b0 < B; b0 += per) {
+    const long long nb = B - b0 < per ? B - b0 : per;
+    p.qkv = in + b0 * image_bytes;
+    p.out = o + b0 * (image_bytes / 3);
+    p.B = (int)nb;
+    p.total_windows = (int)(nb * nW);
+    p.units = (int)(nb * nW * p.nhg);
+    const hipError_t err = persistent ? launch_fwd_bf16_persistent(M, hg, p, cus, st)
+                           : bf16     ? launch_fwd_bf16(M, p, waves, st)
+                                      : launch_fwd_f32(M, p, waves, st);
+    if (err != hipSuccess) return SWIN_ERR_HIP;
+  }
+  return SWIN_OK;
 }
 
 int copy_common(int H, int W, int M, int s, void* dst, int which, void* stream) {

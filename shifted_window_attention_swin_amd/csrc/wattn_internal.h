@@ -10,20 +10,24 @@ namespace swinattn {
 constexpr int kHeadDim = 32;    // one MFMA K-step (16x16x32 bf16) per score tile
 constexpr int kMaxWindow = 12;  // N = 144 = 9 tiles of 16 tokens
 constexpr int kMaxTableLds = 64 * 1024;
+// In-kernel token offsets are 32-bit: one launch covers at most this many
+// bytes of qkv; larger batches are split into several launches.
+constexpr long long kMaxChunkBytes = 1LL << 31;
 
 struct FwdParams {
-  const void* qkv;          // [B][H][W][3][nh][32]
+  const void* qkv;          // [B][H][W][3][nh][32], B = images of this launch
   const float* table;       // [(2M-1)^2][nh]
   void* out;                // [B][H][W][nh*32]
-  const int32_t* rel_index; // [N][N] precomputed
-  const uint8_t* region;    // [nW][N] precomputed region labels
-  const uint8_t* has_mask;  // [nW] precomputed: 1 if the window's labels differ
+  const uint8_t* has_mask;  // [nW] precomputed: 1 if the window's region labels differ
   int B, H, W, nh, shift;
   int nWx, nW;
-  int total_windows;        // B * nW (grid size)
+  int total_windows;        // B * nW (grid size of the per-window kernels)
+  int units;                // B * nW * nhg (work units of the persistent kernel)
+  int nhg;                  // head groups per window (persistent kernel)
   float score_scale;        // log2(e) / sqrt(head_dim)
   float inv_scale;          // sqrt(head_dim): bias and mask are pre-divided by the scale
   float mask_value;         // -100 * sqrt(head_dim)
+  float mask_pieces[3];     // bf16-exact parts summing to 100 * sqrt(head_dim) in fp32
 };
 
 // Queues the precompute kernel.  rel_index [N*N], mask [nW*N*N],
@@ -34,6 +38,16 @@ hipError_t launch_precompute(int H, int W, int M, int s, int32_t* rel_index, flo
 // Queue the forward kernels; M in [1, kMaxWindow].  `waves` = waves per
 // workgroup (heads are dealt round-robin to waves).
 hipError_t launch_fwd_bf16(int M, const FwdParams& p, int waves, hipStream_t stream);
+// Dynamic LDS of one forward workgroup (staged bias table plus slack).
+size_t fwd_lds_bytes(int M, int nh);
 hipError_t launch_fwd_f32(int M, const FwdParams& p, int waves, hipStream_t stream);
+
+// Persistent LDS-staged bf16 forward (windows of at most 4 tiles, M <= 8):
+// heads are processed in groups of HG (1..4, HG divides nh); `cus` = compute
+// units of the device (the grid fills them at the kernel's occupancy).
+constexpr int kMaxPersistentWindow = 8;
+hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int cus,
+                                      hipStream_t stream);
+size_t persistent_lds_bytes(int M, int HG, int nh);
 
 }  // namespace swinattn

@@ -4,213 +4,180 @@
 // heads round-robin.  For one head a wave holds the whole window in VGPRs:
 //
 //   Q, K, V   16-token tiles loaded straight from HBM in MFMA operand layout
-//             (lane = token 16t + lane%16, 16 bytes of head_dim each); the
-//             cyclic shift and window partition are the address arithmetic of
-//             these loads (talk "Swin Transformer training and inference
-//             optimization", uticex.com 1598, section 2: the window ops are
-//             index mapping; section 3: transposes folded into the kernel's
-//             loads and stores).
+//             (lane = token, 16 bytes of head_dim each); the cyclic shift and
+//             the window partition are the address arithmetic of these loads
+//             (talk "Swin Transformer training and inference optimization",
+//             uticex.com 1598, section 2: the window ops are index mapping;
+//             section 3: transposes folded into the kernel's loads/stores).
 //   S^T = K Q^T + C   v_mfma_f32_16x16x32_bf16, K = head_dim = 32 exactly.
-//             The accumulator C is initialised with the relative position bias
-//             (gathered from a head-major copy of the table in LDS) plus the
-//             shift mask, both divided by the score scale, so one fma later
-//             turns D into a base-2 logit.  Transposing S puts one query per
-//             lane column: the softmax over keys is an in-lane reduction plus
-//             two cross-lane steps.
-//   P^T       exp2, row sums in fp32, P rounded to bf16; the C/D layout of S^T
-//             is directly the B-operand layout of the next MFMA.
-//   O^T = V^T P^T   V^T in operand layout comes from an MFMA against a 0/1
-//             selector (an exact transpose inside the matrix core).
+//             The accumulator C starts as relative position bias (+ shift
+//             mask) divided by the score scale, so one fma later turns D into
+//             a base-2 logit.  Transposing S puts one query per lane column:
+//             the softmax over keys is in-lane plus two permlane swaps.
+//   P^T       exp2 of the logits, rounded to bf16: the C/D layout of S^T is
+//             directly the B-operand layout of the next MFMA.
+//   O^T = V^T P^T   V^T in operand layout comes from an MFMA of each value
+//             tile against a 0/1 selector (an exact transpose in the matrix
+//             core); the row sums of P come from one more MFMA against a tile
+//             of ones, so the normaliser sums exactly the weights applied.
 //   store     lane writes 4 consecutive channels of one token: the window
 //             reverse and the roll back are the store addresses.
 //
-// Tiles: N = window^2 tokens padded to NT*16.  Padded keys get -inf in the
-// accumulator initialisation (weight exactly 0); padded tokens load as zero
-// (0 * finite = 0 in the value product); padded queries are not stored.
+// Token layout inside a window ("quad tiles"): with Q = ceil(M/4) the window
+// is padded to (4Q) x (4Q) tokens and cut into Q*Q tiles of 4 rows x 4
+// columns; in-tile token u sits at row 4*(t/Q) + u/4, column 4*(t%Q) + u%4.
+// In the C/D layout row 4g+r of a key tile (g = lane/16) is then window row
+// 4*(t/Q)+g, column 4*(t%Q)+r, so the relative position index
+// (dy+M-1)(2M-1) + (dx+M-1) of (query, key) splits into a per-lane part and
+// a compile-time part: with the bias table stored reversed in LDS, every bias
+// gather is one ds_read with an immediate offset and no address arithmetic.
+// Padded keys get -inf in the accumulator (weight exactly 0); padded tokens
+// load the window's first token as finite stand-in data (weight 0 times
+// finite = 0 in the value product); padded queries are not stored.
 
-#include "wattn_internal.h"
+#include "wattn_common.h"
 
 namespace swinattn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#define SWA_INLINE __device__ __forceinline__
-
-template <int M>
-struct Win {
-  static constexpr int N = M * M;
-  static constexpr int NT = (N + 15) / 16;      // 16-token tiles
-  static constexpr int LV = N - 16 * (NT - 1);  // valid tokens of the last tile (1..16)
-  static constexpr int T = (2 * M - 1) * (2 * M - 1);
-  static constexpr int NK = (NT + 1) / 2;       // 32-key steps of the bf16 value product
-  // row r of key tile t holds key 16t + 4g + r, g = lane / 16
-  static constexpr bool row_empty(int t, int r) { return t == NT - 1 && r >= LV; }
-  static constexpr bool row_full(int t, int r) { return t < NT - 1 || 12 + r < LV; }
-};
-
-// Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each
-// XCD (and its L2) works on one contiguous run of windows.
-SWA_INLINE int xcd_window(int id, int G) {
-  const int per = G >> 3, rem = G & 7, x = id & 7, k = id >> 3;
-  return x * per + (x < rem ? x : rem) + k;
-}
-
-SWA_INLINE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-SWA_INLINE float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // Everything a lane needs about its tokens, built once per workgroup.
 template <int M>
 struct LaneWindow {
   using S = Win<M>;
-  int rc[S::NT];      // query code  rel_index[i][0] - rel_index[0][0], i = 16t + c
-  int cc[S::NT][4];   // key code    rel_index[0][j], j = 16t + 4g + r
-  int li[S::NT];      // region label of query i (masked windows only)
-  int lj[S::NT][4];   // region label of key j
-  long long pix[S::NT];  // flattened image position of token 16t + c
-  bool ok[S::NT];     // token 16t + c exists
+  unsigned in_off[S::NT];   // byte offset of this lane's slice of token (t, c) in the qkv chunk
+  unsigned out_off[S::NT];  // byte offset of this lane's slice of token (t, c) in the out chunk
+  int qbase[S::NT];         // reversed-table index base of query (t, c) for lane group g
+  bool ok[S::NT];           // token (t, c) lies inside the window
+  int li[S::NT];            // region label of query (t, c)            (masked, select path)
+  int lj[S::NT][4];         // region label of key row (t, 4g + r)     (masked, select path)
+  bf16x8 mask_a[S::NT];     // key-side mask operand of tile t          (masked, MFMA path)
+  bf16x8 mask_b[S::NT];     // query-side mask operand of tile t        (masked, MFMA path)
 
-  SWA_INLINE void init(const FwdParams& p, int b, int w, int g, int c, bool masked) {
-    constexpr int N = S::N;
+  SWA_INLINE void init(const FwdParams& p, int b, int w, int g, int c, int elem) {
     const int wy = w / p.nWx, wx = w - wy * p.nWx;
-    const int r00 = p.rel_index[0];
+    const unsigned C = (unsigned)p.nh * kHeadDim;
 #pragma unroll
     for (int t = 0; t < S::NT; ++t) {
-      const int i = 16 * t + c;
-      ok[t] = i < N;
-      const int ti = ok[t] ? i : 0;
-      rc[t] = p.rel_index[ti * N] - r00;
-      // shifted frame position (wy*M+ty, wx*M+tx) holds image position +shift (mod H, W)
-      const int ty = ti / M, tx = ti - ty * M;
-      int y = wy * M + ty + p.shift, x = wx * M + tx + p.shift;
+      const int ty = 4 * (t / S::Q) + c / 4, tx = 4 * (t % S::Q) + c % 4;
+      ok[t] = ty < M && tx < M;
+      // query code (2M-1)*row + col; padded queries borrow token (0, 0)
+      const int a = ok[t] ? S::D * ty + tx : 0;
+      qbase[t] = S::T - 1 - S::C0 - a + S::D * g;
+      // shifted-frame (wy*M+ty, wx*M+tx) holds image position + shift (mod H, W)
+      int y = wy * M + (ok[t] ? ty : 0) + p.shift, x = wx * M + (ok[t] ? tx : 0) + p.shift;
       y -= y >= p.H ? p.H : 0;
       x -= x >= p.W ? p.W : 0;
-      pix[t] = ((long long)b * p.H + y) * p.W + x;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * t + 4 * g + r;
-        cc[t][r] = p.rel_index[j < N ? j : 0];
-      }
+      const unsigned pix = ((unsigned)b * p.H + y) * p.W + x;
+      in_off[t] = (pix * 3u * C + 8u * g) * elem;
+      out_off[t] = (pix * C + 4u * g) * elem;
     }
-    if (masked) {
-      const uint8_t* reg = p.region + (long long)w * N;
+  }
+
+  template <bool MFMA_OPERANDS>
+  SWA_INLINE void init_labels(const FwdParams& p, int w, int g, int c) {
+    const int wy = w / p.nWx, wx = w - wy * p.nWx;
+    if (MFMA_OPERANDS) {
+      // Inside one window the region labels take at most four values: the
+      // window's rows and columns each meet at most two bands, told apart by
+      // "position >= L - shift".  Local label l = 2*[row part] + [column
+      // part] is owned by lane group g = l.  A score tile MFMA of these
+      // operands adds sum_s [l_key == g] x_s * ([l_query == g] - 1)
+      // = -(x_0 + x_1 + x_2) = -100/scale exactly when the labels differ.
 #pragma unroll
       for (int t = 0; t < S::NT; ++t) {
-        li[t] = reg[ok[t] ? 16 * t + c : 0];
+        const int ty = 4 * (t / S::Q) + c / 4, tx = 4 * (t % S::Q) + c % 4;
+        const int loc = 2 * (wy * M + ty >= p.H - p.shift) + (wx * M + tx >= p.W - p.shift);
+        const bool mine = loc == g;
+        bf16x8 a = {}, q = {};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * t + 4 * g + r;
-          lj[t][r] = reg[j < N ? j : 0];
+        for (int k = 0; k < 3; ++k) {
+          a[k] = mine ? (__bf16)p.mask_pieces[k] : (__bf16)0.f;
+          q[k] = mine ? (__bf16)0.f : (__bf16)-1.f;
         }
+        mask_a[t] = a;
+        mask_b[t] = q;
       }
-    } else {
+      return;
+    }
 #pragma unroll
-      for (int t = 0; t < S::NT; ++t) {
-        li[t] = 0;
+    for (int t = 0; t < S::NT; ++t) {
+      const int ty = 4 * (t / S::Q) + c / 4, tx = 4 * (t % S::Q) + c % 4;
+      li[t] = region_label(wy * M + ty, wx * M + tx, p.H, p.W, M, p.shift);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lj[t][r] = 0;
-      }
+      for (int r = 0; r < 4; ++r)
+        lj[t][r] = region_label(wy * M + 4 * (t / S::Q) + g, wx * M + 4 * (t % S::Q) + r, p.H, p.W,
+                                M, p.shift);
     }
   }
 
   // accumulator initialisation of score tile (key tile jt, query tile it):
-  // bias/scale (+ mask/scale), -inf for keys past N
-  SWA_INLINE f32x4 score_init(const float* s_bias, int hoff, int it, int jt, int g, bool masked,
-                              float mask_value) const {
+  // (bias + mask) / scale, -inf for keys outside the window
+  SWA_INLINE f32x4 score_init(const float* s_bias, int hbase, int it, int jt, bool g_ok,
+                              bool select_mask, float mask_value) const {
     f32x4 acc;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float v;
-      if (S::row_empty(jt, r)) {
-        v = -__builtin_inff();
-      } else {
-        v = s_bias[hoff + rc[it] + cc[jt][r]];
-        if (!S::row_full(jt, r)) v = (4 * g + r < S::LV) ? v : -__builtin_inff();
-        if (masked) v = (li[it] == lj[jt][r]) ? v : v + mask_value;
+      if (!S::col_ok(jt, r)) {
+        acc[r] = -__builtin_inff();
+        continue;
       }
+      float v = s_bias[hbase + qbase[it] + S::E(jt) + r];
+      if (!S::rows_all(jt)) v = g_ok ? v : -__builtin_inff();
+      if (select_mask) v = (li[it] == lj[jt][r]) ? v : v + mask_value;
       acc[r] = v;
     }
     return acc;
   }
 };
 
-// Row softmax of one query column block: s[jt][r] holds D for key 16jt+4g+r
-// of the lane's query.  Replaces s by exp2(D*scale - max) and returns the
-// (cross-lane complete) sum.
-template <int M>
-SWA_INLINE float softmax_cols(f32x4 (&s)[Win<M>::NT], float score_scale) {
-  using S = Win<M>;
-  float m = -__builtin_inff();
-#pragma unroll
-  for (int jt = 0; jt < S::NT; ++jt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (!S::row_empty(jt, r)) m = fmaxf(m, s[jt][r]);
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  const float nms = -m * score_scale;
-  float l = 0.f;
-#pragma unroll
-  for (int jt = 0; jt < S::NT; ++jt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (S::row_empty(jt, r)) {
-        s[jt][r] = 0.f;
-      } else {
-        const float e = fast_exp2(fmaf(s[jt][r], score_scale, nms));
-        s[jt][r] = e;
-        l += e;
-      }
-    }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  return l;
-}
-
 // ---------------------------------------------------------------------------
 // bf16 forward
 
 template <int M>
-SWA_INLINE void load_head_bf16(const __bf16* qkv, const LaneWindow<M>& lw, int C, int h, int g,
+SWA_INLINE void load_head_bf16(const char* base, const LaneWindow<M>& lw, unsigned Cb,
                                bf16x8 (&q)[Win<M>::NT], bf16x8 (&k)[Win<M>::NT],
                                bf16x8 (&v)[Win<M>::NT]) {
-  using S = Win<M>;
+  // tokens outside the window read the window's first token instead (their
+  // offsets are clamped): padded keys are -inf in the accumulator, padded
+  // values meet weight 0 and padded queries are never stored, so finite
+  // stand-in data is as good as zeros and needs no masking
 #pragma unroll
-  for (int t = 0; t < S::NT; ++t) {
-    if (lw.ok[t]) {
-      const __bf16* src = qkv + lw.pix[t] * (3LL * C) + h * kHeadDim + 8 * g;
-      q[t] = *reinterpret_cast<const bf16x8*>(src);
-      k[t] = *reinterpret_cast<const bf16x8*>(src + C);
-      v[t] = *reinterpret_cast<const bf16x8*>(src + 2 * C);
-    } else {
-      q[t] = bf16x8{};
-      k[t] = bf16x8{};
-      v[t] = bf16x8{};
-    }
+  for (int t = 0; t < Win<M>::NT; ++t) {
+    const char* src = base + lw.in_off[t];
+    q[t] = *reinterpret_cast<const bf16x8*>(src);
+    k[t] = *reinterpret_cast<const bf16x8*>(src + Cb);
+    v[t] = *reinterpret_cast<const bf16x8*>(src + 2 * Cb);
   }
 }
 
+struct HeadCtx {
+  const float* s_bias;
+  char* out;          // out chunk base
+  float score_scale;
+  float mask_value;
+  bool g_ok;          // lane group is a window row in the last row group
+  bf16x8 sel[2];      // selectors of channel halves for the transpose MFMA
+  bf16x8 ones;
+};
+
 template <int M>
-SWA_INLINE void head_bf16(const FwdParams& p, const LaneWindow<M>& lw, const float* s_bias,
-                          __bf16* out, int C, int h, int g, bool masked, const bf16x8 (&sel)[2],
+SWA_INLINE void head_bf16(const HeadCtx& hc, const LaneWindow<M>& lw, int h, bool masked,
                           const bf16x8 (&q)[Win<M>::NT], const bf16x8 (&k)[Win<M>::NT],
                           const bf16x8 (&v)[Win<M>::NT]) {
   using S = Win<M>;
   constexpr int NT = S::NT, NK = S::NK;
-  // V^T in A-operand layout: MFMA of each value tile against the selector of
-  // channel half `hf` gives D[4g+r][c] = V[16t+4g+r][16hf+c] exactly
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  // V^T in A-operand layout: slots 0-3 from value tile 2kt, 4-7 from 2kt+1;
+  // the selector MFMA gives D[4g+r][c] = V[token (t, 4g+r)][16*hf + c]
   bf16x8 va[2][NK];
 #pragma unroll
   for (int kt = 0; kt < NK; ++kt)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[2 * kt], sel[hf], z, 0, 0, 0);
+      const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[2 * kt], hc.sel[hf], z, 0, 0, 0);
       f32x4 d1 = z;
       if (2 * kt + 1 < NT)
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[2 * kt + 1], sel[hf], z, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[2 * kt + 1], hc.sel[hf], z, 0, 0, 0);
       bf16x8 a;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -220,213 +187,245 @@ SWA_INLINE void head_bf16(const FwdParams& p, const LaneWindow<M>& lw, const flo
       va[hf][kt] = a;
     }
 
-  const int hoff = h * S::T;
+  const int hbase = h * S::T;
+  char* out_h = hc.out + h * kHeadDim * 2;
+  // The label compares are the same for every head; hoisted out of the head
+  // loop they would need 64-bit lane masks by the dozen.  Redo them per head.
+  LaneWindow<M> lwh = lw;
+  if (!S::MASK_MFMA) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      asm volatile("" : "+v"(lwh.li[t]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(lwh.lj[t][r]));
+    }
+  }
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
     f32x4 s[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
-      s[jt] = lw.score_init(s_bias, hoff, it, jt, g, masked, p.mask_value);
+      s[jt] = lwh.score_init(hc.s_bias, hbase, it, jt, hc.g_ok, masked && !S::MASK_MFMA,
+                             hc.mask_value);
       s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[jt], q[it], s[jt], 0, 0, 0);
+      if (S::MASK_MFMA && masked)
+        s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lwh.mask_a[jt], lwh.mask_b[it], s[jt], 0, 0, 0);
     }
-    const float l = softmax_cols<M>(s, p.score_scale);
-    // P^T as B operand: slots 0-3 = key tile 2kt, slots 4-7 = key tile 2kt+1
+    softmax_numerators<M>(s, hc.score_scale);
     bf16x8 pb[NK];
 #pragma unroll
-    for (int kt = 0; kt < NK; ++kt) {
+    for (int kt = 0; kt < NK; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         pb[kt][r] = (__bf16)s[2 * kt][r];
         pb[kt][4 + r] = (2 * kt + 1 < NT) ? (__bf16)s[2 * kt + 1][r] : (__bf16)0.f;
       }
-    }
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 o0 = z, o1 = z, l4 = z;
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
       o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][kt], pb[kt], o0, 0, 0, 0);
       o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][kt], pb[kt], o1, 0, 0, 0);
+      l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hc.ones, pb[kt], l4, 0, 0, 0);
     }
     if (lw.ok[it]) {
-      const float inv = fast_rcp(l);
+      const float inv = fast_rcp(l4[0]);
       bf16x4 w0, w1;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         w0[r] = (__bf16)(o0[r] * inv);
         w1[r] = (__bf16)(o1[r] * inv);
       }
-      __bf16* dst = out + lw.pix[it] * C + h * kHeadDim + 4 * g;
+      char* dst = out_h + lw.out_off[it];
       *reinterpret_cast<bf16x4*>(dst) = w0;
-      *reinterpret_cast<bf16x4*>(dst + 16) = w1;
+      *reinterpret_cast<bf16x4*>(dst + 32) = w1;
     }
+    // keep query tiles apart: interleaving them only raises register pressure
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Heads h = wave, wave + nwaves, ...  With PREFETCH the loads of the next
+// head are issued before the math of the current one (two register buffers,
+// no copies); without it latency is hidden by the other resident waves.
+template <int M, bool PREFETCH>
+SWA_INLINE void run_heads_bf16(const HeadCtx& hc, const LaneWindow<M>& lw, const char* in,
+                               unsigned Cb, int nh, int wave, int nwaves, bool masked,
+                               bf16x8 (&qa)[Win<M>::NT], bf16x8 (&ka)[Win<M>::NT],
+                               bf16x8 (&va)[Win<M>::NT]) {
+  constexpr int NT = Win<M>::NT;
+  if (!PREFETCH) {
+    for (int h = wave; h < nh; h += nwaves) {
+      if (h != wave) load_head_bf16<M>(in + h * kHeadDim * 2, lw, Cb, qa, ka, va);
+      head_bf16<M>(hc, lw, h, masked, qa, ka, va);
+    }
+    return;
+  }
+  bf16x8 qb[NT], kb[NT], vb[NT];
+  for (int h = wave; h < nh;) {
+    const int h1 = h + nwaves;
+    if (h1 < nh) load_head_bf16<M>(in + h1 * kHeadDim * 2, lw, Cb, qb, kb, vb);
+    head_bf16<M>(hc, lw, h, masked, qa, ka, va);
+    if (h1 >= nh) break;
+    const int h2 = h1 + nwaves;
+    if (h2 < nh) load_head_bf16<M>(in + h2 * kHeadDim * 2, lw, Cb, qa, ka, va);
+    head_bf16<M>(hc, lw, h1, masked, qb, kb, vb);
+    h = h2;
   }
 }
 
 template <int M>
 __global__ __launch_bounds__(256) void wattn_fwd_bf16_kernel(FwdParams p) {
   using S = Win<M>;
-  constexpr int NT = S::NT, T = S::T;
+  constexpr int NT = S::NT;
   extern __shared__ float s_bias[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int win = xcd_window(blockIdx.x, p.total_windows);
   const int b = win / p.nW, w = win - b * p.nW;
-  const int nh = p.nh, C = nh * kHeadDim;
-  const __bf16* qkv = static_cast<const __bf16*>(p.qkv);
-  __bf16* out = static_cast<__bf16*>(p.out);
+  const int nh = p.nh;
+  const unsigned Cb = (unsigned)nh * kHeadDim * 2;
+  const char* in = static_cast<const char*>(p.qkv);
 
-  // bias table -> LDS, head-major, divided by the score scale
-  for (int e = tid; e < T * nh; e += blockDim.x) {
-    const int idx = e / nh, h = e - idx * nh;
-    s_bias[h * T + idx] = p.table[e] * p.inv_scale;
-  }
-  const bool masked = p.has_mask[w] != 0;
+  stage_bias<M>(s_bias, p.table, nh, p.inv_scale);
   LaneWindow<M> lw;
-  lw.init(p, b, w, g, c, masked);
+  lw.init(p, b, w, g, c, 2);
+  bf16x8 q[NT], k[NT], v[NT];
+  if (wave < nh) load_head_bf16<M>(in + wave * kHeadDim * 2, lw, Cb, q, k, v);
 
-  bf16x8 sel[2];
+  HeadCtx hc;
+  hc.s_bias = s_bias;
+  hc.out = static_cast<char*>(p.out);
+  hc.score_scale = p.score_scale;
+  hc.mask_value = p.mask_value;
+  hc.g_ok = g < S::LG;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) sel[hf][s] = (8 * g + s == c + 16 * hf) ? (__bf16)1.f : (__bf16)0.f;
-
-  bf16x8 q[NT], k[NT], v[NT];
-  int h = wave;
-  if (h < nh) load_head_bf16<M>(qkv, lw, C, h, g, q, k, v);
-  __syncthreads();
-  for (; h < nh; h += nwaves) {
-    const bool more = h + nwaves < nh;
-    bf16x8 qn[NT], kn[NT], vn[NT];
-    if (more) load_head_bf16<M>(qkv, lw, C, h + nwaves, g, qn, kn, vn);
-    head_bf16<M>(p, lw, s_bias, out, C, h, g, masked, sel, q, k, v);
-    if (more) {
+    for (int s = 0; s < 8; ++s)
+      hc.sel[hf][s] = (8 * g + s == c + 16 * hf) ? (__bf16)1.f : (__bf16)0.f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        q[t] = qn[t];
-        k[t] = kn[t];
-        v[t] = vn[t];
+  for (int s = 0; s < 8; ++s) hc.ones[s] = (__bf16)1.f;
+  __syncthreads();
+
+  const bool masked = p.has_mask[w] != 0;
+  if (masked) lw.template init_labels<S::MASK_MFMA>(p, w, g, c);
+  run_heads_bf16<M, kPrefetch>(hc, lw, in, Cb, nh, wave, nwaves, masked, q, k, v);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 forward: the same layout with v_mfma_f32_16x16x4_f32 (K = 4 per step;
+// lane group g supplies channel 8g+st at step st, for Q and K alike)
+
+template <int M>
+SWA_INLINE void head_f32(const FwdParams& p, const LaneWindow<M>& lw, const float* s_bias,
+                         const char* in, char* out, int h, int g, int c, bool g_ok, bool masked) {
+  using S = Win<M>;
+  constexpr int NT = S::NT;
+  const unsigned Cb = (unsigned)p.nh * kHeadDim * 4;
+  const char* in_h = in + h * kHeadDim * 4;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 vt[NT][2], kk[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    f32x4 v0 = z, v1 = z, k0 = z, k1 = z;
+    if (lw.ok[t]) {
+      const char* src = in_h + lw.in_off[t];
+      k0 = *reinterpret_cast<const f32x4*>(src + Cb);
+      k1 = *reinterpret_cast<const f32x4*>(src + Cb + 16);
+      v0 = *reinterpret_cast<const f32x4*>(src + 2 * Cb);
+      v1 = *reinterpret_cast<const f32x4*>(src + 2 * Cb + 16);
+    }
+    kk[t][0] = k0;
+    kk[t][1] = k1;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 acc = z;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const float sv = (8 * g + st == c + 16 * hf) ? 1.f : 0.f;
+        const float vv = st < 4 ? v0[st] : v1[st - 4];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sv, acc, 0, 0, 0);
       }
+      vt[t][hf] = acc;
+    }
+  }
+  const int hbase = h * S::T;
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    f32x4 q0 = z, q1 = z;
+    if (lw.ok[it]) {
+      const char* src = in_h + lw.in_off[it];
+      q0 = *reinterpret_cast<const f32x4*>(src);
+      q1 = *reinterpret_cast<const f32x4*>(src + 16);
+    }
+    f32x4 s[NT];
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      f32x4 acc = lw.score_init(s_bias, hbase, it, jt, g_ok, masked, p.mask_value);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const float ka = st < 4 ? kk[jt][0][st] : kk[jt][1][st - 4];
+        const float qb = st < 4 ? q0[st] : q1[st - 4];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, qb, acc, 0, 0, 0);
+      }
+      s[jt] = acc;
+    }
+    softmax_numerators<M>(s, p.score_scale);
+    f32x4 o0 = z, o1 = z, l4 = z;
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!S::col_ok(jt, r)) continue;
+        o0 = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[jt][0][r], s[jt][r], o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[jt][1][r], s[jt][r], o1, 0, 0, 0);
+        l4 = __builtin_amdgcn_mfma_f32_16x16x4f32(1.f, s[jt][r], l4, 0, 0, 0);
+      }
+    if (lw.ok[it]) {
+      const float inv = fast_rcp(l4[0]);
+      char* dst = out + h * kHeadDim * 4 + lw.out_off[it];
+      *reinterpret_cast<f32x4*>(dst) = o0 * inv;
+      *reinterpret_cast<f32x4*>(dst + 64) = o1 * inv;
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// fp32 forward: the same structure with v_mfma_f32_16x16x4_f32 (K = 4 per
-// step; lane group g supplies channel 8g+st at step st, for Q and K alike)
-
 template <int M>
 __global__ __launch_bounds__(256) void wattn_fwd_f32_kernel(FwdParams p) {
   using S = Win<M>;
-  constexpr int NT = S::NT, T = S::T;
   extern __shared__ float s_bias[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int win = xcd_window(blockIdx.x, p.total_windows);
   const int b = win / p.nW, w = win - b * p.nW;
-  const int nh = p.nh, C = nh * kHeadDim;
-  const float* qkv = static_cast<const float*>(p.qkv);
-  float* out = static_cast<float*>(p.out);
+  const char* in = static_cast<const char*>(p.qkv);
+  char* out = static_cast<char*>(p.out);
 
-  for (int e = tid; e < T * nh; e += blockDim.x) {
-    const int idx = e / nh, h = e - idx * nh;
-    s_bias[h * T + idx] = p.table[e] * p.inv_scale;
-  }
-  const bool masked = p.has_mask[w] != 0;
+  stage_bias<M>(s_bias, p.table, p.nh, p.inv_scale);
   LaneWindow<M> lw;
-  lw.init(p, b, w, g, c, masked);
+  lw.init(p, b, w, g, c, 4);
+  const bool g_ok = g < S::LG;
   __syncthreads();
-
-  for (int h = wave; h < nh; h += nwaves) {
-    // V^T through the selector: vt[t][hf][r] = V[16t+4g+r][16hf+c]
-    f32x4 vt[NT][2];
-    f32x4 kk[NT][2];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0, k0 = v0, k1 = v0;
-      if (lw.ok[t]) {
-        const float* src = qkv + lw.pix[t] * (3LL * C) + h * kHeadDim + 8 * g;
-        k0 = *reinterpret_cast<const f32x4*>(src + C);
-        k1 = *reinterpret_cast<const f32x4*>(src + C + 4);
-        v0 = *reinterpret_cast<const f32x4*>(src + 2 * C);
-        v1 = *reinterpret_cast<const f32x4*>(src + 2 * C + 4);
-      }
-      kk[t][0] = k0;
-      kk[t][1] = k1;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const float sv = (8 * g + st == c + 16 * hf) ? 1.f : 0.f;
-          const float vv = st < 4 ? v0[st] : v1[st - 4];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sv, acc, 0, 0, 0);
-        }
-        vt[t][hf] = acc;
-      }
-    }
-    const int hoff = h * T;
-#pragma unroll
-    for (int it = 0; it < NT; ++it) {
-      f32x4 q0 = {0.f, 0.f, 0.f, 0.f}, q1 = q0;
-      if (lw.ok[it]) {
-        const float* src = qkv + lw.pix[it] * (3LL * C) + h * kHeadDim + 8 * g;
-        q0 = *reinterpret_cast<const f32x4*>(src);
-        q1 = *reinterpret_cast<const f32x4*>(src + 4);
-      }
-      f32x4 s[NT];
-#pragma unroll
-      for (int jt = 0; jt < NT; ++jt) {
-        f32x4 acc = lw.score_init(s_bias, hoff, it, jt, g, masked, p.mask_value);
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const float ka = st < 4 ? kk[jt][0][st] : kk[jt][1][st - 4];
-          const float qb = st < 4 ? q0[st] : q1[st - 4];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, qb, acc, 0, 0, 0);
-        }
-        s[jt] = acc;
-      }
-      const float l = softmax_cols<M>(s, p.score_scale);
-      f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
-#pragma unroll
-      for (int jt = 0; jt < NT; ++jt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (S::row_empty(jt, r)) continue;
-          o0 = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[jt][0][r], s[jt][r], o0, 0, 0, 0);
-          o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[jt][1][r], s[jt][r], o1, 0, 0, 0);
-        }
-      if (lw.ok[it]) {
-        const float inv = fast_rcp(l);
-        float* dst = out + lw.pix[it] * C + h * kHeadDim + 4 * g;
-        *reinterpret_cast<f32x4*>(dst) = o0 * inv;
-        *reinterpret_cast<f32x4*>(dst + 16) = o1 * inv;
-      }
-    }
-  }
+  const bool masked = p.has_mask[w] != 0;
+  if (masked) lw.template init_labels<false>(p, w, g, c);
+  for (int h = wave; h < p.nh; h += nwaves) head_f32<M>(p, lw, s_bias, in, out, h, g, c, g_ok, masked);
 }
 
 // ---------------------------------------------------------------------------
 // setup: relative position index, shift mask, region labels, has-mask flags
 
-__device__ int band_of(int pos, int L, int M, int s) {
-  return pos < L - M ? 0 : (pos < L - s ? 1 : 2);
-}
-
-__device__ int region_of(int w, int t, int H, int W, int M, int s) {
-  if (s == 0) return 0;
-  const int nWx = W / M, wy = w / nWx, wx = w - wy * nWx, ty = t / M, tx = t - ty * M;
-  return 3 * band_of(wy * M + ty, H, M, s) + band_of(wx * M + tx, W, M, s);
-}
-
 __global__ void precompute_kernel(int H, int W, int M, int s, int32_t* rel_index, float* mask,
                                   uint8_t* region, uint8_t* has_mask) {
-  const int N = M * M, nW = (H / M) * (W / M);
+  const int N = M * M, nWx = W / M, nW = (H / M) * nWx;
   const long long total = (long long)nW * N * N;
   const long long stride = (long long)gridDim.x * blockDim.x;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
     const int j = (int)(e % N);
     const long long rest = e / N;
     const int i = (int)(rest % N), w = (int)(rest / N);
-    const int li = region_of(w, i, H, W, M, s), lj = region_of(w, j, H, W, M, s);
+    const int wy = w / nWx, wx = w - wy * nWx;
+    const int li = region_label(wy * M + i / M, wx * M + i % M, H, W, M, s);
+    const int lj = region_label(wy * M + j / M, wx * M + j % M, H, W, M, s);
     mask[e] = li == lj ? 0.f : -100.f;
     if (w == 0) {
       const int dy = i / M - j / M, dx = i % M - j % M;
@@ -435,23 +434,29 @@ __global__ void precompute_kernel(int H, int W, int M, int s, int32_t* rel_index
     if (j == 0) region[(long long)w * N + i] = (uint8_t)li;
     if (i == 0 && j == 0) {
       int differ = 0;
-      for (int t = 1; t < N; ++t) differ |= region_of(w, t, H, W, M, s) != li;
+      for (int t = 1; t < N; ++t)
+        differ |= region_label(wy * M + t / M, wx * M + t % M, H, W, M, s) != li;
       has_mask[w] = (uint8_t)differ;
     }
   }
 }
 
 template <int M>
+size_t lds_bytes(int nh) {
+  return ((size_t)Win<M>::T * nh + Win<M>::TAIL) * sizeof(float);
+}
+
+template <int M>
 hipError_t launch_bf16_m(const FwdParams& p, int waves, hipStream_t st) {
-  const size_t lds = (size_t)Win<M>::T * p.nh * sizeof(float);
-  hipLaunchKernelGGL(wattn_fwd_bf16_kernel<M>, dim3(p.total_windows), dim3(64 * waves), lds, st, p);
+  hipLaunchKernelGGL(wattn_fwd_bf16_kernel<M>, dim3(p.total_windows), dim3(64 * waves),
+                     lds_bytes<M>(p.nh), st, p);
   return hipGetLastError();
 }
 
 template <int M>
 hipError_t launch_f32_m(const FwdParams& p, int waves, hipStream_t st) {
-  const size_t lds = (size_t)Win<M>::T * p.nh * sizeof(float);
-  hipLaunchKernelGGL(wattn_fwd_f32_kernel<M>, dim3(p.total_windows), dim3(64 * waves), lds, st, p);
+  hipLaunchKernelGGL(wattn_fwd_f32_kernel<M>, dim3(p.total_windows), dim3(64 * waves),
+                     lds_bytes<M>(p.nh), st, p);
   return hipGetLastError();
 }
 
@@ -468,21 +473,33 @@ hipError_t launch_precompute(int H, int W, int M, int s, int32_t* rel_index, flo
   return hipGetLastError();
 }
 
-#define SWA_DISPATCH(FN)                                                                      \
-  switch (M) {                                                                                \
-    case 1: return FN<1>(p, waves, stream);                                                   \
-    case 2: return FN<2>(p, waves, stream);                                                   \
-    case 3: return FN<3>(p, waves, stream);                                                   \
-    case 4: return FN<4>(p, waves, stream);                                                   \
-    case 5: return FN<5>(p, waves, stream);                                                   \
-    case 6: return FN<6>(p, waves, stream);                                                   \
-    case 7: return FN<7>(p, waves, stream);                                                   \
-    case 8: return FN<8>(p, waves, stream);                                                   \
-    case 9: return FN<9>(p, waves, stream);                                                   \
-    case 10: return FN<10>(p, waves, stream);                                                 \
-    case 11: return FN<11>(p, waves, stream);                                                 \
-    case 12: return FN<12>(p, waves, stream);                                                 \
-    default: return hipErrorInvalidValue;                                                     \
+size_t fwd_lds_bytes(int M, int nh) {
+  switch (M) {
+#define SWA_LDS_CASE(m) \
+  case m: return lds_bytes<m>(nh);
+    SWA_LDS_CASE(1) SWA_LDS_CASE(2) SWA_LDS_CASE(3) SWA_LDS_CASE(4) SWA_LDS_CASE(5)
+    SWA_LDS_CASE(6) SWA_LDS_CASE(7) SWA_LDS_CASE(8) SWA_LDS_CASE(9) SWA_LDS_CASE(10)
+    SWA_LDS_CASE(11) SWA_LDS_CASE(12)
+#undef SWA_LDS_CASE
+    default: return 0;
+  }
+}
+
+#define SWA_DISPATCH(FN)                                \
+  switch (M) {                                          \
+    case 1: return FN<1>(p, waves, stream);             \
+    case 2: return FN<2>(p, waves, stream);             \
+    case 3: return FN<3>(p, waves, stream);             \
+    case 4: return FN<4>(p, waves, stream);             \
+    case 5: return FN<5>(p, waves, stream);             \
+    case 6: return FN<6>(p, waves, stream);             \
+    case 7: return FN<7>(p, waves, stream);             \
+    case 8: return FN<8>(p, waves, stream);             \
+    case 9: return FN<9>(p, waves, stream);             \
+    case 10: return FN<10>(p, waves, stream);           \
+    case 11: return FN<11>(p, waves, stream);           \
+    case 12: return FN<12>(p, waves, stream);           \
+    default: return hipErrorInvalidValue;               \
   }
 
 hipError_t launch_fwd_bf16(int M, const FwdParams& p, int waves, hipStream_t stream) {

@@ -1,0 +1,349 @@
+// Persistent, LDS-staged bf16 forward for windows of at most four 16-token
+// tiles (window <= 8; the Swin windows of 7 included).
+//
+// The forward reads every byte once and does little arithmetic per byte, so
+// its speed is set by how many bytes are in flight to HBM.  Here that number
+// is decoupled from the register budget of the attention math:
+//
+//   unit       (image, window, group of HG heads): 3*HG slices (q, k, v of
+//              each head) x NT tiles, each a 1 KB block of 16 tokens x 64 B
+//              staged in LDS.  The Baidu AIAK-Training talk (jxzklqfsx.com
+//              743345, section 2, WindowAttention case) describes the fused
+//              module as tiles moving through the memory hierarchy of HBM,
+//              shared memory and registers; this is that pipeline on gfx950.
+//   workgroup  4 waves, persistent: it walks a contiguous range of units
+//              (one range per XCD, so neighbouring windows share an L2).
+//   pipeline   the next unit's 16-byte loads are issued into registers right
+//              after the current unit is written to LDS, and stay in flight
+//              while the current unit is computed out of LDS.
+//   loads      wave w loads tile w of every slice: a lane owns one token and
+//              one 16-byte part of it, so the shift/partition index map is
+//              one address per lane per unit.  A load instruction covers 16
+//              tokens x 64 contiguous bytes.
+//   compute    (head, query tile) items are spread over the waves; operands
+//              come from LDS with conflict-free ds_read_b128 (a 1 KB block is
+//              read by the 64 lanes in the order the MFMA layout wants).
+//
+// The attention math per item is the one described in wattn_kernels.hip.
+
+#include "wattn_common.h"
+
+namespace swinattn {
+namespace {
+
+constexpr int kWaves = 4;  // waves per workgroup
+
+template <int M, int HG>
+struct Unit {
+  using S = Win<M>;
+  static constexpr int NT = S::NT;
+  static constexpr int SLICES = 3 * HG;                    // q, k, v of HG heads
+  static constexpr int TPW = (NT + kWaves - 1) / kWaves;   // tiles loaded per wave
+  static constexpr int ITEMS = HG * NT;                    // (head, query tile) items
+  static constexpr int IPW = (ITEMS + kWaves - 1) / kWaves;
+  static constexpr int BLOCK = 1024;                       // 16 tokens x 64 bytes
+  static constexpr int BYTES = SLICES * NT * BLOCK;
+  static constexpr int block(int s, int t) { return (s * NT + t) * BLOCK; }
+};
+
+// Window coordinates (row, column) of in-tile token u of tile t.
+template <int M>
+SWA_INLINE void tile_token(int t, int u, int& ty, int& tx) {
+  ty = 4 * (t / Win<M>::Q) + u / 4;
+  tx = 4 * (t % Win<M>::Q) + u % 4;
+}
+
+// Flattened image position (within the launch) of window token (ty, tx);
+// tokens outside the window stand in for the window's first token.
+SWA_INLINE unsigned token_pixel(const FwdParams& p, int M, int b, int wy, int wx, int ty, int tx,
+                                bool ok) {
+  int y = wy * M + (ok ? ty : 0) + p.shift, x = wx * M + (ok ? tx : 0) + p.shift;
+  y -= y >= p.H ? p.H : 0;
+  x -= x >= p.W ? p.W : 0;
+  return ((unsigned)b * p.H + y) * p.W + x;
+}
+
+template <int M, int HG>
+__global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
+  using S = Win<M>;
+  using U = Unit<M, HG>;
+  constexpr int NT = S::NT, NK = S::NK;
+  extern __shared__ float s_lds[];
+  float* s_bias = s_lds;
+  const int bias_floats = p.nh * S::T + S::TAIL;
+  char* s_unit = reinterpret_cast<char*>(s_lds) + ((bias_floats * 4 + 15) & ~15);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gq = lane & 3, cq = lane >> 2;    // load layout: 16-byte part, token
+  const int g = lane >> 4, c = lane & 15;     // MFMA layout: lane group, token
+  const int nh = p.nh;
+  const unsigned Cb = (unsigned)nh * kHeadDim * 2;  // bytes of one q (k, v, out) row
+  const char* in = static_cast<const char*>(p.qkv);
+  char* out = static_cast<char*>(p.out);
+  const int units = p.units;
+
+  // this workgroup's units: one contiguous range per XCD, interleaved over
+  // the XCD's workgroups
+  const int G = gridDim.x, id = blockIdx.x;
+  int u, u_step, u_end;
+  if ((G & 7) == 0) {
+    const int x = id & 7, per = G >> 3;
+    const long long r0 = (long long)units * x / 8, r1 = (long long)units * (x + 1) / 8;
+    u = (int)r0 + (id >> 3);
+    u_step = per;
+    u_end = (int)r1;
+  } else {
+    u = id;
+    u_step = G;
+    u_end = units;
+  }
+
+  // stage the bias table of every head (reversed, divided by the scale)
+  stage_bias<M>(s_bias, p.table, nh, p.inv_scale);
+
+  // register-staged loads of one unit: slice s, tile wv + 4k of this wave
+  bf16x8 R[U::SLICES][U::TPW];
+  auto issue_loads = [&](int uu) {
+    const int hg = uu % p.nhg, bw = uu / p.nhg;
+    const int b = bw / p.nW, w = bw - b * p.nW;
+    const int wy = w / p.nWx, wx = w - wy * p.nWx;
+#pragma unroll
+    for (int k = 0; k < U::TPW; ++k) {
+      const int t = wv + kWaves * k;
+      if (t < NT) {
+        int ty, tx;
+        tile_token<M>(t, cq, ty, tx);
+        const bool ok = ty < M && tx < M;
+        const unsigned pix = token_pixel(p, M, b, wy, wx, ty, tx, ok);
+        const char* src = in + pix * (3u * Cb) + (unsigned)hg * HG * kHeadDim * 2 + 16u * gq;
+#pragma unroll
+        for (int s = 0; s < U::SLICES; ++s)
+          R[s][k] = *reinterpret_cast<const bf16x8*>(src + (s / HG) * Cb + (s % HG) * kHeadDim * 2);
+      }
+    }
+  };
+  auto write_unit = [&]() {
+#pragma unroll
+    for (int k = 0; k < U::TPW; ++k) {
+      const int t = wv + kWaves * k;
+      if (t < NT) {
+#pragma unroll
+        for (int s = 0; s < U::SLICES; ++s)
+          *reinterpret_cast<bf16x8*>(s_unit + U::block(s, t) + lane * 16) = R[s][k];
+      }
+    }
+  };
+
+  const bool g_ok = g < S::LG;  // lane group is a window row in the last row group
+  bf16x8 sel[2], ones;           // channel-half selectors (transpose MFMA), ones (row sums)
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sel[hf][s] = (8 * g + s == c + 16 * hf) ? (__bf16)1.f : (__bf16)0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ones[s] = (__bf16)1.f;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+  if (u < u_end) issue_loads(u);
+  __syncthreads();  // bias table visible
+
+  for (; u < u_end; u += u_step) {
+    write_unit();
+    __syncthreads();  // unit visible to every wave
+    const int un = u + u_step;
+    if (un < u_end) issue_loads(un);
+
+    const int hg = u % p.nhg, bw = u / p.nhg;
+    const int b = bw / p.nW, w = bw - b * p.nW;
+    const int wy = w / p.nWx, wx = w - wy * p.nWx;
+    const bool masked = p.has_mask[w] != 0;
+
+    // key-side mask operands of this window (see LaneWindow::init_labels)
+    bf16x8 mask_a[NT];
+    if (masked) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        int ty, tx;
+        tile_token<M>(t, c, ty, tx);
+        const int loc = 2 * (wy * M + ty >= p.H - p.shift) + (wx * M + tx >= p.W - p.shift);
+        bf16x8 a = {};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) a[k] = loc == g ? (__bf16)p.mask_pieces[k] : (__bf16)0.f;
+        mask_a[t] = a;
+      }
+    }
+
+    int cur = -1;
+    bf16x8 kt[NT], va[2][NK];
+    for (int i = 0; i < U::IPW; ++i) {
+      const int item = wv * U::IPW + i;
+      if (item >= U::ITEMS) break;
+      const int hl = item / NT, it = item - hl * NT;
+      const int h = hg * HG + hl;
+      if (hl != cur) {
+        cur = hl;
+        // key tiles and the transposed value tiles of head hl
+        bf16x8 vt[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          kt[t] = *reinterpret_cast<const bf16x8*>(s_unit + U::block(HG + hl, t) + (4 * c + g) * 16);
+          vt[t] = *reinterpret_cast<const bf16x8*>(s_unit + U::block(2 * HG + hl, t) + (4 * c + g) * 16);
+        }
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[2 * kk], sel[hf], z, 0, 0, 0);
+            f32x4 d1 = z;
+            if (2 * kk + 1 < NT)
+              d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[2 * kk + 1], sel[hf], z, 0, 0, 0);
+            bf16x8 a;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              a[r] = (__bf16)d0[r];
+              a[4 + r] = (__bf16)d1[r];
+            }
+            va[hf][kk] = a;
+          }
+      }
+      // the query tile and what the lane needs about its query token
+      const bf16x8 q = *reinterpret_cast<const bf16x8*>(s_unit + U::block(hl, it) + (4 * c + g) * 16);
+      int ty, tx;
+      tile_token<M>(it, c, ty, tx);
+      const bool ok = ty < M && tx < M;
+      const int qbase = h * S::T + S::T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
+      bf16x8 mask_b = {};
+      if (masked) {
+        const int loc = 2 * (wy * M + ty >= p.H - p.shift) + (wx * M + tx >= p.W - p.shift);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) mask_b[k] = loc == g ? (__bf16)0.f : (__bf16)-1.f;
+      }
+
+      f32x4 sc[NT];
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        f32x4 acc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (!S::col_ok(jt, r)) {
+            acc[r] = -__builtin_inff();
+            continue;
+          }
+          float v = s_bias[qbase + S::E(jt) + r];
+          if (!S::rows_all(jt)) v = g_ok ? v : -__builtin_inff();
+          acc[r] = v;
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[jt], q, acc, 0, 0, 0);
+        if (masked) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mask_a[jt], mask_b, acc, 0, 0, 0);
+        sc[jt] = acc;
+      }
+      softmax_numerators<M>(sc, p.score_scale);
+      bf16x8 pb[NK];
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pb[kk][r] = (__bf16)sc[2 * kk][r];
+          pb[kk][4 + r] = (2 * kk + 1 < NT) ? (__bf16)sc[2 * kk + 1][r] : (__bf16)0.f;
+        }
+      f32x4 o0 = z, o1 = z, l4 = z;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][kk], pb[kk], o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][kk], pb[kk], o1, 0, 0, 0);
+        l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[kk], l4, 0, 0, 0);
+      }
+      if (ok) {
+        const float inv = fast_rcp(l4[0]);
+        bf16x4 w0, w1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          w0[r] = (__bf16)(o0[r] * inv);
+          w1[r] = (__bf16)(o1[r] * inv);
+        }
+        const unsigned pix = token_pixel(p, M, b, wy, wx, ty, tx, true);
+        char* dst = out + pix * Cb + h * kHeadDim * 2 + 8 * g;
+        *reinterpret_cast<bf16x4*>(dst) = w0;
+        *reinterpret_cast<bf16x4*>(dst + 32) = w1;
+      }
+    }
+    __syncthreads();  // every wave is done with the unit before it is overwritten
+  }
+}
+
+template <int M, int HG>
+size_t lds_bytes_mh(int nh) {
+  const size_t bias = ((size_t)nh * Win<M>::T + Win<M>::TAIL) * sizeof(float);
+  return ((bias + 15) & ~size_t(15)) + Unit<M, HG>::BYTES;
+}
+
+template <int M, int HG>
+hipError_t launch_mh(const FwdParams& p, int cus, hipStream_t st) {
+  const size_t lds = lds_bytes_mh<M, HG>(p.nh);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_fwd_bf16_persistent<M, HG>,
+                                                   kWaves * 64, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  long long grid = (long long)cus * per_cu;
+  if (grid > p.units) grid = p.units;
+  if (grid >= 8) grid &= ~7LL;  // whole XCD rounds: one contiguous unit range per XCD
+  hipLaunchKernelGGL((wattn_fwd_bf16_persistent<M, HG>), dim3((unsigned)grid), dim3(kWaves * 64),
+                     lds, st, p);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_m(int HG, const FwdParams& p, int cus, hipStream_t st) {
+  switch (HG) {
+    case 1: return launch_mh<M, 1>(p, cus, st);
+    case 2: return launch_mh<M, 2>(p, cus, st);
+    case 3: return launch_mh<M, 3>(p, cus, st);
+    case 4: return launch_mh<M, 4>(p, cus, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int M>
+size_t lds_m(int HG, int nh) {
+  switch (HG) {
+    case 1: return lds_bytes_mh<M, 1>(nh);
+    case 2: return lds_bytes_mh<M, 2>(nh);
+    case 3: return lds_bytes_mh<M, 3>(nh);
+    case 4: return lds_bytes_mh<M, 4>(nh);
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+size_t persistent_lds_bytes(int M, int HG, int nh) {
+  switch (M) {
+    case 1: return lds_m<1>(HG, nh);
+    case 2: return lds_m<2>(HG, nh);
+    case 3: return lds_m<3>(HG, nh);
+    case 4: return lds_m<4>(HG, nh);
+    case 5: return lds_m<5>(HG, nh);
+    case 6: return lds_m<6>(HG, nh);
+    case 7: return lds_m<7>(HG, nh);
+    case 8: return lds_m<8>(HG, nh);
+    default: return 0;
+  }
+}
+
+hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int cus,
+                                      hipStream_t stream) {
+  switch (M) {
+    case 1: return launch_m<1>(HG, p, cus, stream);
+    case 2: return launch_m<2>(HG, p, cus, stream);
+    case 3: return launch_m<3>(HG, p, cus, stream);
+    case 4: return launch_m<4>(HG, p, cus, stream);
+    case 5: return launch_m<5>(HG, p, cus, stream);
+    case 6: return launch_m<6>(HG, p, cus, stream);
+    case 7: return launch_m<7>(HG, p, cus, stream);
+    case 8: return launch_m<8>(HG, p, cus, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swinattn
