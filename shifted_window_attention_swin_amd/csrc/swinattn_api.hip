@@ -46,7 +46,8 @@ int compute_units(int dev) {
   return g_cus[dev];
 }
 
-// heads per unit of the persistent kernel
+// heads per unit of the persistent kernel: 2 (each wave then owns one head
+// and two query tiles), else 3, else 1
 int head_group(int heads) {
   if (heads % 2 == 0) return 2;
   if (heads % 3 == 0) return 3;

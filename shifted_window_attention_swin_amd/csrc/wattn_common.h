@@ -10,6 +10,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define SWA_INLINE __device__ __forceinline__
 
@@ -54,6 +55,22 @@ SWA_INLINE int band_of(int pos, int L, int M, int s) {
 }
 SWA_INLINE int region_label(int yy, int xx, int H, int W, int M, int s) {
   return s == 0 ? 0 : 3 * band_of(yy, H, M, s) + band_of(xx, W, M, s);
+}
+
+// Channel that column c of a value-transpose tile of channel half hf
+// carries.  With this order, row 4g+r of output tile hf is channel
+// 8g + 4hf + r: each lane ends up with 8 consecutive channels of its query
+// token (one 16-byte store) instead of two 4-channel pieces 32 bytes apart.
+SWA_INLINE int out_channel(int hf, int c) { return 8 * (c / 4) + 4 * hf + c % 4; }
+
+// ds_read_b64_tr_b16: transposing 8-byte LDS read (see its use for the lane
+// mapping).  `p` points into LDS.
+SWA_INLINE bf16x4 lds_read_tr(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 SWA_INLINE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -69,7 +69,7 @@ struct LaneWindow {
       x -= x >= p.W ? p.W : 0;
       const unsigned pix = ((unsigned)b * p.H + y) * p.W + x;
       in_off[t] = (pix * 3u * C + 8u * g) * elem;
-      out_off[t] = (pix * C + 4u * g) * elem;
+      out_off[t] = (pix * C + 8u * g) * elem;
     }
   }
 
@@ -229,15 +229,13 @@ SWA_INLINE void head_bf16(const HeadCtx& hc, const LaneWindow<M>& lw, int h, boo
     }
     if (lw.ok[it]) {
       const float inv = fast_rcp(l4[0]);
-      bf16x4 w0, w1;
+      bf16x8 wv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        w0[r] = (__bf16)(o0[r] * inv);
-        w1[r] = (__bf16)(o1[r] * inv);
+        wv[r] = (__bf16)(o0[r] * inv);
+        wv[4 + r] = (__bf16)(o1[r] * inv);
       }
-      char* dst = out_h + lw.out_off[it];
-      *reinterpret_cast<bf16x4*>(dst) = w0;
-      *reinterpret_cast<bf16x4*>(dst + 32) = w1;
+      *reinterpret_cast<bf16x8*>(out_h + lw.out_off[it]) = wv;
     }
     // keep query tiles apart: interleaving them only raises register pressure
     __builtin_amdgcn_sched_barrier(0);
@@ -302,7 +300,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_kernel(FwdParams p) {
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      hc.sel[hf][s] = (8 * g + s == c + 16 * hf) ? (__bf16)1.f : (__bf16)0.f;
+      hc.sel[hf][s] = (8 * g + s == out_channel(hf, c)) ? (__bf16)1.f : (__bf16)0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) hc.ones[s] = (__bf16)1.f;
   __syncthreads();
@@ -342,7 +340,7 @@ SWA_INLINE void head_f32(const FwdParams& p, const LaneWindow<M>& lw, const floa
       f32x4 acc = z;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const float sv = (8 * g + st == c + 16 * hf) ? 1.f : 0.f;
+        const float sv = (8 * g + st == out_channel(hf, c)) ? 1.f : 0.f;
         const float vv = st < 4 ? v0[st] : v1[st - 4];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sv, acc, 0, 0, 0);
       }
@@ -385,7 +383,7 @@ SWA_INLINE void head_f32(const FwdParams& p, const LaneWindow<M>& lw, const floa
       const float inv = fast_rcp(l4[0]);
       char* dst = out + h * kHeadDim * 4 + lw.out_off[it];
       *reinterpret_cast<f32x4*>(dst) = o0 * inv;
-      *reinterpret_cast<f32x4*>(dst + 64) = o1 * inv;
+      *reinterpret_cast<f32x4*>(dst + 16) = o1 * inv;
     }
   }
 }

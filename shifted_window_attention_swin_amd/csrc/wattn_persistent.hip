@@ -32,6 +32,10 @@ namespace swinattn {
 namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup
+#ifndef SWA_PF_DEPTH
+#define SWA_PF_DEPTH 1
+#endif
+constexpr int kDepth = SWA_PF_DEPTH;  // units whose loads are in flight during the math
 
 template <int M, int HG>
 struct Unit {
@@ -41,6 +45,8 @@ struct Unit {
   static constexpr int TPW = (NT + kWaves - 1) / kWaves;   // tiles loaded per wave
   static constexpr int ITEMS = HG * NT;                    // (head, query tile) items
   static constexpr int IPW = (ITEMS + kWaves - 1) / kWaves;
+  // every wave's items belong to one head: key / value tiles load once
+  static constexpr bool ONE_HEAD = ITEMS % kWaves == 0 && NT % IPW == 0;
   static constexpr int BLOCK = 1024;                       // 16 tokens x 64 bytes
   static constexpr int BYTES = SLICES * NT * BLOCK;
   static constexpr int block(int s, int t) { return (s * NT + t) * BLOCK; }
@@ -102,12 +108,25 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   // stage the bias table of every head (reversed, divided by the scale)
   stage_bias<M>(s_bias, p.table, nh, p.inv_scale);
 
+  // unit u -> (head group, image, window); decoded once, used for the loads
+  // and, one iteration later, for the math
+  struct Pos {
+    int hg, b, w, wy, wx;
+  };
+  auto decode = [&](int uu) {
+    Pos q;
+    q.hg = uu % p.nhg;
+    const int bw = uu / p.nhg;
+    q.b = bw / p.nW;
+    q.w = bw - q.b * p.nW;
+    q.wy = q.w / p.nWx;
+    q.wx = q.w - q.wy * p.nWx;
+    return q;
+  };
+
   // register-staged loads of one unit: slice s, tile wv + 4k of this wave
-  bf16x8 R[U::SLICES][U::TPW];
-  auto issue_loads = [&](int uu) {
-    const int hg = uu % p.nhg, bw = uu / p.nhg;
-    const int b = bw / p.nW, w = bw - b * p.nW;
-    const int wy = w / p.nWx, wx = w - wy * p.nWx;
+  using Regs = u32x4[U::SLICES][U::TPW];  // raw 16-byte chunks
+  auto issue_loads = [&](Regs& R, const Pos& q) {
 #pragma unroll
     for (int k = 0; k < U::TPW; ++k) {
       const int t = wv + kWaves * k;
@@ -115,50 +134,36 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
         int ty, tx;
         tile_token<M>(t, cq, ty, tx);
         const bool ok = ty < M && tx < M;
-        const unsigned pix = token_pixel(p, M, b, wy, wx, ty, tx, ok);
-        const char* src = in + pix * (3u * Cb) + (unsigned)hg * HG * kHeadDim * 2 + 16u * gq;
+        const unsigned pix = token_pixel(p, M, q.b, q.wy, q.wx, ty, tx, ok);
+        const char* src = in + pix * (3u * Cb) + (unsigned)q.hg * HG * kHeadDim * 2 + 16u * gq;
 #pragma unroll
         for (int s = 0; s < U::SLICES; ++s)
-          R[s][k] = *reinterpret_cast<const bf16x8*>(src + (s / HG) * Cb + (s % HG) * kHeadDim * 2);
+          R[s][k] = *reinterpret_cast<const u32x4*>(src + (s / HG) * Cb + (s % HG) * kHeadDim * 2);
       }
     }
   };
-  auto write_unit = [&]() {
+  auto write_unit = [&](const Regs& R) {
 #pragma unroll
     for (int k = 0; k < U::TPW; ++k) {
       const int t = wv + kWaves * k;
       if (t < NT) {
 #pragma unroll
         for (int s = 0; s < U::SLICES; ++s)
-          *reinterpret_cast<bf16x8*>(s_unit + U::block(s, t) + lane * 16) = R[s][k];
+          *reinterpret_cast<u32x4*>(s_unit + U::block(s, t) + lane * 16) = R[s][k];
       }
     }
   };
 
   const bool g_ok = g < S::LG;  // lane group is a window row in the last row group
-  bf16x8 sel[2], ones;           // channel-half selectors (transpose MFMA), ones (row sums)
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sel[hf][s] = (8 * g + s == c + 16 * hf) ? (__bf16)1.f : (__bf16)0.f;
+  bf16x8 ones;                   // A operand of the row-sum MFMA
 #pragma unroll
   for (int s = 0; s < 8; ++s) ones[s] = (__bf16)1.f;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
-  if (u < u_end) issue_loads(u);
-  __syncthreads();  // bias table visible
-
-  for (; u < u_end; u += u_step) {
-    write_unit();
-    __syncthreads();  // unit visible to every wave
-    const int un = u + u_step;
-    if (un < u_end) issue_loads(un);
-
-    const int hg = u % p.nhg, bw = u / p.nhg;
-    const int b = bw / p.nW, w = bw - b * p.nW;
-    const int wy = w / p.nWx, wx = w - wy * p.nWx;
+  // the math of one unit, out of LDS
+  auto process = [&](const Pos& pos) {
+    const int hg = pos.hg, b = pos.b, w = pos.w, wy = pos.wy, wx = pos.wx;
     const bool masked = p.has_mask[w] != 0;
-
     // key-side mask operands of this window (see LaneWindow::init_labels)
     bf16x8 mask_a[NT];
     if (masked) {
@@ -174,38 +179,42 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       }
     }
 
-    int cur = -1;
+    // key tiles and the transposed value tiles of local head hl
     bf16x8 kt[NT], va[2][NK];
+    auto load_head = [&](int hl) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        kt[t] = *reinterpret_cast<const bf16x8*>(s_unit + U::block(HG + hl, t) + (4 * c + g) * 16);
+      // V^T straight from LDS with the transposing read: in each group of 16
+      // lanes, lane i receives element i%4 of the 8-byte chunks read by lanes
+      // i/4, i/4+4, i/4+8, i/4+12.  Lane L reading bytes 8*hf.. of its own
+      // 16-byte slot of a value tile therefore receives, for k = 0..3, channel
+      // out_channel(hf, c) of in-tile token 4g+k: rows 4g..4g+3 of V^T, the
+      // A-operand slots of key tile t.
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int t1 = 2 * kk + 1 < NT ? 2 * kk + 1 : 2 * kk;  // odd tile count: any finite data
+          const bf16x4 lo = lds_read_tr(s_unit + U::block(2 * HG + hl, 2 * kk) + lane * 16 + 8 * hf);
+          const bf16x4 hi = lds_read_tr(s_unit + U::block(2 * HG + hl, t1) + lane * 16 + 8 * hf);
+          va[hf][kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    int cur = -1;
+    if (U::ONE_HEAD) {
+      cur = wv * U::IPW / NT;
+      load_head(cur);
+    }
+#pragma unroll
     for (int i = 0; i < U::IPW; ++i) {
       const int item = wv * U::IPW + i;
       if (item >= U::ITEMS) break;
       const int hl = item / NT, it = item - hl * NT;
       const int h = hg * HG + hl;
-      if (hl != cur) {
+      if (!U::ONE_HEAD && hl != cur) {
         cur = hl;
-        // key tiles and the transposed value tiles of head hl
-        bf16x8 vt[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          kt[t] = *reinterpret_cast<const bf16x8*>(s_unit + U::block(HG + hl, t) + (4 * c + g) * 16);
-          vt[t] = *reinterpret_cast<const bf16x8*>(s_unit + U::block(2 * HG + hl, t) + (4 * c + g) * 16);
-        }
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[2 * kk], sel[hf], z, 0, 0, 0);
-            f32x4 d1 = z;
-            if (2 * kk + 1 < NT)
-              d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[2 * kk + 1], sel[hf], z, 0, 0, 0);
-            bf16x8 a;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              a[r] = (__bf16)d0[r];
-              a[4 + r] = (__bf16)d1[r];
-            }
-            va[hf][kk] = a;
-          }
+        load_head(hl);
       }
       // the query tile and what the lane needs about its query token
       const bf16x8 q = *reinterpret_cast<const bf16x8*>(s_unit + U::block(hl, it) + (4 * c + g) * 16);
@@ -256,19 +265,65 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       }
       if (ok) {
         const float inv = fast_rcp(l4[0]);
-        bf16x4 w0, w1;
+        bf16x8 ov;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          w0[r] = (__bf16)(o0[r] * inv);
-          w1[r] = (__bf16)(o1[r] * inv);
+          ov[r] = (__bf16)(o0[r] * inv);
+          ov[4 + r] = (__bf16)(o1[r] * inv);
         }
         const unsigned pix = token_pixel(p, M, b, wy, wx, ty, tx, true);
-        char* dst = out + pix * Cb + h * kHeadDim * 2 + 8 * g;
-        *reinterpret_cast<bf16x4*>(dst) = w0;
-        *reinterpret_cast<bf16x4*>(dst + 32) = w1;
+        *reinterpret_cast<bf16x8*>(out + pix * Cb + h * kHeadDim * 2 + 16 * g) = ov;
       }
     }
-    __syncthreads();  // every wave is done with the unit before it is overwritten
+  };
+
+  // software pipeline: the loads of the next kDepth units are in flight
+  // while a unit is written to LDS and computed
+  if (kDepth == 1) {
+    Regs R;
+    Pos nxt = decode(u);
+    if (u < u_end) issue_loads(R, nxt);
+    __syncthreads();  // bias table visible
+    for (; u < u_end; u += u_step) {
+      write_unit(R);
+      __syncthreads();  // unit visible to every wave
+      const Pos cur = nxt;
+      if (u + u_step < u_end) {
+        nxt = decode(u + u_step);
+        issue_loads(R, nxt);
+      }
+      process(cur);
+      __syncthreads();  // every wave is done with the unit before it is overwritten
+    }
+  } else {
+    Regs R0, R1;
+    Pos p0 = decode(u), p1 = decode(u + u_step);
+    if (u < u_end) issue_loads(R0, p0);
+    if (u + u_step < u_end) issue_loads(R1, p1);
+    __syncthreads();  // bias table visible
+    while (u < u_end) {
+      write_unit(R0);
+      __syncthreads();
+      Pos cur = p0;
+      if (u + 2 * u_step < u_end) {
+        p0 = decode(u + 2 * u_step);
+        issue_loads(R0, p0);
+      }
+      process(cur);
+      __syncthreads();
+      u += u_step;
+      if (u >= u_end) break;
+      write_unit(R1);
+      __syncthreads();
+      cur = p1;
+      if (u + 2 * u_step < u_end) {
+        p1 = decode(u + 2 * u_step);
+        issue_loads(R1, p1);
+      }
+      process(cur);
+      __syncthreads();
+      u += u_step;
+    }
   }
 }
 
