@@ -25,12 +25,18 @@ METRIC = "shifted-window attn fwd GB/s & TFLOP/s (Swin-L stage1, bf16, B=64); % 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 * 2 ** 20
-KERNEL_SRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc", "wattn_kernels.hip")
+CSRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every kernel source file: a committed traffic measurement is
+    only reported while the sources it was taken on are unchanged."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic(B, H, W, heads, head_dim, window, elem=2):
@@ -40,6 +46,16 @@ def algorithmic(B, H, W, heads, head_dim, window, elem=2):
     C = heads * head_dim
     N = window * window
     return 4 * C * T * elem, 4 * N * C * T
+
+
+def fwd_kernel_name(window: int, heads: int) -> str:
+    """Name of the forward kernel the library launches (mirrors its dispatch:
+    windows up to 8 use the persistent kernel with head groups of 2, else 3,
+    else 1)."""
+    if window <= 8:
+        hg = 2 if heads % 2 == 0 else 3 if heads % 3 == 0 else 1
+        return f"wattn_fwd_bf16_persistent<{window}, {hg}>"
+    return f"wattn_fwd_bf16_kernel<{window}>"
 
 
 def measured_traffic(workload: str):
@@ -188,7 +204,7 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"wattn_fwd_bf16_kernel<{M}>",
+                     "kernel": fwd_kernel_name(M, nh),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "alg_bytes_per_launch": nbytes // len(shifts),
                      "alg_flops_per_launch": nflops // len(shifts),
