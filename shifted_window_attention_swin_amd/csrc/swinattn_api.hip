@@ -46,9 +46,11 @@ int compute_units(int dev) {
   return g_cus[dev];
 }
 
-// heads per unit of the persistent kernel: 2 (each wave then owns one head
-// and two query tiles), else 3, else 1
-int head_group(int heads) {
+// heads per unit of the persistent kernel.  Windows of up to 4 tiles: 2
+// (each wave then owns one head and two query tiles), else 3, else 1.
+// Larger windows: 1 (a unit is already 9 tiles per slice).
+int head_group(int heads, int M) {
+  if ((M + 3) / 4 > 2) return 1;
   if (heads % 2 == 0) return 2;
   if (heads % 3 == 0) return 3;
   return 1;
@@ -129,7 +131,7 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
     }
   }
   // bf16 windows of up to 4 tiles go to the persistent LDS-staged kernel
-  const int hg = head_group(heads);
+  const int hg = head_group(heads, M);
   const bool persistent = bf16 && M <= kMaxPersistentWindow &&
                           persistent_lds_bytes(M, hg, heads) <= (size_t)kMaxTableLds;
   const int cus = persistent ? compute_units(dev) : 0;

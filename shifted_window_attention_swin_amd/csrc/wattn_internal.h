@@ -42,10 +42,11 @@ hipError_t launch_fwd_bf16(int M, const FwdParams& p, int waves, hipStream_t str
 size_t fwd_lds_bytes(int M, int nh);
 hipError_t launch_fwd_f32(int M, const FwdParams& p, int waves, hipStream_t stream);
 
-// Persistent LDS-staged bf16 forward (windows of at most 4 tiles, M <= 8):
-// heads are processed in groups of HG (1..4, HG divides nh); `cus` = compute
-// units of the device (the grid fills them at the kernel's occupancy).
-constexpr int kMaxPersistentWindow = 8;
+// Persistent LDS-staged bf16 forward (every window up to kMaxWindow): heads
+// are processed in groups of HG (1..4, HG divides nh; 1 for windows of more
+// than 4 tiles); `cus` = compute units of the device (the grid fills them at
+// the kernel's occupancy).
+constexpr int kMaxPersistentWindow = 12;
 hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int cus,
                                       hipStream_t stream);
 size_t persistent_lds_bytes(int M, int HG, int nh);

@@ -1,5 +1,5 @@
-// Persistent, LDS-staged bf16 forward for windows of at most four 16-token
-// tiles (window <= 8; the Swin windows of 7 included).
+// Persistent, LDS-staged bf16 forward (windows up to 12: 1, 4 or 9 tiles of
+// 16 tokens; the Swin windows of 7 and 12 included).
 //
 // The forward reads every byte once and does little arithmetic per byte, so
 // its speed is set by how many bytes are in flight to HBM.  Here that number
@@ -48,8 +48,13 @@ struct Unit {
   // every wave's items belong to one head: key / value tiles load once
   static constexpr bool ONE_HEAD = ITEMS % kWaves == 0 && NT % IPW == 0;
   static constexpr int BLOCK = 1024;                       // 16 tokens x 64 bytes
-  static constexpr int BYTES = SLICES * NT * BLOCK;
+  // windows of up to 4 tiles keep key tiles, V^T and mask operands in
+  // registers for all items of a wave; larger windows re-read them from LDS
+  static constexpr bool HOLD = NT <= 4;
+  static constexpr int MASK_BYTES = HOLD ? 0 : NT * BLOCK;  // key-side mask operands
+  static constexpr int BYTES = SLICES * NT * BLOCK + MASK_BYTES;
   static constexpr int block(int s, int t) { return (s * NT + t) * BLOCK; }
+  static constexpr int mask_block(int t) { return (SLICES * NT + t) * BLOCK; }
 };
 
 // Window coordinates (row, column) of in-tile token u of tile t.
@@ -142,6 +147,27 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       }
     }
   };
+  // key-side mask operands of a window for large windows: wave w writes
+  // tiles w, w+4, ...  (each lane's operand depends on the lane only)
+  auto write_mask = [&](const Pos& q) {
+    if constexpr (!U::HOLD) {
+      if (p.has_mask[q.w]) {
+#pragma unroll
+        for (int k = 0; k < U::TPW; ++k) {
+          const int t = wv + kWaves * k;
+          if (t < NT) {
+            int ty, tx;
+            tile_token<M>(t, c, ty, tx);
+            const int loc = 2 * (q.wy * M + ty >= p.H - p.shift) + (q.wx * M + tx >= p.W - p.shift);
+            bf16x8 a = {};
+#pragma unroll
+            for (int j = 0; j < 3; ++j) a[j] = loc == g ? (__bf16)p.mask_pieces[j] : (__bf16)0.f;
+            *reinterpret_cast<bf16x8*>(s_unit + U::mask_block(t) + lane * 16) = a;
+          }
+        }
+      }
+    }
+  };
   auto write_unit = [&](const Regs& R) {
 #pragma unroll
     for (int k = 0; k < U::TPW; ++k) {
@@ -164,42 +190,52 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   auto process = [&](const Pos& pos) {
     const int hg = pos.hg, b = pos.b, w = pos.w, wy = pos.wy, wx = pos.wx;
     const bool masked = p.has_mask[w] != 0;
-    // key-side mask operands of this window (see LaneWindow::init_labels)
-    bf16x8 mask_a[NT];
+    // key-side mask operand of key tile t for this lane (see
+    // LaneWindow::init_labels): it depends on the lane only, not the head
+    auto key_mask = [&](int t) {
+      int ty, tx;
+      tile_token<M>(t, c, ty, tx);
+      const int loc = 2 * (wy * M + ty >= p.H - p.shift) + (wx * M + tx >= p.W - p.shift);
+      bf16x8 a = {};
+#pragma unroll
+      for (int k = 0; k < 3; ++k) a[k] = loc == g ? (__bf16)p.mask_pieces[k] : (__bf16)0.f;
+      return a;
+    };
+    bf16x8 mask_a[U::HOLD ? NT : 1];
     if (masked) {
+      if constexpr (U::HOLD) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        int ty, tx;
-        tile_token<M>(t, c, ty, tx);
-        const int loc = 2 * (wy * M + ty >= p.H - p.shift) + (wx * M + tx >= p.W - p.shift);
-        bf16x8 a = {};
-#pragma unroll
-        for (int k = 0; k < 3; ++k) a[k] = loc == g ? (__bf16)p.mask_pieces[k] : (__bf16)0.f;
-        mask_a[t] = a;
+        for (int t = 0; t < NT; ++t) mask_a[t] = key_mask(t);
       }
     }
 
     // key tiles and the transposed value tiles of local head hl
-    bf16x8 kt[NT], va[2][NK];
+    constexpr int NH = U::HOLD ? NT : 1, NKH = U::HOLD ? NK : 1;
+    bf16x8 kt[NH], va[2][NKH];
+    auto key_tile = [&](int hl, int t) {
+      return *reinterpret_cast<const bf16x8*>(s_unit + U::block(HG + hl, t) + (4 * c + g) * 16);
+    };
+    // V^T straight from LDS with the transposing read: in each group of 16
+    // lanes, lane i receives element i%4 of the 8-byte chunks read by lanes
+    // i/4, i/4+4, i/4+8, i/4+12.  Lane L reading bytes 8*hf.. of its own
+    // 16-byte slot of a value tile therefore receives, for k = 0..3, channel
+    // out_channel(hf, c) of in-tile token 4g+k: rows 4g..4g+3 of V^T, the
+    // A-operand slots of key tile t.
+    auto value_t = [&](int hl, int kk, int hf) {
+      const int t1 = 2 * kk + 1 < NT ? 2 * kk + 1 : 2 * kk;  // odd tile count: any finite data
+      const bf16x4 lo = lds_read_tr(s_unit + U::block(2 * HG + hl, 2 * kk) + lane * 16 + 8 * hf);
+      const bf16x4 hi = lds_read_tr(s_unit + U::block(2 * HG + hl, t1) + lane * 16 + 8 * hf);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
     auto load_head = [&](int hl) {
+      if constexpr (U::HOLD) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        kt[t] = *reinterpret_cast<const bf16x8*>(s_unit + U::block(HG + hl, t) + (4 * c + g) * 16);
-      // V^T straight from LDS with the transposing read: in each group of 16
-      // lanes, lane i receives element i%4 of the 8-byte chunks read by lanes
-      // i/4, i/4+4, i/4+8, i/4+12.  Lane L reading bytes 8*hf.. of its own
-      // 16-byte slot of a value tile therefore receives, for k = 0..3, channel
-      // out_channel(hf, c) of in-tile token 4g+k: rows 4g..4g+3 of V^T, the
-      // A-operand slots of key tile t.
+        for (int t = 0; t < NT; ++t) kt[t] = key_tile(hl, t);
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
+        for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int t1 = 2 * kk + 1 < NT ? 2 * kk + 1 : 2 * kk;  // odd tile count: any finite data
-          const bf16x4 lo = lds_read_tr(s_unit + U::block(2 * HG + hl, 2 * kk) + lane * 16 + 8 * hf);
-          const bf16x4 hi = lds_read_tr(s_unit + U::block(2 * HG + hl, t1) + lane * 16 + 8 * hf);
-          va[hf][kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+          for (int hf = 0; hf < 2; ++hf) va[hf][kk] = value_t(hl, kk, hf);
+      }
     };
     int cur = -1;
     if (U::ONE_HEAD) {
@@ -243,8 +279,16 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
           if (!S::rows_all(jt)) v = g_ok ? v : -__builtin_inff();
           acc[r] = v;
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[jt], q, acc, 0, 0, 0);
-        if (masked) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mask_a[jt], mask_b, acc, 0, 0, 0);
+        bf16x8 kj;
+        if constexpr (U::HOLD) kj = kt[jt];
+        else kj = key_tile(hl, jt);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kj, q, acc, 0, 0, 0);
+        if (masked) {
+          bf16x8 mj;
+          if constexpr (U::HOLD) mj = mask_a[jt];
+          else mj = *reinterpret_cast<const bf16x8*>(s_unit + U::mask_block(jt) + lane * 16);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mj, mask_b, acc, 0, 0, 0);
+        }
         sc[jt] = acc;
       }
       softmax_numerators<M>(sc, p.score_scale);
@@ -259,8 +303,16 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       f32x4 o0 = z, o1 = z, l4 = z;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][kk], pb[kk], o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][kk], pb[kk], o1, 0, 0, 0);
+        bf16x8 v0, v1;
+        if constexpr (U::HOLD) {
+          v0 = va[0][kk];
+          v1 = va[1][kk];
+        } else {
+          v0 = value_t(hl, kk, 0);
+          v1 = value_t(hl, kk, 1);
+        }
+        o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb[kk], o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pb[kk], o1, 0, 0, 0);
         l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[kk], l4, 0, 0, 0);
       }
       if (ok) {
@@ -286,6 +338,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     __syncthreads();  // bias table visible
     for (; u < u_end; u += u_step) {
       write_unit(R);
+      write_mask(nxt);
       __syncthreads();  // unit visible to every wave
       const Pos cur = nxt;
       if (u + u_step < u_end) {
@@ -303,6 +356,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     __syncthreads();  // bias table visible
     while (u < u_end) {
       write_unit(R0);
+      write_mask(p0);
       __syncthreads();
       Pos cur = p0;
       if (u + 2 * u_step < u_end) {
@@ -314,6 +368,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       u += u_step;
       if (u >= u_end) break;
       write_unit(R1);
+      write_mask(p1);
       __syncthreads();
       cur = p1;
       if (u + 2 * u_step < u_end) {
@@ -350,6 +405,7 @@ hipError_t launch_mh(const FwdParams& p, int cus, hipStream_t st) {
 
 template <int M>
 hipError_t launch_m(int HG, const FwdParams& p, int cus, hipStream_t st) {
+  if (Win<M>::NT > 4) return HG == 1 ? launch_mh<M, 1>(p, cus, st) : hipErrorInvalidValue;
   switch (HG) {
     case 1: return launch_mh<M, 1>(p, cus, st);
     case 2: return launch_mh<M, 2>(p, cus, st);
@@ -361,6 +417,7 @@ hipError_t launch_m(int HG, const FwdParams& p, int cus, hipStream_t st) {
 
 template <int M>
 size_t lds_m(int HG, int nh) {
+  if (Win<M>::NT > 4) return HG == 1 ? lds_bytes_mh<M, 1>(nh) : 0;
   switch (HG) {
     case 1: return lds_bytes_mh<M, 1>(nh);
     case 2: return lds_bytes_mh<M, 2>(nh);
@@ -372,33 +429,36 @@ size_t lds_m(int HG, int nh) {
 
 }  // namespace
 
-size_t persistent_lds_bytes(int M, int HG, int nh) {
-  switch (M) {
-    case 1: return lds_m<1>(HG, nh);
-    case 2: return lds_m<2>(HG, nh);
-    case 3: return lds_m<3>(HG, nh);
-    case 4: return lds_m<4>(HG, nh);
-    case 5: return lds_m<5>(HG, nh);
-    case 6: return lds_m<6>(HG, nh);
-    case 7: return lds_m<7>(HG, nh);
-    case 8: return lds_m<8>(HG, nh);
-    default: return 0;
+#define SWA_PERSISTENT_M(CALL)                                                   \
+  switch (M) {                                                                   \
+    case 1: return CALL(1);                                                      \
+    case 2: return CALL(2);                                                      \
+    case 3: return CALL(3);                                                      \
+    case 4: return CALL(4);                                                      \
+    case 5: return CALL(5);                                                      \
+    case 6: return CALL(6);                                                      \
+    case 7: return CALL(7);                                                      \
+    case 8: return CALL(8);                                                      \
+    case 9: return CALL(9);                                                      \
+    case 10: return CALL(10);                                                    \
+    case 11: return CALL(11);                                                    \
+    case 12: return CALL(12);                                                    \
+    default: break;                                                              \
   }
+
+size_t persistent_lds_bytes(int M, int HG, int nh) {
+#define SWA_LDS(m) lds_m<m>(HG, nh)
+  SWA_PERSISTENT_M(SWA_LDS)
+#undef SWA_LDS
+  return 0;
 }
 
 hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int cus,
                                       hipStream_t stream) {
-  switch (M) {
-    case 1: return launch_m<1>(HG, p, cus, stream);
-    case 2: return launch_m<2>(HG, p, cus, stream);
-    case 3: return launch_m<3>(HG, p, cus, stream);
-    case 4: return launch_m<4>(HG, p, cus, stream);
-    case 5: return launch_m<5>(HG, p, cus, stream);
-    case 6: return launch_m<6>(HG, p, cus, stream);
-    case 7: return launch_m<7>(HG, p, cus, stream);
-    case 8: return launch_m<8>(HG, p, cus, stream);
-    default: return hipErrorInvalidValue;
-  }
+#define SWA_LAUNCH(m) launch_m<m>(HG, p, cus, stream)
+  SWA_PERSISTENT_M(SWA_LAUNCH)
+#undef SWA_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace swinattn
