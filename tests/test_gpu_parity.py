@@ -239,3 +239,46 @@ def test_not_prepared_and_release():
     torch.cuda.synchronize()
     # zero q, k, bias and no mask beyond regions: output is a mean of zeros
     assert bool((out == 0).all())
+
+
+@pytest.mark.parametrize("B,H,W,nh,M,s", [
+    (1, 14, 14, 64, 7, 3),   # bias table + unit beyond 64 KiB of LDS: per-window kernel
+    (1, 24, 24, 20, 12, 6),
+])
+def test_bf16_many_heads_fallback_kernel(B, H, W, nh, M, s):
+    _say(f"bf16 many heads B={B} H={H} W={W} nh={nh} M={M} s={s}")
+    qkv, table = synth.make_inputs(B, H, W, nh, 32, M, seed=300 + nh, dtype="bf16")
+    got = _f64(_run(qkv, table, M, s))
+    _check(got, oracle.swin_wattn_fwd(qkv, table, M, s), True, "bf16 many heads")
+
+
+def test_bf16_batch_split_over_2gib():
+    # 600 images of the Swin-L stage-1 shape are 2.17 GB of qkv: the host
+    # splits the batch at 594 images (32-bit in-kernel offsets).  Eight
+    # distinct images are tiled along the batch on the device; windows on both
+    # sides of the split are checked against the oracle of their source image.
+    w = synth.WORKLOADS["swin-l-s1"]
+    H, W, nh, M, s = w["H"], w["W"], w["heads"], w["window"], w["shifts"][0]
+    qkv8, table = synth.workload_inputs("swin-l-s1", batch=8)
+    B = 600
+    _say(f"bf16 batch split B={B}")
+    q8 = _to_dev(qkv8)
+    q = q8.repeat(B // 8, 1, 1, 1, 1, 1)
+    t = torch.from_numpy(table).to(_dev())
+    out = torch.full((B, H, W, nh * 32), float("nan"), dtype=torch.bfloat16, device=_dev())
+    swa.check(swa.swin_wattn_precompute(H, W, M, s))
+    swa.check(swa.swin_wattn_fwd(q, t, out, B, H, W, nh, 32, M, s))
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item()
+    nW = (H // M) * (W // M)
+    images = [0, 593, 594, 595, 599]
+    sel = np.array([(b % 8) * nW + wi for b in images for wi in (0, 7, 56, 63, 27)], dtype=np.int64)
+    ref, pos = oracle.swin_wattn_windows(qkv8, table, M, s, sel)
+    k = 0
+    for b in images:
+        for _ in range(5):
+            got = _f64(out.view(B * H * W, nh * 32)[torch.from_numpy(pos[k] + (b - b % 8) * H * W).to(_dev())])
+            _check(got, ref[k], True, f"image {b}")
+            k += 1
+    del q, out
+    torch.cuda.empty_cache()
