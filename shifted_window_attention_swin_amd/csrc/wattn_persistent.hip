@@ -110,8 +110,6 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     u_end = units;
   }
 
-  // stage the bias table of every head (reversed, divided by the scale)
-  stage_bias<M>(s_bias, p.table, nh, p.inv_scale);
 
   // unit u -> (head group, image, window); decoded once, used for the loads
   // and, one iteration later, for the math
@@ -335,6 +333,9 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     Regs R;
     Pos nxt = decode(u);
     if (u < u_end) issue_loads(R, nxt);
+    // the bias table (reversed, divided by the scale) is staged while the
+    // first unit's loads are in flight
+    stage_bias<M>(s_bias, p.table, nh, p.inv_scale);
     __syncthreads();  // bias table visible
     for (; u < u_end; u += u_step) {
       write_unit(R);
@@ -353,6 +354,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     Pos p0 = decode(u), p1 = decode(u + u_step);
     if (u < u_end) issue_loads(R0, p0);
     if (u + u_step < u_end) issue_loads(R1, p1);
+    stage_bias<M>(s_bias, p.table, nh, p.inv_scale);
     __syncthreads();  // bias table visible
     while (u < u_end) {
       write_unit(R0);
