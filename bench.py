@@ -147,9 +147,6 @@ def main() -> int:
     qs = [q0] + [q0.clone() for _ in range(sets - 1)]
     outs = [torch.empty(B, H, W, nh * d, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
     stream = torch.cuda.current_stream()
-    for s in shifts:
-        swa.check(swa.swin_wattn_precompute(H, W, M, s, stream), "precompute")
-    torch.cuda.synchronize()
 
     def step(i):
         k = i % sets

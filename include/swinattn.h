@@ -14,10 +14,12 @@
  *   - same talk, section 2: shift, partition and merge are pure index mapping
  *     (here folded into the kernel's loads and stores); the fused attention
  *     takes the mask and the bias as tensors.
- *   - same talk, section 3: the position-bias lookup is moved to a one-time
- *     preprocessing step (swin_wattn_precompute); batch GEMM, softmax and
- *     batch GEMM run as one kernel whose loads and stores absorb the
- *     transposes.
+ *   - same talk, section 3: the position-bias lookup is moved out of the
+ *     forward to a one-time step (here it is a closed form of the token
+ *     coordinates, resolved when the kernel is compiled;
+ *     swin_wattn_precompute materialises the index and mask tensors); batch
+ *     GEMM, softmax and batch GEMM run as one kernel whose loads and stores
+ *     absorb the transposes.
  *   - Baidu AIAK-Training talk (jxzklqfsx.com article 743345), section 2,
  *     WindowAttention case: the whole module as one kernel, tiles staged
  *     through the memory hierarchy, two matrix products and a softmax.
@@ -51,15 +53,17 @@ typedef enum {
   SWIN_OK = 0,
   SWIN_ERR_INVALID_ARG = -1,  /* null or misaligned pointer, bad size, shift, divisibility */
   SWIN_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim != 32, window > 12, too many heads */
-  SWIN_ERR_NOT_PREPARED = -3, /* no swin_wattn_precompute for (device, H, W, window, shift) */
+  SWIN_ERR_NOT_PREPARED = -3, /* copy calls: no swin_wattn_precompute for the key */
   SWIN_ERR_HIP = -4           /* the HIP runtime reported an error (allocation, launch) */
 } swin_status_t;
 
-/* Setup, once per (device, H, W, window, shift), before swin_wattn_fwd*.
- * Builds in library-owned device memory: the relative position index
- * [N][N] int32 (N = window^2), the shift mask [nW][N][N] float32 (0 or -100,
- * nW = (H/window)*(W/window)), and the compact form the kernels read
- * (per-window region labels [nW][N] uint8 and a per-window has-mask flag).
+/* Materialises, once per (device, H, W, window, shift), in library-owned
+ * device memory: the relative position index [N][N] int32 (N = window^2),
+ * the shift mask [nW][N][N] float32 (0 or -100, nW = (H/window)*(W/window))
+ * and the per-window region labels [nW][N] uint8, for callers that keep
+ * these tensors (a Swin block's index and mask buffers) and for
+ * verification through the copy calls.  The forward calls do not need it:
+ * they evaluate the index and the mask from token coordinates.
  * May allocate device memory (hipMalloc); the fill is queued on `stream`.
  * Calling it again for a prepared key is a no-op returning SWIN_OK.
  * Requires H, W > 0, 1 <= window <= 12, H % window == 0, W % window == 0,
@@ -78,9 +82,9 @@ int swin_wattn_precompute(int H, int W, int window, int shift, void* stream);
  * accumulation, attention weights rounded to bf16 before the value product,
  * output rounded to nearest-even bf16.  B == 0 queues nothing and returns
  * SWIN_OK.  head_dim must be 32; heads * (2*window-1)^2 * 4 bytes must fit
- * in 64 KiB (the bias table is staged in LDS).  No allocation, no host
- * synchronisation; safe to call concurrently from several threads once the
- * precompute for the key has completed. */
+ * in 64 KiB (the bias table is staged in LDS).  No setup call needed, no
+ * allocation, no host synchronisation; safe to call concurrently from
+ * several threads. */
 int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int B, int H, int W,
                    int heads, int head_dim, int window, int shift, void* stream);
 
@@ -99,8 +103,9 @@ int swin_wattn_copy_mask(int H, int W, int window, int shift, float* dst, void* 
 int swin_wattn_copy_region(int H, int W, int window, int shift, uint8_t* dst, void* stream);
 
 /* Frees every precomputed buffer on every device (synchronises each device
- * first).  Afterwards swin_wattn_fwd* return SWIN_ERR_NOT_PREPARED until the
- * next precompute.  Must not run concurrently with other calls. */
+ * first).  Afterwards the copy calls return SWIN_ERR_NOT_PREPARED until the
+ * next precompute; the forward calls are unaffected.  Must not run
+ * concurrently with other calls. */
 int swin_wattn_release(void);
 
 /* Static, human-readable name of a status code. */

@@ -1,8 +1,11 @@
-// C-ABI front of libswinattn: argument checks, the per-device cache of
-// precomputed index/mask tensors, and kernel launches on the caller's stream.
-// The bias lookup structure is built once at setup and reused by every call
-// (talk "Swin Transformer training and inference optimization", uticex.com
-// 1598, section 3: computations needed once are hoisted to preprocessing).
+// C-ABI front of libswinattn: argument checks, kernel launches on the
+// caller's stream, and the per-device cache of materialised index/mask
+// tensors.  The talk "Swin Transformer training and inference optimization"
+// (uticex.com 1598, section 3) hoists the bias index lookup to a one-time
+// preprocessing step; the forward kernels go one step further and evaluate
+// the index and the mask as closed forms of the token coordinates, so the
+// forward reads no setup state.  The precompute call builds the tensors for
+// callers that want them and for verification.
 
 #include <math.h>
 #include <stdint.h>
@@ -20,11 +23,10 @@ namespace {
 
 struct Prepared {
   int dev, H, W, M, s;
-  void* block;  // one allocation holding the four arrays below
+  void* block;  // one allocation holding the three arrays below
   int32_t* rel_index;
   float* mask;
   uint8_t* region;
-  uint8_t* has_mask;
 };
 
 std::mutex g_mu;
@@ -94,22 +96,17 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
     return SWIN_ERR_INVALID_ARG;
   if (B == 0) return SWIN_OK;
 
+  // the relative position index and the shift mask are closed forms of the
+  // token coordinates, evaluated in the kernels: no setup state is read
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SWIN_ERR_HIP;
-  Prepared prep;
-  {
-    std::lock_guard<std::mutex> lock(g_mu);
-    Prepared* e = find(dev, H, W, M, s);
-    if (!e) return SWIN_ERR_NOT_PREPARED;
-    prep = *e;
-  }
   FwdParams p;
   p.table = table;
-  p.has_mask = prep.has_mask;
   p.H = H;
   p.W = W;
   p.nh = heads;
   p.shift = s;
+  p.nWy = H / M;
   p.nWx = W / M;
   p.nW = (int)nW;
   const double sd = sqrt((double)head_dim);
@@ -130,7 +127,8 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
       rest -= piece;
     }
   }
-  // bf16 windows of up to 4 tiles go to the persistent LDS-staged kernel
+  // bf16 windows whose bias table and unit fit in LDS go to the persistent
+  // LDS-staged kernel, the rest to the per-window kernels
   const int hg = head_group(heads, M);
   const bool persistent = bf16 && M <= kMaxPersistentWindow &&
                           persistent_lds_bytes(M, hg, heads) <= (size_t)kMaxTableLds;
@@ -195,9 +193,9 @@ int swin_wattn_precompute(int H, int W, int window, int shift, void* stream) {
   if (find(dev, H, W, window, shift)) return SWIN_OK;
   const size_t N = (size_t)window * window, nW = (size_t)(H / window) * (W / window);
   const size_t b_idx = align256(N * N * 4), b_mask = align256(nW * N * N * 4),
-               b_reg = align256(nW * N), b_flag = align256(nW);
+               b_reg = align256(nW * N);
   void* block = nullptr;
-  if (hipMalloc(&block, b_idx + b_mask + b_reg + b_flag) != hipSuccess) return SWIN_ERR_HIP;
+  if (hipMalloc(&block, b_idx + b_mask + b_reg) != hipSuccess) return SWIN_ERR_HIP;
   Prepared e;
   e.dev = dev;
   e.H = H;
@@ -209,9 +207,8 @@ int swin_wattn_precompute(int H, int W, int window, int shift, void* stream) {
   e.rel_index = reinterpret_cast<int32_t*>(base);
   e.mask = reinterpret_cast<float*>(base + b_idx);
   e.region = reinterpret_cast<uint8_t*>(base + b_idx + b_mask);
-  e.has_mask = reinterpret_cast<uint8_t*>(base + b_idx + b_mask + b_reg);
   const hipError_t err = launch_precompute(H, W, window, shift, e.rel_index, e.mask, e.region,
-                                           e.has_mask, static_cast<hipStream_t>(stream));
+                                           static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     (void)hipFree(block);
     return SWIN_ERR_HIP;
@@ -264,7 +261,7 @@ const char* swin_wattn_status_string(int status) {
     case SWIN_OK: return "SWIN_OK";
     case SWIN_ERR_INVALID_ARG: return "SWIN_ERR_INVALID_ARG: invalid argument";
     case SWIN_ERR_UNSUPPORTED: return "SWIN_ERR_UNSUPPORTED: configuration not supported";
-    case SWIN_ERR_NOT_PREPARED: return "SWIN_ERR_NOT_PREPARED: swin_wattn_precompute not called";
+    case SWIN_ERR_NOT_PREPARED: return "SWIN_ERR_NOT_PREPARED: swin_wattn_precompute not called for this key";
     case SWIN_ERR_HIP: return "SWIN_ERR_HIP: HIP runtime error";
     default: return "unknown status";
   }

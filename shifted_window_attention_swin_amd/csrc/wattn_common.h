@@ -56,6 +56,14 @@ SWA_INLINE int band_of(int pos, int L, int M, int s) {
 SWA_INLINE int region_label(int yy, int xx, int H, int W, int M, int s) {
   return s == 0 ? 0 : 3 * band_of(yy, H, M, s) + band_of(xx, W, M, s);
 }
+// Whether window (wy, wx) of an nWy x nWx grid holds more than one region.
+// With 0 < s < M every window off the last window row and column lies inside
+// band 0 of both axes; a window on the last row (column) holds rows
+// (columns) of bands 1 and 2, each at least one wide.  So the mask is needed
+// exactly there, and no per-window flag has to be read from memory.
+SWA_INLINE bool window_masked(int s, int wy, int wx, int nWy, int nWx) {
+  return s > 0 && (wy == nWy - 1 || wx == nWx - 1);
+}
 
 // Channel that column c of a value-transpose tile of channel half hf
 // carries.  With this order, row 4g+r of output tile hf is channel

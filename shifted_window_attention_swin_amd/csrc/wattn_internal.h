@@ -18,9 +18,8 @@ struct FwdParams {
   const void* qkv;          // [B][H][W][3][nh][32], B = images of this launch
   const float* table;       // [(2M-1)^2][nh]
   void* out;                // [B][H][W][nh*32]
-  const uint8_t* has_mask;  // [nW] precomputed: 1 if the window's region labels differ
   int B, H, W, nh, shift;
-  int nWx, nW;
+  int nWy, nWx, nW;         // window grid: rows, columns, rows * columns
   int total_windows;        // B * nW (grid size of the per-window kernels)
   int units;                // B * nW * nhg (work units of the persistent kernel)
   int nhg;                  // head groups per window (persistent kernel)
@@ -31,9 +30,9 @@ struct FwdParams {
 };
 
 // Queues the precompute kernel.  rel_index [N*N], mask [nW*N*N],
-// region [nW*N], has_mask [nW].
+// region [nW*N].
 hipError_t launch_precompute(int H, int W, int M, int s, int32_t* rel_index, float* mask,
-                             uint8_t* region, uint8_t* has_mask, hipStream_t stream);
+                             uint8_t* region, hipStream_t stream);
 
 // Queue the forward kernels; M in [1, kMaxWindow].  `waves` = waves per
 // workgroup (heads are dealt round-robin to waves).

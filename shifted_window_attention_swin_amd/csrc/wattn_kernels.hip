@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_kernel(FwdParams p) {
   for (int s = 0; s < 8; ++s) hc.ones[s] = (__bf16)1.f;
   __syncthreads();
 
-  const bool masked = p.has_mask[w] != 0;
+  const bool masked = window_masked(p.shift, w / p.nWx, w % p.nWx, p.nWy, p.nWx);
   if (masked) lw.template init_labels<S::MASK_MFMA>(p, w, g, c);
   run_heads_bf16<M, kPrefetch>(hc, lw, in, Cb, nh, wave, nwaves, masked, q, k, v);
 }
@@ -404,16 +404,16 @@ __global__ __launch_bounds__(256) void wattn_fwd_f32_kernel(FwdParams p) {
   lw.init(p, b, w, g, c, 4);
   const bool g_ok = g < S::LG;
   __syncthreads();
-  const bool masked = p.has_mask[w] != 0;
+  const bool masked = window_masked(p.shift, w / p.nWx, w % p.nWx, p.nWy, p.nWx);
   if (masked) lw.template init_labels<false>(p, w, g, c);
   for (int h = wave; h < p.nh; h += nwaves) head_f32<M>(p, lw, s_bias, in, out, h, g, c, g_ok, masked);
 }
 
 // ---------------------------------------------------------------------------
-// setup: relative position index, shift mask, region labels, has-mask flags
+// setup: relative position index, shift mask, region labels
 
 __global__ void precompute_kernel(int H, int W, int M, int s, int32_t* rel_index, float* mask,
-                                  uint8_t* region, uint8_t* has_mask) {
+                                  uint8_t* region) {
   const int N = M * M, nWx = W / M, nW = (H / M) * nWx;
   const long long total = (long long)nW * N * N;
   const long long stride = (long long)gridDim.x * blockDim.x;
@@ -430,12 +430,6 @@ __global__ void precompute_kernel(int H, int W, int M, int s, int32_t* rel_index
       rel_index[i * N + j] = (dy + M - 1) * (2 * M - 1) + (dx + M - 1);
     }
     if (j == 0) region[(long long)w * N + i] = (uint8_t)li;
-    if (i == 0 && j == 0) {
-      int differ = 0;
-      for (int t = 1; t < N; ++t)
-        differ |= region_label(wy * M + t / M, wx * M + t % M, H, W, M, s) != li;
-      has_mask[w] = (uint8_t)differ;
-    }
   }
 }
 
@@ -461,13 +455,13 @@ hipError_t launch_f32_m(const FwdParams& p, int waves, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_precompute(int H, int W, int M, int s, int32_t* rel_index, float* mask,
-                             uint8_t* region, uint8_t* has_mask, hipStream_t stream) {
+                             uint8_t* region, hipStream_t stream) {
   const long long total = (long long)(H / M) * (W / M) * M * M * M * M;
   long long blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(precompute_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, H, W, M, s,
-                     rel_index, mask, region, has_mask);
+                     rel_index, mask, region);
   return hipGetLastError();
 }
 

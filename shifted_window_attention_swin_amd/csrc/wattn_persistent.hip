@@ -114,16 +114,16 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   // unit u -> (head group, image, window); decoded once, used for the loads
   // and, one iteration later, for the math
   struct Pos {
-    int hg, b, w, wy, wx;
+    int hg, b, wy, wx;
   };
   auto decode = [&](int uu) {
     Pos q;
     q.hg = uu % p.nhg;
     const int bw = uu / p.nhg;
     q.b = bw / p.nW;
-    q.w = bw - q.b * p.nW;
-    q.wy = q.w / p.nWx;
-    q.wx = q.w - q.wy * p.nWx;
+    const int w = bw - q.b * p.nW;
+    q.wy = w / p.nWx;
+    q.wx = w - q.wy * p.nWx;
     return q;
   };
 
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   // tiles w, w+4, ...  (each lane's operand depends on the lane only)
   auto write_mask = [&](const Pos& q) {
     if constexpr (!U::HOLD) {
-      if (p.has_mask[q.w]) {
+      if (window_masked(p.shift, q.wy, q.wx, p.nWy, p.nWx)) {
 #pragma unroll
         for (int k = 0; k < U::TPW; ++k) {
           const int t = wv + kWaves * k;
@@ -186,8 +186,8 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
 
   // the math of one unit, out of LDS
   auto process = [&](const Pos& pos) {
-    const int hg = pos.hg, b = pos.b, w = pos.w, wy = pos.wy, wx = pos.wx;
-    const bool masked = p.has_mask[w] != 0;
+    const int hg = pos.hg, b = pos.b, wy = pos.wy, wx = pos.wx;
+    const bool masked = window_masked(p.shift, wy, wx, p.nWy, p.nWx);
     // key-side mask operand of key tile t for this lane (see
     // LaneWindow::init_labels): it depends on the lane only, not the head
     auto key_mask = [&](int t) {

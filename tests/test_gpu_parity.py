@@ -39,7 +39,6 @@ def _run(qkv, table, M, s, out=None):
     t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.float32)).to(_dev())
     if out is None:
         out = torch.full((B, H, W, nh * d), float("nan"), dtype=q.dtype, device=_dev())
-    swa.check(swa.swin_wattn_precompute(H, W, M, s), "precompute")
     fn = swa.swin_wattn_fwd if q.dtype == torch.bfloat16 else swa.swin_wattn_fwd_f32
     swa.check(fn(q, t, out, B, H, W, nh, d, M, s), "fwd")
     torch.cuda.synchronize()
@@ -222,23 +221,23 @@ def test_empty_batch_writes_nothing():
     assert bool((out == 7.0).all())
 
 
-def test_not_prepared_and_release():
-    _say("not prepared / release")
-    q = torch.zeros(1, 22, 22, 3, 1, 32, dtype=torch.bfloat16, device=_dev())
-    t = torch.zeros(9, 1, device=_dev())
-    out = torch.empty(1, 22, 22, 32, dtype=torch.bfloat16, device=_dev())
-    assert swa.swin_wattn_fwd(q, t, out, 1, 22, 22, 1, 32, 2, 1) == swa.SWIN_ERR_NOT_PREPARED
-    swa.check(swa.swin_wattn_precompute(22, 22, 2, 1))
-    assert swa.swin_wattn_fwd(q, t, out, 1, 22, 22, 1, 32, 2, 1) == swa.SWIN_OK
-    torch.cuda.synchronize()
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_needs_no_setup_and_release(dtype):
+    """The forward evaluates index and mask itself: it runs, and matches the
+    oracle, with nothing prepared; only the copy calls need the precompute."""
+    _say(f"forward without precompute / release, {dtype}")
     swa.check(swa.swin_wattn_release())
-    assert swa.swin_wattn_fwd(q, t, out, 1, 22, 22, 1, 32, 2, 1) == swa.SWIN_ERR_NOT_PREPARED
-    assert swa.swin_wattn_copy_index(22, 22, 2, 1, out) == swa.SWIN_ERR_NOT_PREPARED
+    qkv, table = synth.make_inputs(2, 22, 22, 3, 32, 2, seed=1234, dtype=dtype)
+    got = _f64(_run(qkv, table, 2, 1))
+    _check(got, oracle.swin_wattn_fwd(qkv, table, 2, 1), dtype == "bf16", "no precompute")
+    idx = torch.empty(16, dtype=torch.int32, device=_dev())
+    assert swa.swin_wattn_copy_index(22, 22, 2, 1, idx) == swa.SWIN_ERR_NOT_PREPARED
     swa.check(swa.swin_wattn_precompute(22, 22, 2, 1))
-    assert swa.swin_wattn_fwd(q, t, out, 1, 22, 22, 1, 32, 2, 1) == swa.SWIN_OK
-    torch.cuda.synchronize()
-    # zero q, k, bias and no mask beyond regions: output is a mean of zeros
-    assert bool((out == 0).all())
+    swa.check(swa.swin_wattn_copy_index(22, 22, 2, 1, idx))
+    again = _f64(_run(qkv, table, 2, 1))
+    assert np.array_equal(got, again)
+    swa.check(swa.swin_wattn_release())
+    assert swa.swin_wattn_copy_index(22, 22, 2, 1, idx) == swa.SWIN_ERR_NOT_PREPARED
 
 
 @pytest.mark.parametrize("B,H,W,nh,M,s", [

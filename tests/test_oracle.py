@@ -134,6 +134,21 @@ def test_mask_closed_form_counts(oracle_lib, H, W, M, s):
     assert np.all(np.diagonal(m, axis1=1, axis2=2) == 0.0)
 
 
+def test_masked_windows_are_last_row_and_column(oracle_lib):
+    """Brute force over every window size up to 8, every shift and grids of
+    1-3 windows per axis: a window needs the mask exactly when the shift is
+    nonzero and the window is on the last window row or column."""
+    for M in range(1, 9):
+        for s in range(M):
+            for nWy in (1, 2, 3):
+                for nWx in (1, 3):
+                    m = oracle.shift_mask(nWy * M, nWx * M, M, s)
+                    got = (m != 0).reshape(nWy, nWx, -1).any(-1)
+                    wy, wx = np.meshgrid(np.arange(nWy), np.arange(nWx), indexing="ij")
+                    expect = (s > 0) & ((wy == nWy - 1) | (wx == nWx - 1))
+                    assert np.array_equal(got, expect), (M, s, nWy, nWx)
+
+
 def test_mask_zero_without_shift(oracle_lib):
     assert np.all(oracle.shift_mask(56, 56, 7, 0) == 0.0)
 
