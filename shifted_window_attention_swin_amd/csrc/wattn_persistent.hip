@@ -20,9 +20,13 @@
 //              one 16-byte part of it, so the shift/partition index map is
 //              one address per lane per unit.  A load instruction covers 16
 //              tokens x 64 contiguous bytes.
-//   compute    (head, query tile) items are spread over the waves; operands
+//   compute    (head, query tile) items are spread over the waves, a
+//              wave's items being all heads of its query tiles; operands
 //              come from LDS with conflict-free ds_read_b128 (a 1 KB block is
 //              read by the 64 lanes in the order the MFMA layout wants).
+//   stores     the HG heads of a token leave one wave back to back as
+//              non-temporal 16-byte stores: whole output cache lines, which
+//              the output never re-reads.
 //
 // The attention math per item is the one described in wattn_kernels.hip.
 
@@ -45,8 +49,12 @@ struct Unit {
   static constexpr int TPW = (NT + kWaves - 1) / kWaves;   // tiles loaded per wave
   static constexpr int ITEMS = HG * NT;                    // (head, query tile) items
   static constexpr int IPW = (ITEMS + kWaves - 1) / kWaves;
+  // head-inner order: a wave's items are all HG heads of its query tiles, so
+  // the HG * 64 output bytes of a token leave the wave together (whole cache
+  // lines) instead of 64-byte halves from different waves
+  static constexpr bool HEAD_INNER = HG > 1 && IPW % HG == 0;
   // every wave's items belong to one head: key / value tiles load once
-  static constexpr bool ONE_HEAD = ITEMS % kWaves == 0 && NT % IPW == 0;
+  static constexpr bool ONE_HEAD = !HEAD_INNER && ITEMS % kWaves == 0 && NT % IPW == 0;
   static constexpr int BLOCK = 1024;                       // 16 tokens x 64 bytes
   // windows of up to 4 tiles keep key tiles, V^T and mask operands in
   // registers for all items of a wave; larger windows re-read them from LDS
@@ -240,11 +248,19 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       cur = wv * U::IPW / NT;
       load_head(cur);
     }
+    bf16x8 ovs[HG];  // head-inner: outputs of the query tile's heads, stored together
 #pragma unroll
     for (int i = 0; i < U::IPW; ++i) {
       const int item = wv * U::IPW + i;
       if (item >= U::ITEMS) break;
-      const int hl = item / NT, it = item - hl * NT;
+      int hl, it;
+      if constexpr (U::HEAD_INNER) {
+        hl = i % HG;
+        it = wv * (U::IPW / HG) + i / HG;
+      } else {
+        hl = item / NT;
+        it = item - hl * NT;
+      }
       const int h = hg * HG + hl;
       if (!U::ONE_HEAD && hl != cur) {
         cur = hl;
@@ -322,7 +338,20 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
           ov[4 + r] = (__bf16)(o1[r] * inv);
         }
         const unsigned pix = token_pixel(p, M, b, wy, wx, ty, tx, true);
-        *reinterpret_cast<bf16x8*>(out + pix * Cb + h * kHeadDim * 2 + 16 * g) = ov;
+        bf16x8* dst = reinterpret_cast<bf16x8*>(out + pix * Cb + h * kHeadDim * 2 + 16 * g);
+        // the output is not read again: non-temporal stores keep it from
+        // displacing cached input lines
+        auto store = [&](bf16x8* d, const bf16x8& v) { __builtin_nontemporal_store(v, d); };
+        if constexpr (U::HEAD_INNER) {
+          ovs[hl] = ov;
+          if (hl == HG - 1) {
+            // head hl' of the token sits (hl' - hl) * 64 bytes from dst
+#pragma unroll
+            for (int k = 0; k < HG; ++k) store(dst + 4 * (k - (HG - 1)), ovs[k]);
+          }
+        } else {
+          store(dst, ov);
+        }
       }
     }
   };
@@ -407,25 +436,31 @@ hipError_t launch_mh(const FwdParams& p, int cus, hipStream_t st) {
 
 template <int M>
 hipError_t launch_m(int HG, const FwdParams& p, int cus, hipStream_t st) {
-  if (Win<M>::NT > 4) return HG == 1 ? launch_mh<M, 1>(p, cus, st) : hipErrorInvalidValue;
-  switch (HG) {
-    case 1: return launch_mh<M, 1>(p, cus, st);
-    case 2: return launch_mh<M, 2>(p, cus, st);
-    case 3: return launch_mh<M, 3>(p, cus, st);
-    case 4: return launch_mh<M, 4>(p, cus, st);
-    default: return hipErrorInvalidValue;
+  if constexpr (Win<M>::NT > 4) {  // larger windows: one head per unit
+    return HG == 1 ? launch_mh<M, 1>(p, cus, st) : hipErrorInvalidValue;
+  } else {
+    switch (HG) {
+      case 1: return launch_mh<M, 1>(p, cus, st);
+      case 2: return launch_mh<M, 2>(p, cus, st);
+      case 3: return launch_mh<M, 3>(p, cus, st);
+      case 4: return launch_mh<M, 4>(p, cus, st);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
 template <int M>
 size_t lds_m(int HG, int nh) {
-  if (Win<M>::NT > 4) return HG == 1 ? lds_bytes_mh<M, 1>(nh) : 0;
-  switch (HG) {
-    case 1: return lds_bytes_mh<M, 1>(nh);
-    case 2: return lds_bytes_mh<M, 2>(nh);
-    case 3: return lds_bytes_mh<M, 3>(nh);
-    case 4: return lds_bytes_mh<M, 4>(nh);
-    default: return 0;
+  if constexpr (Win<M>::NT > 4) {
+    return HG == 1 ? lds_bytes_mh<M, 1>(nh) : 0;
+  } else {
+    switch (HG) {
+      case 1: return lds_bytes_mh<M, 1>(nh);
+      case 2: return lds_bytes_mh<M, 2>(nh);
+      case 3: return lds_bytes_mh<M, 3>(nh);
+      case 4: return lds_bytes_mh<M, 4>(nh);
+      default: return 0;
+    }
   }
 }
 
