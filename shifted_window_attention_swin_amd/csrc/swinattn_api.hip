@@ -134,6 +134,9 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
                           persistent_lds_bytes(M, hg, heads) <= (size_t)kMaxTableLds;
   const int cus = persistent ? compute_units(dev) : 0;
   p.nhg = heads / hg;
+  // a unit's per-token slice is hg * 64 bytes: with odd hg and several head
+  // groups, neighbouring units of a window share 128-byte lines
+  p.xcd_ranges = (hg % 2 == 1 && p.nhg > 1) ? 1 : 0;
   // per-window kernels: heads are dealt round-robin to the waves of a
   // workgroup, preferably 2-3 heads per wave
   int waves = 1;

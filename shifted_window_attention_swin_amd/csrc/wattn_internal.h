@@ -23,6 +23,7 @@ struct FwdParams {
   int total_windows;        // B * nW (grid size of the per-window kernels)
   int units;                // B * nW * nhg (work units of the persistent kernel)
   int nhg;                  // head groups per window (persistent kernel)
+  int xcd_ranges;           // persistent kernel: one contiguous unit range per XCD
   float score_scale;        // log2(e) / sqrt(head_dim)
   float inv_scale;          // sqrt(head_dim): bias and mask are pre-divided by the scale
   float mask_value;         // -100 * sqrt(head_dim)

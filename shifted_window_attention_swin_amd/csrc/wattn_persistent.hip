@@ -11,8 +11,10 @@
 //              743345, section 2, WindowAttention case) describes the fused
 //              module as tiles moving through the memory hierarchy of HBM,
 //              shared memory and registers; this is that pipeline on gfx950.
-//   workgroup  4 waves, persistent: it walks a contiguous range of units
-//              (one range per XCD, so neighbouring windows share an L2).
+//   workgroup  4 waves, persistent: the grid walks the units in order, so
+//              the units in flight are one compact stretch of the batch;
+//              when the units of a window share cache lines, each XCD
+//              instead walks its own contiguous range (one L2 per line).
 //   pipeline   the next unit's 16-byte loads are issued into registers right
 //              after the current unit is written to LDS, and stay in flight
 //              while the current unit is computed out of LDS.
@@ -102,11 +104,14 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   char* out = static_cast<char*>(p.out);
   const int units = p.units;
 
-  // this workgroup's units: one contiguous range per XCD, interleaved over
-  // the XCD's workgroups
+  // this workgroup's units.  Default: the grid walks the units in order
+  // (unit id + k * grid), so the units in flight form one compact stretch of
+  // the batch.  Units of one window whose slices share cache lines (64-byte
+  // head slices) instead take one contiguous range per XCD, interleaved over
+  // the XCD's workgroups: the halves of a line then meet in one L2.
   const int G = gridDim.x, id = blockIdx.x;
   int u, u_step, u_end;
-  if ((G & 7) == 0) {
+  if (p.xcd_ranges && (G & 7) == 0) {
     const int x = id & 7, per = G >> 3;
     const long long r0 = (long long)units * x / 8, r1 = (long long)units * (x + 1) / 8;
     u = (int)r0 + (id >> 3);
@@ -428,7 +433,7 @@ hipError_t launch_mh(const FwdParams& p, int cus, hipStream_t st) {
     per_cu = 1;
   long long grid = (long long)cus * per_cu;
   if (grid > p.units) grid = p.units;
-  if (grid >= 8) grid &= ~7LL;  // whole XCD rounds: one contiguous unit range per XCD
+  if (grid >= 8) grid &= ~7LL;  // whole XCD rounds (equal share per XCD)
   hipLaunchKernelGGL((wattn_fwd_bf16_persistent<M, HG>), dim3((unsigned)grid), dim3(kWaves * 64),
                      lds, st, p);
   return hipGetLastError();
