@@ -49,11 +49,21 @@ def algorithmic(B, H, W, heads, head_dim, window, elem=2):
 
 
 def fwd_kernel_name(window: int, heads: int) -> str:
-    """Name of the forward kernel the library launches (mirrors its dispatch:
-    windows up to 8 use the persistent kernel with head groups of 2, else 3,
-    else 1)."""
-    if window <= 8:
+    """Name of the bf16 forward kernel the library launches.  Mirrors its
+    dispatch: head groups of 2, else 3, else 1 for windows of up to 4 tiles
+    of 16 tokens (window <= 8), 1 beyond; the persistent kernel when the bias
+    table and one unit fit in 64 KiB of LDS, else the per-window kernel."""
+    q = (window + 3) // 4
+    nt = q * q
+    if nt > 4:
+        hg = 1
+    else:
         hg = 2 if heads % 2 == 0 else 3 if heads % 3 == 0 else 1
+    t = (2 * window - 1) ** 2
+    tail = 2 * window * (4 * q - window)
+    bias = ((heads * t + tail) * 4 + 15) // 16 * 16
+    unit = 3 * hg * nt * 1024 + (nt * 1024 if nt > 4 else 0)
+    if bias + unit <= 64 * 1024:
         return f"wattn_fwd_bf16_persistent<{window}, {hg}>"
     return f"wattn_fwd_bf16_kernel<{window}>"
 
@@ -95,8 +105,10 @@ def cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_re
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=1000)
+    # the GPU needs some tens of milliseconds of sustained load before its
+    # launches reach steady speed: 1000 warmup launches are about 60 ms here
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="swin-l-s1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batch", type=int, default=64)
@@ -169,15 +181,19 @@ def main() -> int:
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / K
     value = nbytes * K / (total_ms / 1e3) / 1e9
-    # duration of each launch, from HIP events recorded on the launch stream
+    # average launch duration: the HIP events around the timed region, on the
+    # stream the kernel is launched on, over its K * len(shifts) launches
+    # (back to back: this is what a kernel trace's mean duration agrees with)
+    avg_launch_s = total_ms / 1e3 / (K * len(shifts))
+    # for reference, launches timed one by one (each event pair adds its own
+    # overhead to the launch it brackets)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for i in range(K):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_launch_s = sum(launch_ms) / K / 1e3 / len(shifts)
+    isolated_s = sum(a.elapsed_time(b) for a, b in ev) / K / 1e3 / len(shifts)
 
     achieved = (nbytes / len(shifts)) / avg_launch_s / 1e9
     traffic = measured_traffic(args.workload)
@@ -203,6 +219,7 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": fwd_kernel_name(M, nh),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "isolated_launch_us": round(isolated_s * 1e6, 3),
                      "alg_bytes_per_launch": nbytes // len(shifts),
                      "alg_flops_per_launch": nflops // len(shifts),
                      "mfma_tflops": round((nflops / len(shifts)) / avg_launch_s / 1e12, 3),

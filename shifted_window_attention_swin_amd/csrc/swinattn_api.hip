@@ -11,6 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -32,20 +33,18 @@ struct Prepared {
 std::mutex g_mu;
 std::vector<Prepared> g_cache;
 
-// compute units per device (looked up once per device)
-constexpr int kMaxDevices = 64;
-int g_cus[kMaxDevices];
+// compute units per device, looked up on first use (lock-free: a racing
+// first use stores the same value twice)
+std::atomic<int> g_cus[kMaxDevices];
 
 int compute_units(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return 256;
-  std::lock_guard<std::mutex> lock(g_mu);
-  if (g_cus[dev] <= 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    g_cus[dev] = v;
-  }
-  return g_cus[dev];
+  int v = g_cus[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  g_cus[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 // heads per unit of the persistent kernel.  Windows of up to 4 tiles: 2
@@ -159,7 +158,7 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
     p.B = (int)nb;
     p.total_windows = (int)(nb * nW);
     p.units = (int)(nb * nW * p.nhg);
-    const hipError_t err = persistent ? launch_fwd_bf16_persistent(M, hg, p, cus, st)
+    const hipError_t err = persistent ? launch_fwd_bf16_persistent(M, hg, p, dev, cus, st)
                            : bf16     ? launch_fwd_bf16(M, p, waves, st)
                                       : launch_fwd_f32(M, p, waves, st);
     if (err != hipSuccess) return SWIN_ERR_HIP;

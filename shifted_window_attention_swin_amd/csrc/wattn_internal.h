@@ -13,6 +13,7 @@ constexpr int kMaxTableLds = 64 * 1024;
 // In-kernel token offsets are 32-bit: one launch covers at most this many
 // bytes of qkv; larger batches are split into several launches.
 constexpr long long kMaxChunkBytes = 1LL << 31;
+constexpr int kMaxDevices = 64;  // devices with cached launch properties
 
 struct FwdParams {
   const void* qkv;          // [B][H][W][3][nh][32], B = images of this launch
@@ -44,10 +45,10 @@ hipError_t launch_fwd_f32(int M, const FwdParams& p, int waves, hipStream_t stre
 
 // Persistent LDS-staged bf16 forward (every window up to kMaxWindow): heads
 // are processed in groups of HG (1..4, HG divides nh; 1 for windows of more
-// than 4 tiles); `cus` = compute units of the device (the grid fills them at
-// the kernel's occupancy).
+// than 4 tiles); `dev` = current device, `cus` = its compute units (the grid
+// fills them at the kernel's occupancy, cached per device).
 constexpr int kMaxPersistentWindow = 12;
-hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int cus,
+hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
                                       hipStream_t stream);
 size_t persistent_lds_bytes(int M, int HG, int nh);
 

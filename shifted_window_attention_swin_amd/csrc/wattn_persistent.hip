@@ -32,6 +32,8 @@
 //
 // The attention math per item is the one described in wattn_kernels.hip.
 
+#include <atomic>
+
 #include "wattn_common.h"
 
 namespace swinattn {
@@ -424,14 +426,29 @@ size_t lds_bytes_mh(int nh) {
   return ((bias + 15) & ~size_t(15)) + Unit<M, HG>::BYTES;
 }
 
+// workgroups of wattn_fwd_bf16_persistent<M, HG> resident per CU for `lds`
+// bytes of dynamic LDS; cached per device as (lds << 8 | blocks)
 template <int M, int HG>
-hipError_t launch_mh(const FwdParams& p, int cus, hipStream_t st) {
-  const size_t lds = lds_bytes_mh<M, HG>(p.nh);
+int blocks_per_cu(int dev, size_t lds) {
+  static std::atomic<long long> cache[kMaxDevices];
+  const bool cacheable = dev >= 0 && dev < kMaxDevices;
+  if (cacheable) {
+    const long long c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0 && (size_t)(c >> 8) == lds) return (int)(c & 255);
+  }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_fwd_bf16_persistent<M, HG>,
                                                    kWaves * 64, lds) != hipSuccess || per_cu < 1)
     per_cu = 1;
-  long long grid = (long long)cus * per_cu;
+  if (per_cu > 255) per_cu = 255;
+  if (cacheable) cache[dev].store(((long long)lds << 8) | per_cu, std::memory_order_relaxed);
+  return per_cu;
+}
+
+template <int M, int HG>
+hipError_t launch_mh(const FwdParams& p, int dev, int cus, hipStream_t st) {
+  const size_t lds = lds_bytes_mh<M, HG>(p.nh);
+  long long grid = (long long)cus * blocks_per_cu<M, HG>(dev, lds);
   if (grid > p.units) grid = p.units;
   if (grid >= 8) grid &= ~7LL;  // whole XCD rounds (equal share per XCD)
   hipLaunchKernelGGL((wattn_fwd_bf16_persistent<M, HG>), dim3((unsigned)grid), dim3(kWaves * 64),
@@ -440,15 +457,15 @@ hipError_t launch_mh(const FwdParams& p, int cus, hipStream_t st) {
 }
 
 template <int M>
-hipError_t launch_m(int HG, const FwdParams& p, int cus, hipStream_t st) {
+hipError_t launch_m(int HG, const FwdParams& p, int dev, int cus, hipStream_t st) {
   if constexpr (Win<M>::NT > 4) {  // larger windows: one head per unit
-    return HG == 1 ? launch_mh<M, 1>(p, cus, st) : hipErrorInvalidValue;
+    return HG == 1 ? launch_mh<M, 1>(p, dev, cus, st) : hipErrorInvalidValue;
   } else {
     switch (HG) {
-      case 1: return launch_mh<M, 1>(p, cus, st);
-      case 2: return launch_mh<M, 2>(p, cus, st);
-      case 3: return launch_mh<M, 3>(p, cus, st);
-      case 4: return launch_mh<M, 4>(p, cus, st);
+      case 1: return launch_mh<M, 1>(p, dev, cus, st);
+      case 2: return launch_mh<M, 2>(p, dev, cus, st);
+      case 3: return launch_mh<M, 3>(p, dev, cus, st);
+      case 4: return launch_mh<M, 4>(p, dev, cus, st);
       default: return hipErrorInvalidValue;
     }
   }
@@ -495,9 +512,9 @@ size_t persistent_lds_bytes(int M, int HG, int nh) {
   return 0;
 }
 
-hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int cus,
+hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
                                       hipStream_t stream) {
-#define SWA_LAUNCH(m) launch_m<m>(HG, p, cus, stream)
+#define SWA_LAUNCH(m) launch_m<m>(HG, p, dev, cus, stream)
   SWA_PERSISTENT_M(SWA_LAUNCH)
 #undef SWA_LAUNCH
   return hipErrorInvalidValue;
