@@ -49,6 +49,8 @@ def lib():
         L.oracle_swin_wattn_fwd.restype = I
         L.oracle_swin_wattn_windows.argtypes = [P, I, P, I, I, I, I, I, I, I, L64, P, I, P, P]
         L.oracle_swin_wattn_windows.restype = I
+        L.oracle_linear.argtypes = [P, I, L64, I, P, I, I, P, P, I, I, P]
+        L.oracle_linear.restype = I
         _lib = L
     return _lib
 
@@ -165,3 +167,30 @@ def swin_wattn_windows(qkv, table, window: int, shift: int, sel, nthreads: int =
     if used < 0:
         raise ValueError("oracle rejected the arguments")
     return out, pos
+
+
+def linear(x, w, bias=None, residual=None, nthreads: int = 0):
+    """``y = x @ w.T + bias (+ residual)`` in fp64.  ``x [..., K]``, ``w [N, K]``
+    (uint16 = bfloat16 patterns, float32 or float64), ``bias [N]`` float32,
+    ``residual [..., N]``.  Returns float64 ``[..., N]``."""
+    xq, xc = _qkv_arg(x)
+    wq, wc = _qkv_arg(w)
+    N, K = wq.shape
+    assert xq.shape[-1] == K
+    lead = xq.shape[:-1]
+    T = int(np.prod(lead)) if lead else 1
+    bp = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.shape == (N,)
+        bp = _ptr(bias)
+    rp, rc = None, F64
+    if residual is not None:
+        rq, rc = _qkv_arg(residual)
+        assert rq.shape == lead + (N,)
+        rp = _ptr(rq)
+    y = np.empty(lead + (N,), dtype=np.float64)
+    used = lib().oracle_linear(_ptr(xq), xc, T, K, _ptr(wq), wc, N, bp, rp, rc, nthreads, _ptr(y))
+    if used < 0:
+        raise ValueError("oracle rejected the arguments")
+    return y

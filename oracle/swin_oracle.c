@@ -330,3 +330,50 @@ int oracle_swin_wattn_windows(const void* qkv, int dtype, const float* table, in
   free(msel);
   return used;
 }
+
+/* ---------------------------------------------------------------------- */
+/* linear layer: every output element is its own dot product in fp64 */
+
+typedef struct {
+  const void* x;
+  const void* w;
+  const void* r;
+  const float* bias;
+  int xdtype, wdtype, rdtype, K, N;
+  long t0, t1;
+  double* y;
+} linear_job;
+
+static void* linear_worker(void* arg) {
+  const linear_job* J = (const linear_job*)arg;
+  for (long t = J->t0; t < J->t1; ++t)
+    for (int j = 0; j < J->N; ++j) {
+      double acc = 0.0;
+      for (int c = 0; c < J->K; ++c)
+        acc += load_elem(J->x, J->xdtype, t * J->K + c) * load_elem(J->w, J->wdtype, (long)j * J->K + c);
+      if (J->bias) acc += (double)J->bias[j];
+      if (J->r) acc += load_elem(J->r, J->rdtype, t * J->N + j);
+      J->y[t * J->N + j] = acc;
+    }
+  return NULL;
+}
+
+int oracle_linear(const void* x, int xdtype, long T, int K, const void* w, int wdtype, int N,
+                  const float* bias, const void* residual, int rdtype, int nthreads, double* y) {
+  if (T < 0 || K <= 0 || N <= 0 || xdtype < ORACLE_F64 || xdtype > ORACLE_BF16 ||
+      wdtype < ORACLE_F64 || wdtype > ORACLE_BF16 || rdtype < ORACLE_F64 || rdtype > ORACLE_BF16)
+    return -1;
+  nthreads = resolve_threads(nthreads, T > 0 ? T : 1);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  linear_job* jobs = (linear_job*)malloc(sizeof(linear_job) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    linear_job J = {x, w, residual, bias, xdtype, wdtype, rdtype, K, N,
+                    T * i / nthreads, T * (i + 1) / nthreads, y};
+    jobs[i] = J;
+    pthread_create(&th[i], NULL, linear_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  return nthreads;
+}

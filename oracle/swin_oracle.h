@@ -93,6 +93,22 @@ int oracle_swin_wattn_windows(const void* qkv, int dtype, const float* table, in
                               int W, int nh, int d, int M, int s, long nsel, const int64_t* sel,
                               int nthreads, double* out, int64_t* pos);
 
+/* Linear layer with bias and optional residual, the operations on either
+ * side of the attention:
+ *   y[t][j] = sum_c x[t][c] * w[j][c] + bias[j]  (+ residual[t][j])
+ * x [T][K] of type xdtype; w [N][K] of type wdtype (out_features x
+ * in_features); bias [N] fp32 or NULL (no bias); residual [T][N] of type
+ * rdtype or NULL (no residual); y [T][N] fp64.
+ *  - QKV GEMM + bias: K = C, N = 3C, output columns in [3][nh][d] order,
+ *    which is the qkv token row the attention reads (NVIDIA talk, section 3
+ *    "inference optimization": the QKV GEMM is fused with its bias, in a
+ *    format prepared for the attention kernel).
+ *  - Output projection + bias + residual: K = N = C (same section: the
+ *    add-bias-then-add-residual kernel).
+ * Returns the thread count used, or -1 on bad arguments. */
+int oracle_linear(const void* x, int xdtype, long T, int K, const void* w, int wdtype, int N,
+                  const float* bias, const void* residual, int rdtype, int nthreads, double* y);
+
 #ifdef __cplusplus
 }
 #endif

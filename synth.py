@@ -120,3 +120,41 @@ def workload_inputs(name: str, batch: int | None = None):
     B = w["B"] if batch is None else batch
     return make_inputs(B, w["H"], w["W"], w["heads"], w["head_dim"], w["window"], w["seed"],
                        w["dtype"])
+
+
+# ---------------------------------------------------------------------------
+# Linear-layer workloads on either side of the attention, at Swin stage
+# shapes: the QKV projection (K = C, N = 3C, with bias) and the output
+# projection (K = N = C, with bias and residual).  tokens = B * H * W.
+
+LINEAR_WORKLOADS = {
+    "qkv-t-s1": dict(tokens=32 * 56 * 56, K=96, N=288, residual=False, seed=2001,
+                     desc="Swin-T stage 1 QKV projection, B=32, 56x56, C=96"),
+    "qkv-t-s3": dict(tokens=64 * 14 * 14, K=384, N=1152, residual=False, seed=2002,
+                     desc="Swin-T stage 3 QKV projection, B=64, 14x14, C=384"),
+    "qkv-l-s1": dict(tokens=64 * 56 * 56, K=192, N=576, residual=False, seed=2003,
+                     desc="Swin-L stage 1 QKV projection, B=64, 56x56, C=192"),
+    "proj-l-s1": dict(tokens=64 * 56 * 56, K=192, N=192, residual=True, seed=2004,
+                      desc="Swin-L stage 1 output projection + residual, B=64, 56x56, C=192"),
+    "proj-t-s3": dict(tokens=64 * 14 * 14, K=384, N=384, residual=True, seed=2005,
+                      desc="Swin-T stage 3 output projection + residual, B=64, 14x14, C=384"),
+}
+
+
+def make_linear_inputs(T: int, K: int, N: int, seed: int, residual: bool,
+                       x_std: float = 1.0, w_std: float = 0.02, bias_std: float = 0.02):
+    """Returns ``(x, w, bias, res)``: ``x [T, K]`` and ``w [N, K]`` as bfloat16
+    patterns, ``bias [N]`` float32, ``res [T, N]`` bfloat16 patterns or None.
+    A smaller T gives a prefix of the tokens of a larger one."""
+    x = bf16_bits(normal(stream_key(seed, 0), T * K, x_std)).reshape(T, K)
+    w = bf16_bits(normal(stream_key(seed, 1), N * K, w_std)).reshape(N, K)
+    bias = normal(stream_key(seed, 2), N, bias_std)
+    res = bf16_bits(normal(stream_key(seed, 3), T * N, 1.0)).reshape(T, N) if residual else None
+    return x, w, bias, res
+
+
+def linear_inputs(name: str, tokens: int | None = None):
+    """Inputs of a named linear workload (optionally its first `tokens` tokens)."""
+    w = LINEAR_WORKLOADS[name]
+    T = w["tokens"] if tokens is None else tokens
+    return make_linear_inputs(T, w["K"], w["N"], w["seed"], w["residual"])

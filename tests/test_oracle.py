@@ -330,3 +330,77 @@ def test_thread_count_does_not_change_result(oracle_lib):
     a = oracle.swin_wattn_fwd(q, table, 7, 3, nthreads=1)
     b = oracle.swin_wattn_fwd(q, table, 7, 3, nthreads=3)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- linear layer
+
+def test_linear_golden(oracle_lib):
+    x = np.array([[1, 2, 3], [-1, 0, 2]], dtype=np.float64)
+    w = np.array([[1, 0, -1], [2, 1, 0]], dtype=np.float64)
+    b = np.array([0.5, -1], dtype=np.float32)
+    r = np.array([[10, 20], [30, 40]], dtype=np.float64)
+    assert np.array_equal(oracle.linear(x, w, b, r), _golden("linear_t2_k3_n2.txt"))
+
+
+@pytest.mark.parametrize("T,K,N,with_bias,with_res", [(1, 1, 1, True, False), (37, 96, 288, True, False),
+                                                       (64, 192, 576, True, False),
+                                                       (50, 192, 192, True, True), (9, 32, 64, False, True),
+                                                       (0, 32, 96, True, True)])
+def test_linear_matches_numpy_float64(oracle_lib, T, K, N, with_bias, with_res):
+    """Special case reducing to a library routine: numpy's float64 matmul."""
+    rng = _rng(T * 7 + K + N)
+    x, w = rng.standard_normal((T, K)), rng.standard_normal((N, K)) * 0.05
+    b = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    r = rng.standard_normal((T, N)) if with_res else None
+    ref = x @ w.T
+    if with_bias:
+        ref = ref + b.astype(np.float64)
+    if with_res:
+        ref = ref + r
+    got = oracle.linear(x, w, b, r)
+    assert got.shape == (T, N)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_identity_and_one_hot(oracle_lib):
+    """Closed forms: w = I gives x + bias exactly; a one-hot row j -> c copies
+    input channel c to output j (a transposed operand would fail this)."""
+    rng = _rng(5)
+    x = rng.standard_normal((11, 8))
+    b = rng.standard_normal(8).astype(np.float32)
+    assert np.array_equal(oracle.linear(x, np.eye(8), b), x + b.astype(np.float64))
+    w = np.zeros((3, 8))
+    w[0, 5] = w[1, 0] = w[2, 7] = 1.0
+    assert np.array_equal(oracle.linear(x, w), x[:, [5, 0, 7]])
+
+
+def test_linear_bf16_read_exactly(oracle_lib):
+    rng = _rng(6)
+    x = synth.bf16_bits(rng.standard_normal((13, 32)).astype(np.float32))
+    w = synth.bf16_bits((rng.standard_normal((64, 32)) * 0.02).astype(np.float32))
+    r = synth.bf16_bits(rng.standard_normal((13, 64)).astype(np.float32))
+    xf, wf, rf = (synth.bf16_to_f32(a).astype(np.float64) for a in (x, w, r))
+    assert np.array_equal(oracle.linear(x, w, None, r), oracle.linear(xf, wf, None, rf))
+
+
+def test_linear_thread_count_does_not_change_result(oracle_lib):
+    rng = _rng(8)
+    x, w = rng.standard_normal((101, 64)), rng.standard_normal((96, 64))
+    assert np.array_equal(oracle.linear(x, w, nthreads=1), oracle.linear(x, w, nthreads=7))
+
+
+def test_qkv_columns_are_the_attention_layout(oracle_lib):
+    """Reading: the QKV projection's N = 3C outputs are ordered [3][heads][d],
+    so reshaping a token row to (3, heads, d) gives q, k, v per head; output
+    row (i, h, e) of the weight produces component i of head h, channel e."""
+    rng = _rng(9)
+    nh, d, C = 3, 32, 96
+    x = rng.standard_normal((2, 4, 4, C))
+    w = rng.standard_normal((3 * C, C)) * 0.05
+    b = rng.standard_normal(3 * C).astype(np.float32)
+    qkv = oracle.linear(x, w, b).reshape(2, 4, 4, 3, nh, d)
+    for i in range(3):
+        for h in range(nh):
+            rows = slice((i * nh + h) * d, (i * nh + h + 1) * d)
+            ref = x @ w[rows].T + b[rows].astype(np.float64)
+            assert np.allclose(qkv[:, :, :, i, h, :], ref, rtol=1e-12, atol=1e-12)

@@ -37,3 +37,15 @@ def test_smaller_batch_is_a_prefix():
     a, ta = synth.workload_inputs("swin-t-s3", batch=2)
     b, tb = synth.make_inputs(3, 14, 14, 12, 32, 7, seed=1003)
     assert np.array_equal(a, b[:2]) and np.array_equal(ta, tb)
+
+
+def test_linear_inputs_prefix_and_shapes():
+    for name, w in synth.LINEAR_WORKLOADS.items():
+        x, wt, b, r = synth.linear_inputs(name, tokens=5)
+        x2, wt2, b2, r2 = synth.linear_inputs(name, tokens=9)
+        assert x.shape == (5, w["K"]) and wt.shape == (w["N"], w["K"]) and b.shape == (w["N"],)
+        assert x.dtype == np.uint16 and wt.dtype == np.uint16 and b.dtype == np.float32
+        assert np.array_equal(x, x2[:5]) and np.array_equal(wt, wt2) and np.array_equal(b, b2)
+        assert (r is None) == (not w["residual"])
+        if r is not None:
+            assert r.shape == (5, w["N"]) and np.array_equal(r, r2[:5])
