@@ -93,6 +93,35 @@ int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int 
 int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out, int B, int H,
                        int W, int heads, int head_dim, int window, int shift, void* stream);
 
+/* Linear layer on either side of the attention, bf16 with fp32 accumulation:
+ *   y[t][j] = sum_c x[t][c] * W[j][c] + bias[j]  (+ residual[t][j])
+ *  - QKV GEMM + bias (K = C, N = 3C): the output token row is [3][heads][d],
+ *    the qkv row swin_wattn_fwd reads (NVIDIA talk, section 3: the QKV GEMM
+ *    fused with its bias, the weight put in a kernel-friendly format once).
+ *  - Output projection + bias + residual (K = N = C): the same talk,
+ *    section 3, adds a bias and then the residual in one kernel.
+ *
+ * swin_linear_pack_weight: W [N][K] bf16 (out_features x in_features, the
+ * nn.Linear layout), device pointer, 16-byte aligned -> packed, N*K bf16 in
+ * the operand order swin_linear_fwd reads; caller-owned device memory that
+ * must not overlap W.  Once per weight; queued on `stream`.
+ *
+ * swin_linear_fwd:
+ *   x         [T][K] bf16, contiguous, 16-byte aligned (device)
+ *   packed    the output of swin_linear_pack_weight for this W
+ *   bias      [N] float32, 16-byte aligned, or NULL (no bias)
+ *   residual  [T][N] bf16, 16-byte aligned, or NULL (no residual); may be y
+ *             itself (in-place add), otherwise must not overlap y
+ *   y         [T][N] bf16, 16-byte aligned; must not overlap x, packed, bias
+ * Products of bf16 inputs accumulate in float32; bias and residual are added
+ * in float32; y is rounded to nearest-even bf16.  K and N must be positive
+ * multiples of 32 (else SWIN_ERR_INVALID_ARG); K <= 384 (else
+ * SWIN_ERR_UNSUPPORTED).  T == 0 queues nothing.  No allocation, no host
+ * synchronisation. */
+int swin_linear_pack_weight(const void* weight, void* packed, int N, int K, void* stream);
+int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
+                    const void* residual, void* y, long long T, int K, int N, void* stream);
+
 /* Copies of the precomputed tensors into caller-owned device memory, queued
  * on `stream` (for verification).  SWIN_ERR_NOT_PREPARED without a prior
  * swin_wattn_precompute for the key.

@@ -30,6 +30,7 @@ SWIN_ERR_HIP = -4
 
 EXPORTS = ("swin_wattn_precompute", "swin_wattn_fwd", "swin_wattn_fwd_f32",
            "swin_wattn_copy_index", "swin_wattn_copy_mask", "swin_wattn_copy_region",
+           "swin_linear_pack_weight", "swin_linear_fwd",
            "swin_wattn_release", "swin_wattn_status_string")
 
 
@@ -51,6 +52,8 @@ _lib.swin_wattn_fwd.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]
 _lib.swin_wattn_fwd_f32.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]
 for _n in ("swin_wattn_copy_index", "swin_wattn_copy_mask", "swin_wattn_copy_region"):
     getattr(_lib, _n).argtypes = [_I, _I, _I, _I, _P, _P]
+_lib.swin_linear_pack_weight.argtypes = [_P, _P, _I, _I, _P]
+_lib.swin_linear_fwd.argtypes = [_P, _P, _P, _P, _P, ctypes.c_longlong, _I, _I, _P]
 _lib.swin_wattn_release.argtypes = []
 _lib.swin_wattn_status_string.argtypes = [_I]
 _lib.swin_wattn_status_string.restype = ctypes.c_char_p
@@ -102,6 +105,16 @@ def swin_wattn_copy_mask(H: int, W: int, window: int, shift: int, dst, stream=No
 
 def swin_wattn_copy_region(H: int, W: int, window: int, shift: int, dst, stream=None) -> int:
     return _lib.swin_wattn_copy_region(H, W, window, shift, _addr(dst), _stream(stream))
+
+
+def swin_linear_pack_weight(weight, packed, N: int, K: int, stream=None) -> int:
+    return _lib.swin_linear_pack_weight(_addr(weight), _addr(packed), N, K, _stream(stream))
+
+
+def swin_linear_fwd(x, packed_weight, bias, residual, y, T: int, K: int, N: int,
+                    stream=None) -> int:
+    return _lib.swin_linear_fwd(_addr(x), _addr(packed_weight), _addr(bias), _addr(residual),
+                                _addr(y), T, K, N, _stream(stream))
 
 
 def swin_wattn_release() -> int:

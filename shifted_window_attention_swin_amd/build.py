@@ -19,7 +19,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libswinattn.so")
-SOURCES = ["swinattn_api.hip", "wattn_kernels.hip", "wattn_persistent.hip"]
+SOURCES = ["swinattn_api.hip", "wattn_kernels.hip", "wattn_persistent.hip", "linear_gemm.hip"]
 ARCH = "gfx950"
 
 

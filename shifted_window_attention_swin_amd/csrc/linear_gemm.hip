@@ -1,0 +1,334 @@
+// Linear layer with bias and optional residual, the operations on either side
+// of the window attention (gfx950):
+//
+//   y[t][j] = sum_c x[t][c] * W[j][c] + bias[j]  (+ residual[t][j])
+//
+//  - QKV GEMM + bias: K = C, N = 3C.  The output token row is [3][heads][d],
+//    the qkv row the attention kernel reads.  The NVIDIA talk "Swin
+//    Transformer training and inference optimization" (uticex.com 1598),
+//    section 3, fuses the QKV GEMM with its bias and transforms the weight
+//    into a kernel-friendly format ahead of time; here that format is the
+//    MFMA operand order of swin_linear_pack_weight.
+//  - Output projection + bias + residual: K = N = C (same section: the kernel
+//    that adds a bias, then the residual).
+//
+// At Swin sizes K = C is small (96..384), so the layer moves more bytes than
+// it does arithmetic per byte (Swin-L stage 1 QKV: 144 FLOP/B against a bf16
+// ridge of about 310): the kernel is built to stream x and y at HBM speed.
+//
+//   row block  32 tokens x K, staged in LDS as 1 KB blocks of 16 tokens x 64
+//              bytes (32 input channels), read in the conflict-free order the
+//              MFMA B operand wants; the next block waits in registers.
+//   workgroup  6, 4 or 2 waves (the widest that divides N / 32), persistent,
+//              owning one column group (a 32-channel block per wave: whole
+//              128-byte lines of every token) for the whole launch and
+//              walking row blocks;
+//              the column groups of a row block run side by side on one XCD,
+//              so x comes from HBM once and from that XCD's L2 after.
+//   weight     packed once: column block cb, k-step ks, tile i is one 1 KB
+//              MFMA A operand.  Each wave loads its block's tiles into
+//              registers once and keeps them.
+//   product    D = W_tile * x^T: D rows are output channels, columns tokens.
+//              Row m of packed tile i carries channel out_channel(i, m), so a
+//              lane ends with 8 consecutive channels of one token.
+//   epilogue   the fp32 products go through an LDS tile so that every store
+//              instruction writes whole lines (8 tokens x 128 bytes): + bias,
+//              + residual (read as whole lines too), round to bf16,
+//              non-temporal 16-byte stores.  Halves of a line written by
+//              different waves cost a quarter more HBM write traffic.
+
+#include <atomic>
+
+#include "wattn_common.h"
+
+namespace swinattn {
+namespace {
+
+constexpr int kLinRows = 32;               // tokens per row block: 2 tiles of 16
+constexpr int kLinTiles = kLinRows / 16;
+// bytes per token of the fp32 output tile of a WAVES-wave workgroup (padded)
+constexpr int lin_out_stride(int waves) { return waves * 32 * 4 + 16; }
+
+// WAVES waves per workgroup, one 32-column block each: the workgroup's
+// WAVES * 32 channels are WAVES / 2 whole 128-byte lines of every token
+template <int KS, bool RES, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) {
+  constexpr int kLinWaves = WAVES;
+  constexpr int kLinCols = 32 * WAVES;
+  constexpr int kOutStride = lin_out_stride(WAVES);
+  constexpr int NB = kLinTiles * KS;                      // LDS blocks per row block
+  constexpr int BPW = (NB + kLinWaves - 1) / kLinWaves;   // blocks loaded per wave
+  constexpr int CPT = kLinCols / 8;                       // 16-byte chunks per token
+  extern __shared__ char s_lds[];
+  char* s_x = s_lds;              // NB blocks of 1 KB: the row block of x
+  char* s_o = s_lds + NB * 1024;  // kLinRows x kOutStride: the fp32 output tile
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wv >= 0 && wv < kLinWaves);
+  const int T = (int)p.T;                   // the host keeps T below 2^31
+  const int gq = lane & 3, cq = lane >> 2;  // load layout: 16-byte part, token
+  const int g = lane >> 4, c = lane & 15;   // MFMA layout: lane group, token
+  const char* xb = static_cast<const char*>(p.x);
+  const char* rb = static_cast<const char*>(p.res);
+  char* yb = static_cast<char*>(p.y);
+  const size_t xrow = (size_t)KS * 64;      // bytes of one x row
+  const size_t yrow = (size_t)p.N * 2;      // bytes of one y (residual) row
+
+  // This workgroup's column group and row blocks.  The grid is a multiple
+  // of the column-group count, so a workgroup keeps one column group for the
+  // whole launch.  When the grid also covers the 8 XCDs evenly, each XCD
+  // owns a contiguous range of row blocks and the column groups of a row
+  // block run side by side on one XCD: x is fetched into its L2 once.
+  const int G = gridDim.x, id = blockIdx.x, ncg = p.ncg;
+  int cg, r, step, r_end;
+  if (G % (8 * ncg) == 0) {
+    const int x = id & 7, j = id >> 3, per = G >> 3;
+    cg = j % ncg;
+    step = per / ncg;
+    r = (int)((long long)p.blocks * x / 8) + j / ncg;
+    r_end = (int)((long long)p.blocks * (x + 1) / 8);
+  } else {
+    cg = id % ncg;
+    step = G / ncg;
+    r = id / ncg;
+    r_end = p.blocks;
+  }
+  const int cb = cg * kLinWaves + wv;  // this wave's column block (product phase)
+  const bool active = cb < p.ncb;
+  // store phase: the output tile is kLinRows * CPT chunks of 16 bytes (8
+  // channels); wave wv stores chunks 128 wv + 64 j + lane, j = 0, 1, in
+  // token-major order, so consecutive lanes cover whole lines of a token
+  int srow[2], sch[2];
+  bool s_active[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = 128 * wv + 64 * j + lane;
+    srow[j] = q / CPT;
+    sch[j] = cg * kLinCols + 8 * (q - srow[j] * CPT);
+    s_active[j] = sch[j] < p.N;
+  }
+
+  // the wave's weight tiles stay in registers for the whole launch
+  bf16x8 a[KS][2];
+  if (active) {
+    const char* wcb = static_cast<const char*>(p.wp) + (size_t)cb * KS * 2048 + lane * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      a[ks][0] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2) * 1024);
+      a[ks][1] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2 + 1) * 1024);
+    }
+  }
+  f32x4 bias[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    bias[j][0] = bias[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s_active[j] && p.bias) {
+      bias[j][0] = *reinterpret_cast<const f32x4*>(p.bias + sch[j]);
+      bias[j][1] = *reinterpret_cast<const f32x4*>(p.bias + sch[j] + 4);
+    }
+  }
+
+  // register-staged loads of row block rr: LDS block bi = tile * KS + k-step;
+  // rows past the end load the last row (finite stand-in data, not stored)
+  using Regs = u32x4[BPW];
+  auto issue = [&](Regs& R, int rr) {
+#pragma unroll
+    for (int k = 0; k < BPW; ++k) {
+      const int bi = wv + kLinWaves * k;
+      if (bi < NB) {
+        const int tt = bi / KS, ks = bi - tt * KS;
+        int tok = rr * kLinRows + tt * 16 + cq;
+        if (tok >= T) tok = T - 1;
+        R[k] = *reinterpret_cast<const u32x4*>(xb + (size_t)tok * xrow + ks * 64 + 16 * gq);
+      }
+    }
+  };
+  auto write = [&](const Regs& R) {
+#pragma unroll
+    for (int k = 0; k < BPW; ++k) {
+      const int bi = wv + kLinWaves * k;
+      if (bi < NB) *reinterpret_cast<u32x4*>(s_x + bi * 1024 + lane * 16) = R[k];
+    }
+  };
+
+  Regs R;
+  if (r < r_end) issue(R, r);
+  for (; r < r_end; r += step) {
+    write(R);
+    __syncthreads();  // row block visible to every wave
+    const int tok0 = r * kLinRows;
+    // the residual goes out before the next row block's loads, so waiting
+    // for it never waits for them (vector memory returns count in order)
+    bf16x8 res[RES ? 2 : 1];
+    if constexpr (RES) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (s_active[j]) {
+          int tok = tok0 + srow[j];
+          if (tok >= T) tok = T - 1;
+          res[j] = *reinterpret_cast<const bf16x8*>(rb + (size_t)tok * yrow + sch[j] * 2);
+        }
+    }
+    if (r + step < r_end) issue(R, r + step);
+    if (active) {
+      f32x4 acc[kLinTiles][2];
+#pragma unroll
+      for (int tt = 0; tt < kLinTiles; ++tt) acc[tt][0] = acc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        // keep each k-step's operand reads next to its products: hoisting
+        // every read of the row block would hold 8 * KS registers
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < kLinTiles; ++tt) {
+          const bf16x8 b =
+              *reinterpret_cast<const bf16x8*>(s_x + (tt * KS + ks) * 1024 + (4 * c + g) * 16);
+          acc[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][0], b, acc[tt][0], 0, 0, 0);
+          acc[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][1], b, acc[tt][1], 0, 0, 0);
+        }
+      }
+      // lane (g, c) holds channels 8g + 4i + q of the wave's block for
+      // token c of each tile: 8 consecutive floats of the output tile
+#pragma unroll
+      for (int tt = 0; tt < kLinTiles; ++tt) {
+        char* o = s_o + (tt * 16 + c) * kOutStride + (wv * 32 + 8 * g) * 4;
+        *reinterpret_cast<f32x4*>(o) = acc[tt][0];
+        *reinterpret_cast<f32x4*>(o + 16) = acc[tt][1];
+      }
+    }
+    __syncthreads();  // output tile complete
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tok = tok0 + srow[j];
+      if (s_active[j] && tok < T) {
+        const char* o = s_o + srow[j] * kOutStride + (sch[j] - cg * kLinCols) * 4;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(o);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(o + 16);
+        bf16x8 out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float y0 = v0[q] + bias[j][0][q], y1 = v1[q] + bias[j][1][q];
+          if constexpr (RES) {
+            y0 += (float)res[j][q];
+            y1 += (float)res[j][4 + q];
+          }
+          out[q] = (__bf16)y0;
+          out[4 + q] = (__bf16)y1;
+        }
+        __builtin_nontemporal_store(out, reinterpret_cast<bf16x8*>(yb + (size_t)tok * yrow + sch[j] * 2));
+      }
+    }
+    __syncthreads();  // every wave is done with both tiles before they are overwritten
+  }
+}
+
+// packed[cb][ks][i][lane][s] = W[cb*32 + out_channel(i, lane % 16)][ks*32 + 8*(lane/16) + s]
+__global__ void linear_pack_kernel(const uint16_t* w, uint16_t* wp, int N, int K) {
+  const int KS = K / 32;
+  const long long total = (long long)(N / 32) * KS * 2 * 64;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(e & 63);
+    const long long t = e >> 6;  // (cb * KS + ks) * 2 + i
+    const int i = (int)(t & 1);
+    const long long cks = t >> 1;
+    const int ks = (int)(cks % KS), cb = (int)(cks / KS);
+    const int row = cb * 32 + out_channel(i, lane % 16);
+    const int col = ks * 32 + 8 * (lane / 16);
+    *reinterpret_cast<u32x4*>(wp + e * 8) =
+        *reinterpret_cast<const u32x4*>(w + (size_t)row * K + col);
+  }
+}
+
+// waves per workgroup for N / 32 column blocks: the widest whole-line
+// group that divides them (fewer re-reads of x), else 2
+int linear_waves(int ncb) { return ncb % 6 == 0 ? 6 : ncb % 4 == 0 ? 4 : 2; }
+
+size_t linear_lds_waves(int K, int waves) {
+  return (size_t)kLinTiles * (K / 32) * 1024 + (size_t)kLinRows * lin_out_stride(waves);
+}
+
+template <int KS, bool RES, int WAVES>
+int linear_blocks_per_cu(int dev) {
+  static std::atomic<int> cache[kMaxDevices];
+  const bool cacheable = dev >= 0 && dev < kMaxDevices;
+  if (cacheable) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, linear_fwd_kernel<KS, RES, WAVES>,
+                                                   WAVES * 64, linear_lds_waves(KS * 32, WAVES)) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (cacheable) cache[dev].store(per_cu, std::memory_order_relaxed);
+  return per_cu;
+}
+
+template <int KS, bool RES, int WAVES>
+hipError_t launch_linear_krw(LinearParams p, int dev, int cus, hipStream_t st) {
+  p.ncg = (p.ncb + WAVES - 1) / WAVES;
+  // a multiple of the column groups (each workgroup keeps one), and of
+  // 8 x that when large enough (even XCD shares); never more than the units
+  const long long units = (long long)p.blocks * p.ncg;
+  long long grid = (long long)cus * linear_blocks_per_cu<KS, RES, WAVES>(dev);
+  if (grid > units) grid = units;
+  if (grid >= 8LL * p.ncg) grid -= grid % (8LL * p.ncg);
+  else grid -= grid % p.ncg;
+  hipLaunchKernelGGL((linear_fwd_kernel<KS, RES, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64),
+                     linear_lds_waves(KS * 32, WAVES), st, p);
+  return hipGetLastError();
+}
+
+template <int KS, bool RES>
+hipError_t launch_linear_kr(const LinearParams& p, int dev, int cus, hipStream_t st) {
+  switch (linear_waves(p.ncb)) {
+    case 6: return launch_linear_krw<KS, RES, 6>(p, dev, cus, st);
+    case 4: return launch_linear_krw<KS, RES, 4>(p, dev, cus, st);
+    default: return launch_linear_krw<KS, RES, 2>(p, dev, cus, st);
+  }
+}
+
+template <int KS>
+hipError_t launch_linear_ks(const LinearParams& p, int dev, int cus, hipStream_t st) {
+  return p.res ? launch_linear_kr<KS, true>(p, dev, cus, st)
+               : launch_linear_kr<KS, false>(p, dev, cus, st);
+}
+
+}  // namespace
+
+size_t linear_lds_bytes(int K, int N) { return linear_lds_waves(K, linear_waves(N / 32)); }
+
+hipError_t launch_linear_pack(const void* w, void* wp, int N, int K, hipStream_t stream) {
+  const long long total = (long long)(N / 32) * (K / 32) * 2 * 64;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(linear_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(w), static_cast<uint16_t*>(wp), N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear(const LinearParams& q, int dev, int cus, hipStream_t stream) {
+  LinearParams p = q;
+  p.blocks = (int)((p.T + kLinRows - 1) / kLinRows);
+  switch (p.K / 32) {
+    case 1: return launch_linear_ks<1>(p, dev, cus, stream);
+    case 2: return launch_linear_ks<2>(p, dev, cus, stream);
+    case 3: return launch_linear_ks<3>(p, dev, cus, stream);
+    case 4: return launch_linear_ks<4>(p, dev, cus, stream);
+    case 5: return launch_linear_ks<5>(p, dev, cus, stream);
+    case 6: return launch_linear_ks<6>(p, dev, cus, stream);
+    case 7: return launch_linear_ks<7>(p, dev, cus, stream);
+    case 8: return launch_linear_ks<8>(p, dev, cus, stream);
+    case 9: return launch_linear_ks<9>(p, dev, cus, stream);
+    case 10: return launch_linear_ks<10>(p, dev, cus, stream);
+    case 11: return launch_linear_ks<11>(p, dev, cus, stream);
+    case 12: return launch_linear_ks<12>(p, dev, cus, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swinattn

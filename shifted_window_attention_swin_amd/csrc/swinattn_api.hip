@@ -231,6 +231,54 @@ int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out
                     false);
 }
 
+int swin_linear_pack_weight(const void* weight, void* packed, int N, int K, void* stream) {
+  if (!weight || !packed || !aligned(weight, 16) || !aligned(packed, 16)) return SWIN_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return SWIN_ERR_INVALID_ARG;
+  if (K > kMaxLinearK) return SWIN_ERR_UNSUPPORTED;
+  const size_t bytes = (size_t)N * K * 2;
+  if (overlap(weight, bytes, packed, bytes)) return SWIN_ERR_INVALID_ARG;
+  return launch_linear_pack(weight, packed, N, K, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SWIN_OK
+             : SWIN_ERR_HIP;
+}
+
+int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
+                    const void* residual, void* y, long long T, int K, int N, void* stream) {
+  if (!x || !packed_weight || !y) return SWIN_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(packed_weight, 16) || !aligned(y, 16) ||
+      (bias && !aligned(bias, 16)) || (residual && !aligned(residual, 16)))
+    return SWIN_ERR_INVALID_ARG;
+  if (T < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return SWIN_ERR_INVALID_ARG;
+  if (K > kMaxLinearK) return SWIN_ERR_UNSUPPORTED;
+  const size_t xb = (size_t)T * K * 2, yb = (size_t)T * N * 2, wb = (size_t)N * K * 2;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, packed_weight, wb) ||
+      (bias && overlap(y, yb, bias, (size_t)N * 4)))
+    return SWIN_ERR_INVALID_ARG;
+  // the residual may be y itself (in-place residual add), or lie apart from it
+  if (residual && residual != y && overlap(y, yb, residual, yb)) return SWIN_ERR_INVALID_ARG;
+  if (T == 0) return SWIN_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SWIN_ERR_HIP;
+  const int cus = compute_units(dev);
+  LinearParams p;
+  p.wp = packed_weight;
+  p.bias = bias;
+  p.K = K;
+  p.N = N;
+  p.ncb = N / 32;
+  // token indices inside the kernel are 32-bit: at most 2^30 tokens a launch
+  for (long long t0 = 0; t0 < T; t0 += kMaxLinearTokens) {
+    const long long n = T - t0 < kMaxLinearTokens ? T - t0 : kMaxLinearTokens;
+    p.x = static_cast<const char*>(x) + t0 * K * 2;
+    p.res = residual ? static_cast<const char*>(residual) + t0 * N * 2 : nullptr;
+    p.y = static_cast<char*>(y) + t0 * N * 2;
+    p.T = n;
+    if (launch_linear(p, dev, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
+      return SWIN_ERR_HIP;
+  }
+  return SWIN_OK;
+}
+
 int swin_wattn_copy_index(int H, int W, int window, int shift, int32_t* dst, void* stream) {
   return copy_common(H, W, window, shift, dst, 0, stream);
 }

@@ -52,4 +52,24 @@ hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int dev
                                       hipStream_t stream);
 size_t persistent_lds_bytes(int M, int HG, int nh);
 
+// Linear layer y = x W^T + bias (+ residual), bf16 in and out, fp32 bias
+// (linear_gemm.hip).  K and N are multiples of 32, K <= kMaxLinearK.
+constexpr int kMaxLinearK = 384;
+constexpr long long kMaxLinearTokens = 1LL << 30;  // tokens per launch (32-bit indices)
+struct LinearParams {
+  const void* x;      // [T][K] bf16
+  const void* wp;     // packed weight [N/32][K/32][2][64][8] bf16
+  const float* bias;  // [N] or null
+  const void* res;    // [T][N] bf16 or null
+  void* y;            // [T][N] bf16
+  long long T;
+  int K, N;
+  int ncb;     // N / 32 column blocks
+  int ncg;     // column groups, one per workgroup (set by launch_linear)
+  int blocks;  // row blocks (set by launch_linear)
+};
+size_t linear_lds_bytes(int K, int N);
+hipError_t launch_linear_pack(const void* w, void* wp, int N, int K, hipStream_t stream);
+hipError_t launch_linear(const LinearParams& p, int dev, int cus, hipStream_t stream);
+
 }  // namespace swinattn

@@ -19,7 +19,7 @@ A16, A32, A48 = 1 << 20, 2 << 20, 3 << 20
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*|void)\s+(swin_wattn_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*|void)\s+(swin_\w+)\s*\(", src, re.M)))
 
 
 def test_header_declares_the_binding_names():
@@ -29,7 +29,7 @@ def test_header_declares_the_binding_names():
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", swa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT\s+(swin_wattn_\w+)", out))
+    exported = set(re.findall(r"\bT\s+(swin_\w+)", out))
     for name in _declared():
         assert name in exported, name
         assert hasattr(swa.library(), name)
@@ -98,3 +98,32 @@ def test_precompute_and_copies_reject_invalid_shapes():
     for fn in (swa.swin_wattn_copy_index, swa.swin_wattn_copy_mask, swa.swin_wattn_copy_region):
         assert fn(14, 14, 7, 3, 0) == E
         assert fn(14, 14, 7, 9, A16) == E
+
+
+def test_linear_rejects_invalid_arguments():
+    E, U = swa.SWIN_ERR_INVALID_ARG, swa.SWIN_ERR_UNSUPPORTED
+    a, b, c = 1 << 20, 2 << 20, 3 << 20      # aligned, distinct, never dereferenced
+    assert swa.swin_linear_fwd(0, b, None, None, c, 64, 192, 576) == E          # null x
+    assert swa.swin_linear_fwd(a, 0, None, None, c, 64, 192, 576) == E          # null weight
+    assert swa.swin_linear_fwd(a, b, None, None, 0, 64, 192, 576) == E          # null y
+    assert swa.swin_linear_fwd(a + 8, b, None, None, c, 64, 192, 576) == E      # misaligned x
+    assert swa.swin_linear_fwd(a, b, a + 4, None, c, 64, 192, 576) == E         # misaligned bias
+    assert swa.swin_linear_fwd(a, b, None, c + 8, c, 64, 192, 576) == E         # misaligned residual
+    assert swa.swin_linear_fwd(a, b, None, None, c, -1, 192, 576) == E          # negative T
+    assert swa.swin_linear_fwd(a, b, None, None, c, 64, 100, 576) == E          # K % 32
+    assert swa.swin_linear_fwd(a, b, None, None, c, 64, 192, 500) == E          # N % 32
+    assert swa.swin_linear_fwd(a, b, None, None, c, 64, 0, 576) == E
+    assert swa.swin_linear_fwd(a, b, None, None, c, 64, 416, 576) == U          # K > 384
+    assert swa.swin_linear_fwd(a, b, None, None, a, 64, 192, 576) == E          # y overlaps x
+    assert swa.swin_linear_fwd(a, b, None, c + 64, c, 64, 192, 576) == E        # residual overlaps y
+    assert swa.swin_linear_pack_weight(0, b, 576, 192) == E
+    assert swa.swin_linear_pack_weight(a, b, 576, 100) == E
+    assert swa.swin_linear_pack_weight(a, b, 500, 192) == E
+    assert swa.swin_linear_pack_weight(a, a, 576, 192) == E                     # packed overlaps W
+    assert swa.swin_linear_pack_weight(a, b, 576, 416) == U
+
+
+def test_linear_empty_is_a_no_op():
+    assert swa.swin_linear_fwd(1 << 20, 2 << 20, None, None, 3 << 20, 0, 192, 576) == swa.SWIN_OK
+    # in-place residual (residual == y) is accepted
+    assert swa.swin_linear_fwd(1 << 20, 2 << 20, None, 3 << 20, 3 << 20, 0, 192, 192) == swa.SWIN_OK
