@@ -7,6 +7,9 @@ the working set of the timed region exceeds twice the 256 MB Infinity Cache
 (cold cache).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+With --workload naming a linear-layer workload (qkv-l-s1, proj-l-s1, ...) a
+step is one swin_linear_fwd over its tokens instead.
 """
 from __future__ import annotations
 
@@ -28,14 +31,21 @@ MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
-    """Hash of every kernel source file: a committed traffic measurement is
-    only reported while the sources it was taken on are unchanged."""
+# the sources that define each kernel family's device code
+KERNEL_SOURCES = {
+    "wattn_fwd_bf16": ("wattn_internal.h", "wattn_common.h", "wattn_persistent.hip"),
+    "linear_fwd": ("wattn_internal.h", "wattn_common.h", "linear_gemm.hip"),
+}
+
+
+def kernel_source_hash(family: str = "wattn_fwd_bf16") -> str:
+    """Hash of the sources of a kernel family: a committed traffic
+    measurement is only reported while the sources it was taken on are
+    unchanged."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES[family]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -68,15 +78,15 @@ def fwd_kernel_name(window: int, heads: int) -> str:
     return f"wattn_fwd_bf16_kernel<{window}>"
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, family: str = "wattn_fwd_bf16"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"wattn_fwd_bf16_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{family}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(family):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -100,6 +110,139 @@ def cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_re
             "kind": "oracle",
             "sample": f"{name}, first {sample_batch} of {w['B']} images, whole forward x{reps} "
                       f"({dt:.1f} s wall, fp64, {used} threads)"}
+
+
+def time_steps(torch, step, K: int, warmup: int, stream, launches_per_step: int):
+    """W untimed steps, then K timed steps between two synchronisations (HIP
+    events on the launch stream); then K steps with an event pair around
+    each.  Returns (total_ms, avg_launch_s, isolated_launch_s)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    # average launch duration: the HIP events around the timed region, on the
+    # stream the kernel is launched on, over its launches (back to back: this
+    # is what a kernel trace's mean duration agrees with)
+    avg_launch_s = total_ms / 1e3 / (K * launches_per_step)
+    # for reference, launches timed one by one (each event pair adds its own
+    # overhead to the launch it brackets)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    isolated_s = sum(a.elapsed_time(b) for a, b in ev) / K / 1e3 / launches_per_step
+    return total_ms, avg_launch_s, isolated_s
+
+
+def linear_algorithmic(T, K, N, residual, elem=2):
+    """Bytes: x read once, y written once, the residual read once.  FLOPs:
+    one multiply-add per (token, input, output)."""
+    return (T * K + T * N * (2 if residual else 1)) * elem, 2 * T * K * N
+
+
+def linear_kernel_name(K: int, N: int, residual: bool) -> str:
+    """The linear kernel the library launches (mirrors its dispatch: 6, 4 or
+    2 waves, the widest that divides N / 32)."""
+    ncb = N // 32
+    waves = 6 if ncb % 6 == 0 else 4 if ncb % 4 == 0 else 2
+    return f"linear_fwd_kernel<{K // 32}, {str(residual).lower()}, {waves}>"
+
+
+def linear_cpu_baseline(name: str, min_seconds: float = 10.0):
+    """The fp64 oracle on the first tokens of the workload (grown until one
+    call takes about `min_seconds`), reported in GB/s of algorithmic bytes."""
+    import oracle
+    import synth
+    w = synth.LINEAR_WORKLOADS[name]
+    n = 512
+    while True:
+        x, wt, b, r = synth.linear_inputs(name, tokens=n)
+        t0 = time.perf_counter()
+        _, used = oracle.linear(x, wt, b, r, return_threads=True)
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds / 4 or n >= w["tokens"]:
+            break
+        n = min(w["tokens"], n * 4)
+    reps = 1
+    while time.perf_counter() - t0 < min_seconds and reps < 50:
+        oracle.linear(x, wt, b, r)
+        reps += 1
+    dt = time.perf_counter() - t0
+    nbytes, _ = linear_algorithmic(n, w["K"], w["N"], w["residual"])
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{name}, first {n} of {w['tokens']} tokens x{reps} ({dt:.1f} s wall, fp64, "
+                      f"{used} threads)"}
+
+
+def linear_bench(args, torch, np) -> int:
+    """One swin_linear_fwd per step over a whole linear workload."""
+    import shifted_window_attention_swin_amd as swa
+    import synth
+    w = synth.LINEAR_WORKLOADS[args.workload]
+    T, K, N, res = w["tokens"], w["K"], w["N"], w["residual"]
+    dev = torch.device("cuda:0")
+    x_np, w_np, b_np, r_np = synth.linear_inputs(args.workload)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    x0, wt, bias = bf(x_np), bf(w_np), torch.from_numpy(b_np).to(dev)
+    r0 = bf(r_np) if res else None
+    del x_np, r_np
+    packed = torch.empty_like(wt)
+    swa.check(swa.swin_linear_pack_weight(wt, packed, N, K), "pack")
+    nbytes, nflops = linear_algorithmic(T, K, N, res)
+    sets = 1 if args.hot else 2 * MALL_BYTES // nbytes + 1
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    rs = [r0] + [r0.clone() for _ in range(sets - 1)] if res else [None] * sets
+    ys = [torch.empty(T, N, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        k = i % sets
+        swa.check(swa.swin_linear_fwd(xs[k], packed, bias, rs[k], ys[k], T, K, N, stream), "linear")
+
+    K_ = args.steps
+    total_ms, avg_launch_s, isolated_s = time_steps(torch, step, K_, args.warmup, stream, 1)
+    value = nbytes * K_ / (total_ms / 1e3) / 1e9
+    achieved = nbytes / avg_launch_s / 1e9
+    result = {
+        "metric": f"linear layer GB/s ({w['desc']}, bf16); % HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K_, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, x ~ N(0,1), W and bias ~ N(0,0.02))",
+        "config": {"workload": args.workload, "desc": w["desc"], "tokens": T, "K": K, "N": N,
+                   "residual": res, "buffer_sets": sets, "cache": "hot" if args.hot else "cold"},
+        "tflops": round(nflops * K_ / (total_ms / 1e3) / 1e12, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, "linear_fwd"),
+                     "kernel": linear_kernel_name(K, N, res),
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "isolated_launch_us": round(isolated_s * 1e6, 3),
+                     "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
+                     "mfma_tflops": round(nflops / avg_launch_s / 1e12, 3),
+                     "mfma_peak_tflops": BF16_PEAK_TFLOPS},
+        "cpu_baseline": None if args.no_cpu_baseline else linear_cpu_baseline(args.workload),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -139,6 +282,8 @@ def main() -> int:
     import shifted_window_attention_swin_amd as swa
     import synth
 
+    if args.workload in synth.LINEAR_WORKLOADS:
+        return linear_bench(args, torch, np)
     w = synth.WORKLOADS[args.workload]
     if w["dtype"] != "bf16":
         print("bench.py: the benchmark times the bf16 path", file=sys.stderr)
@@ -165,36 +310,10 @@ def main() -> int:
         for s in shifts:
             swa.check(swa.swin_wattn_fwd(qs[k], table, outs[k], B, H, W, nh, d, M, s, stream), "fwd")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
     K = args.steps
-    # throughput: exactly K steps between two synchronisations
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(K):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms, avg_launch_s, isolated_s = time_steps(torch, step, K, args.warmup, stream, len(shifts))
     ms_per_step = total_ms / K
     value = nbytes * K / (total_ms / 1e3) / 1e9
-    # average launch duration: the HIP events around the timed region, on the
-    # stream the kernel is launched on, over its K * len(shifts) launches
-    # (back to back: this is what a kernel trace's mean duration agrees with)
-    avg_launch_s = total_ms / 1e3 / (K * len(shifts))
-    # for reference, launches timed one by one (each event pair adds its own
-    # overhead to the launch it brackets)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for i in range(K):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    isolated_s = sum(a.elapsed_time(b) for a, b in ev) / K / 1e3 / len(shifts)
-
     achieved = (nbytes / len(shifts)) / avg_launch_s / 1e9
     traffic = measured_traffic(args.workload)
     result = {

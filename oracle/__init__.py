@@ -169,7 +169,7 @@ def swin_wattn_windows(qkv, table, window: int, shift: int, sel, nthreads: int =
     return out, pos
 
 
-def linear(x, w, bias=None, residual=None, nthreads: int = 0):
+def linear(x, w, bias=None, residual=None, nthreads: int = 0, return_threads: bool = False):
     """``y = x @ w.T + bias (+ residual)`` in fp64.  ``x [..., K]``, ``w [N, K]``
     (uint16 = bfloat16 patterns, float32 or float64), ``bias [N]`` float32,
     ``residual [..., N]``.  Returns float64 ``[..., N]``."""
@@ -193,4 +193,4 @@ def linear(x, w, bias=None, residual=None, nthreads: int = 0):
     used = lib().oracle_linear(_ptr(xq), xc, T, K, _ptr(wq), wc, N, bp, rp, rc, nthreads, _ptr(y))
     if used < 0:
         raise ValueError("oracle rejected the arguments")
-    return y
+    return (y, used) if return_threads else y
