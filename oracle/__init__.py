@@ -51,6 +51,8 @@ def lib():
         L.oracle_swin_wattn_windows.restype = I
         L.oracle_linear.argtypes = [P, I, L64, I, P, I, I, P, P, I, I, P]
         L.oracle_linear.restype = I
+        L.oracle_layernorm.argtypes = [P, I, L64, I, P, P, ctypes.c_double, P]
+        L.oracle_layernorm.restype = I
         _lib = L
     return _lib
 
@@ -194,3 +196,19 @@ def linear(x, w, bias=None, residual=None, nthreads: int = 0, return_threads: bo
     if used < 0:
         raise ValueError("oracle rejected the arguments")
     return (y, used) if return_threads else y
+
+
+def layernorm(x, gamma, beta, eps: float = 1e-5):
+    """Layer normalisation over the last dimension in fp64.  ``x [..., C]``
+    (uint16 = bfloat16 patterns, float32 or float64); ``gamma, beta [C]``
+    float32.  Returns float64 ``[..., C]``."""
+    xq, xc = _qkv_arg(x)
+    C = xq.shape[-1]
+    T = int(np.prod(xq.shape[:-1])) if xq.ndim > 1 else 1
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    assert gamma.shape == (C,) and beta.shape == (C,)
+    y = np.empty(xq.shape, dtype=np.float64)
+    if lib().oracle_layernorm(_ptr(xq), xc, T, C, _ptr(gamma), _ptr(beta), eps, _ptr(y)) < 0:
+        raise ValueError("oracle rejected the arguments")
+    return y

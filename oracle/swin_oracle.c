@@ -377,3 +377,28 @@ int oracle_linear(const void* x, int xdtype, long T, int K, const void* w, int w
   free(jobs);
   return nthreads;
 }
+
+/* ---------------------------------------------------------------------- */
+/* layer normalisation: two passes over each row, mean then variance */
+
+int oracle_layernorm(const void* x, int xdtype, long T, int C, const float* gamma,
+                     const float* beta, double eps, double* y) {
+  if (T < 0 || C <= 0 || !gamma || !beta || eps < 0.0 || xdtype < ORACLE_F64 ||
+      xdtype > ORACLE_BF16)
+    return -1;
+  for (long t = 0; t < T; ++t) {
+    double mu = 0.0;
+    for (int c = 0; c < C; ++c) mu += load_elem(x, xdtype, t * C + c);
+    mu /= C;
+    double var = 0.0;
+    for (int c = 0; c < C; ++c) {
+      const double dv = load_elem(x, xdtype, t * C + c) - mu;
+      var += dv * dv;
+    }
+    var /= C;
+    const double r = 1.0 / sqrt(var + eps);
+    for (int c = 0; c < C; ++c)
+      y[t * C + c] = (load_elem(x, xdtype, t * C + c) - mu) * r * (double)gamma[c] + (double)beta[c];
+  }
+  return 0;
+}

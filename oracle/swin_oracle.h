@@ -109,6 +109,16 @@ int oracle_swin_wattn_windows(const void* qkv, int dtype, const float* table, in
 int oracle_linear(const void* x, int xdtype, long T, int K, const void* w, int wdtype, int N,
                   const float* bias, const void* residual, int rdtype, int nthreads, double* y);
 
+/* Layer normalisation over the last dimension, fp64:
+ *   mu[t] = mean_c x[t][c],  var[t] = mean_c (x[t][c] - mu[t])^2
+ *   y[t][c] = (x[t][c] - mu[t]) / sqrt(var[t] + eps) * gamma[c] + beta[c]
+ * x [T][C] of type xdtype; gamma, beta [C] fp32; y [T][C] fp64.  In a Swin
+ * block it precedes the window attention; the pages fuse it with the window
+ * shift and partition into one kernel (NVIDIA talk, section 3).
+ * Returns 0, or -1 on bad arguments. */
+int oracle_layernorm(const void* x, int xdtype, long T, int C, const float* gamma,
+                     const float* beta, double eps, double* y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -158,3 +158,35 @@ def linear_inputs(name: str, tokens: int | None = None):
     w = LINEAR_WORKLOADS[name]
     T = w["tokens"] if tokens is None else tokens
     return make_linear_inputs(T, w["K"], w["N"], w["seed"], w["residual"])
+
+
+# ---------------------------------------------------------------------------
+# Layer norm + QKV projection workloads: x with a nonzero mean and spread
+# (2 z + 0.5), gamma = 1 + 0.1 z, beta = 0.1 z, W and bias as above.
+
+LN_LINEAR_WORKLOADS = {
+    "lnqkv-t-s1": dict(tokens=32 * 56 * 56, K=96, N=288, seed=3001,
+                       desc="Swin-T stage 1 layer norm + QKV projection, B=32, 56x56, C=96"),
+    "lnqkv-t-s3": dict(tokens=64 * 14 * 14, K=384, N=1152, seed=3002,
+                       desc="Swin-T stage 3 layer norm + QKV projection, B=64, 14x14, C=384"),
+    "lnqkv-l-s1": dict(tokens=64 * 56 * 56, K=192, N=576, seed=3003,
+                       desc="Swin-L stage 1 layer norm + QKV projection, B=64, 56x56, C=192"),
+}
+
+
+def make_ln_linear_inputs(T: int, K: int, N: int, seed: int):
+    """Returns ``(x, gamma, beta, w, bias)``: ``x [T, K]`` and ``w [N, K]`` as
+    bfloat16 patterns, ``gamma, beta [K]`` and ``bias [N]`` float32."""
+    x = bf16_bits(normal(stream_key(seed, 0), T * K, 2.0) + np.float32(0.5)).reshape(T, K)
+    gamma = normal(stream_key(seed, 1), K, 0.1) + np.float32(1.0)
+    beta = normal(stream_key(seed, 2), K, 0.1)
+    w = bf16_bits(normal(stream_key(seed, 3), N * K, 0.02)).reshape(N, K)
+    bias = normal(stream_key(seed, 4), N, 0.02)
+    return x, gamma, beta, w, bias
+
+
+def ln_linear_inputs(name: str, tokens: int | None = None):
+    """Inputs of a named layer norm + linear workload (optionally its first tokens)."""
+    w = LN_LINEAR_WORKLOADS[name]
+    T = w["tokens"] if tokens is None else tokens
+    return make_ln_linear_inputs(T, w["K"], w["N"], w["seed"])

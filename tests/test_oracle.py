@@ -404,3 +404,52 @@ def test_qkv_columns_are_the_attention_layout(oracle_lib):
             rows = slice((i * nh + h) * d, (i * nh + h + 1) * d)
             ref = x @ w[rows].T + b[rows].astype(np.float64)
             assert np.allclose(qkv[:, :, :, i, h, :], ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- layer norm
+
+def test_layernorm_golden(oracle_lib):
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    y1 = oracle.layernorm(x[None], np.ones(4, np.float32), np.zeros(4, np.float32), eps=0.0)
+    y2 = oracle.layernorm(x[None], np.array([2, 1, 1, 1], np.float32),
+                          np.array([0, 0, 0, 1], np.float32), eps=0.0)
+    g = _golden("layernorm_c4.txt")
+    assert np.allclose(y1[0], g[0], rtol=0, atol=1e-14)
+    assert np.allclose(y2[0], g[1], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("T,C,eps", [(1, 1, 1e-5), (9, 96, 1e-5), (33, 192, 1e-6), (5, 384, 1e-3)])
+def test_layernorm_matches_torch_float64(oracle_lib, T, C, eps):
+    """Special case reducing to a library routine: torch's layer_norm in float64."""
+    rng = _rng(T + C)
+    x = rng.standard_normal((T, C)) * 3 + 1.5
+    g, b = rng.standard_normal(C).astype(np.float32), rng.standard_normal(C).astype(np.float32)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (C,), torch.from_numpy(g.astype(np.float64)),
+                                         torch.from_numpy(b.astype(np.float64)), eps).numpy()
+    assert np.allclose(oracle.layernorm(x, g, b, eps), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layernorm_closed_forms(oracle_lib):
+    rng = _rng(12)
+    C = 64
+    ones, zeros = np.ones(C, np.float32), np.zeros(C, np.float32)
+    b = rng.standard_normal(C).astype(np.float32)
+    # a constant row has zero variance: the output is beta
+    assert np.array_equal(oracle.layernorm(np.full((3, C), 7.25), ones, b, eps=1e-5),
+                          np.broadcast_to(b.astype(np.float64), (3, C)))
+    # unit scale, zero shift: each row has mean 0 and variance var / (var + eps)
+    x = rng.standard_normal((6, C)) * 2 + 5
+    y = oracle.layernorm(x, ones, zeros, eps=0.5)
+    var = x.var(axis=1)
+    assert np.allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    assert np.allclose(y.var(axis=1), var / (var + 0.5), rtol=1e-12)
+    # without eps the result is invariant under x -> a x + c, a > 0
+    assert np.allclose(oracle.layernorm(3 * x - 11, ones, b, eps=0.0),
+                       oracle.layernorm(x, ones, b, eps=0.0), rtol=1e-12, atol=1e-12)
+
+
+def test_layernorm_bf16_read_exactly(oracle_lib):
+    rng = _rng(13)
+    xb = synth.bf16_bits(rng.standard_normal((5, 96)).astype(np.float32))
+    g, b = rng.standard_normal(96).astype(np.float32), rng.standard_normal(96).astype(np.float32)
+    assert np.array_equal(oracle.layernorm(xb, g, b), oracle.layernorm(synth.bf16_to_f32(xb).astype(np.float64), g, b))

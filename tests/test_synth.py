@@ -49,3 +49,12 @@ def test_linear_inputs_prefix_and_shapes():
         assert (r is None) == (not w["residual"])
         if r is not None:
             assert r.shape == (5, w["N"]) and np.array_equal(r, r2[:5])
+
+
+def test_ln_linear_inputs_prefix_and_shapes():
+    for name, w in synth.LN_LINEAR_WORKLOADS.items():
+        x, g, b, wt, bias = synth.ln_linear_inputs(name, tokens=4)
+        x2, g2, _, wt2, _ = synth.ln_linear_inputs(name, tokens=7)
+        assert x.shape == (4, w["K"]) and g.shape == (w["K"],) and wt.shape == (w["N"], w["K"])
+        assert g.dtype == np.float32 and bias.shape == (w["N"],)
+        assert np.array_equal(x, x2[:4]) and np.array_equal(g, g2) and np.array_equal(wt, wt2)
