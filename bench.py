@@ -9,7 +9,8 @@ the working set of the timed region exceeds twice the 256 MB Infinity Cache
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 With --workload naming a linear-layer workload (qkv-l-s1, proj-l-s1, ...) a
-step is one swin_linear_fwd over its tokens instead.
+step is one swin_linear_fwd over its tokens instead, and with a layer norm +
+QKV workload (lnqkv-l-s1, ...) one swin_ln_linear_fwd.
 """
 from __future__ import annotations
 
@@ -145,16 +146,27 @@ def time_steps(torch, step, K: int, warmup: int, stream, launches_per_step: int)
 
 def linear_algorithmic(T, K, N, residual, elem=2):
     """Bytes: x read once, y written once, the residual read once.  FLOPs:
-    one multiply-add per (token, input, output)."""
+    one multiply-add per (token, input, output); a fused layer norm adds no
+    bytes and is not counted as FLOPs."""
     return (T * K + T * N * (2 if residual else 1)) * elem, 2 * T * K * N
 
 
-def linear_kernel_name(K: int, N: int, residual: bool) -> str:
-    """The linear kernel the library launches (mirrors its dispatch: 6, 4 or
-    2 waves, the widest that divides N / 32)."""
+def linear_kernel_name(K: int, N: int, residual: bool, layernorm: bool = False) -> str:
+    """The linear kernel the library launches (mirrors its dispatch: mode 0
+    plain, 1 residual, 2 layer norm; 6, 4 or 2 waves, the widest that
+    divides N / 32)."""
     ncb = N // 32
     waves = 6 if ncb % 6 == 0 else 4 if ncb % 4 == 0 else 2
-    return f"linear_fwd_kernel<{K // 32}, {str(residual).lower()}, {waves}>"
+    mode = 2 if layernorm else 1 if residual else 0
+    return f"linear_fwd_kernel<{K // 32}, {mode}, {waves}>"
+
+
+def _linear_workload(name: str):
+    """(spec, layer norm?) of a linear or layer norm + linear workload."""
+    import synth
+    if name in synth.LN_LINEAR_WORKLOADS:
+        return dict(synth.LN_LINEAR_WORKLOADS[name], residual=False), True
+    return synth.LINEAR_WORKLOADS[name], False
 
 
 def linear_cpu_baseline(name: str, min_seconds: float = 10.0):
@@ -162,19 +174,27 @@ def linear_cpu_baseline(name: str, min_seconds: float = 10.0):
     call takes about `min_seconds`), reported in GB/s of algorithmic bytes."""
     import oracle
     import synth
-    w = synth.LINEAR_WORKLOADS[name]
+    w, ln = _linear_workload(name)
+
+    def run(n):
+        if ln:
+            x, g, be, wt, b = synth.ln_linear_inputs(name, tokens=n)
+            return lambda: oracle.linear(oracle.layernorm(x, g, be), wt, b, return_threads=True)
+        x, wt, b, r = synth.linear_inputs(name, tokens=n)
+        return lambda: oracle.linear(x, wt, b, r, return_threads=True)
+
     n = 512
     while True:
-        x, wt, b, r = synth.linear_inputs(name, tokens=n)
+        call = run(n)
         t0 = time.perf_counter()
-        _, used = oracle.linear(x, wt, b, r, return_threads=True)
+        _, used = call()
         dt = time.perf_counter() - t0
         if dt >= min_seconds / 4 or n >= w["tokens"]:
             break
         n = min(w["tokens"], n * 4)
     reps = 1
     while time.perf_counter() - t0 < min_seconds and reps < 50:
-        oracle.linear(x, wt, b, r)
+        call()
         reps += 1
     dt = time.perf_counter() - t0
     nbytes, _ = linear_algorithmic(n, w["K"], w["N"], w["residual"])
@@ -188,16 +208,25 @@ def linear_bench(args, torch, np) -> int:
     """One swin_linear_fwd per step over a whole linear workload."""
     import shifted_window_attention_swin_amd as swa
     import synth
-    w = synth.LINEAR_WORKLOADS[args.workload]
+    w, ln = _linear_workload(args.workload)
     T, K, N, res = w["tokens"], w["K"], w["N"], w["residual"]
     dev = torch.device("cuda:0")
-    x_np, w_np, b_np, r_np = synth.linear_inputs(args.workload)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    if ln:
+        x_np, g_np, be_np, w_np, b_np = synth.ln_linear_inputs(args.workload)
+        gamma, beta = torch.from_numpy(g_np).to(dev), torch.from_numpy(be_np).to(dev)
+        r_np = None
+    else:
+        x_np, w_np, b_np, r_np = synth.linear_inputs(args.workload)
     x0, wt, bias = bf(x_np), bf(w_np), torch.from_numpy(b_np).to(dev)
     r0 = bf(r_np) if res else None
     del x_np, r_np
     packed = torch.empty_like(wt)
-    swa.check(swa.swin_linear_pack_weight(wt, packed, N, K), "pack")
+    if ln:
+        consts = torch.empty(2, N, dtype=torch.float32, device=dev)
+        swa.check(swa.swin_ln_linear_pack_weight(wt, gamma, beta, bias, packed, consts, N, K), "pack")
+    else:
+        swa.check(swa.swin_linear_pack_weight(wt, packed, N, K), "pack")
     nbytes, nflops = linear_algorithmic(T, K, N, res)
     sets = 1 if args.hot else 2 * MALL_BYTES // nbytes + 1
     xs = [x0] + [x0.clone() for _ in range(sets - 1)]
@@ -207,14 +236,18 @@ def linear_bench(args, torch, np) -> int:
 
     def step(i):
         k = i % sets
-        swa.check(swa.swin_linear_fwd(xs[k], packed, bias, rs[k], ys[k], T, K, N, stream), "linear")
+        if ln:
+            swa.check(swa.swin_ln_linear_fwd(xs[k], packed, consts, 1e-5, ys[k], T, K, N, stream),
+                      "ln_linear")
+        else:
+            swa.check(swa.swin_linear_fwd(xs[k], packed, bias, rs[k], ys[k], T, K, N, stream), "linear")
 
     K_ = args.steps
     total_ms, avg_launch_s, isolated_s = time_steps(torch, step, K_, args.warmup, stream, 1)
     value = nbytes * K_ / (total_ms / 1e3) / 1e9
     achieved = nbytes / avg_launch_s / 1e9
     result = {
-        "metric": f"linear layer GB/s ({w['desc']}, bf16); % HBM peak",
+        "metric": f"{'layer norm + ' if ln else ''}linear layer GB/s ({w['desc']}, bf16); % HBM peak",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -225,15 +258,18 @@ def linear_bench(args, torch, np) -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded SplitMix64/Box-Muller, x ~ N(0,1), W and bias ~ N(0,0.02))",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, " + ("x ~ N(0.5,2), gamma ~ N(1,0.1), "
+                                                                "beta ~ N(0,0.1)" if ln else "x ~ N(0,1)")
+                + ", W and bias ~ N(0,0.02))",
         "config": {"workload": args.workload, "desc": w["desc"], "tokens": T, "K": K, "N": N,
-                   "residual": res, "buffer_sets": sets, "cache": "hot" if args.hot else "cold"},
+                   "residual": res, "layernorm": ln, "buffer_sets": sets,
+                   "cache": "hot" if args.hot else "cold"},
         "tflops": round(nflops * K_ / (total_ms / 1e3) / 1e12, 3),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload, "linear_fwd"),
-                     "kernel": linear_kernel_name(K, N, res),
+                     "kernel": linear_kernel_name(K, N, res, ln),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "isolated_launch_us": round(isolated_s * 1e6, 3),
                      "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
@@ -282,7 +318,7 @@ def main() -> int:
     import shifted_window_attention_swin_amd as swa
     import synth
 
-    if args.workload in synth.LINEAR_WORKLOADS:
+    if args.workload in synth.LINEAR_WORKLOADS or args.workload in synth.LN_LINEAR_WORKLOADS:
         return linear_bench(args, torch, np)
     w = synth.WORKLOADS[args.workload]
     if w["dtype"] != "bf16":

@@ -122,6 +122,32 @@ int swin_linear_pack_weight(const void* weight, void* packed, int N, int K, void
 int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
                     const void* residual, void* y, long long T, int K, int N, void* stream);
 
+/* Layer normalisation fused into the QKV projection:
+ *   xn[t][c] = (x[t][c] - mean_t) / sqrt(var_t + eps) * gamma[c] + beta[c]
+ *   y = xn W^T + bias
+ * (mean and biased variance of each token row over its K channels, in
+ * float32).  The NVIDIA talk, section 3, fuses the layer norm with the
+ * window shift and partition that follow it, and prepares the QKV weight
+ * and bias in advance; here the shift and partition are part of
+ * swin_wattn_fwd's loads, and the layer norm folds into the weight:
+ *   y_j = (sum_c x_c W'_jc - mean_t s_j) / sigma_t + b'_j,
+ *   W' = gamma o W (bf16), s_j = sum_c W'_jc, b'_j = bias_j + sum_c beta_c W_jc,
+ * so one pass reads raw x and writes the qkv the attention reads.
+ *
+ * swin_ln_linear_pack_weight: W [N][K] bf16 (16-byte aligned), gamma and
+ * beta [K] float32, bias [N] float32 or NULL -> packed (N*K bf16, caller-
+ * owned, 16-byte aligned, must not overlap W) and consts [2][N] float32
+ * (s, then b'; caller-owned, 16-byte aligned, overlapping no input).  Once
+ * per weight; queued on `stream`.
+ * swin_ln_linear_fwd: x [T][K] bf16 raw (not normalised); packed and consts
+ * from swin_ln_linear_pack_weight; eps >= 0.  Other arguments, layouts and
+ * errors as swin_linear_fwd (no residual). */
+int swin_ln_linear_pack_weight(const void* weight, const float* gamma, const float* beta,
+                               const float* bias, void* packed, float* consts, int N, int K,
+                               void* stream);
+int swin_ln_linear_fwd(const void* x, const void* packed_weight, const float* consts, float eps,
+                       void* y, long long T, int K, int N, void* stream);
+
 /* Copies of the precomputed tensors into caller-owned device memory, queued
  * on `stream` (for verification).  SWIN_ERR_NOT_PREPARED without a prior
  * swin_wattn_precompute for the key.

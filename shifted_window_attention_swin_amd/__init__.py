@@ -30,7 +30,8 @@ SWIN_ERR_HIP = -4
 
 EXPORTS = ("swin_wattn_precompute", "swin_wattn_fwd", "swin_wattn_fwd_f32",
            "swin_wattn_copy_index", "swin_wattn_copy_mask", "swin_wattn_copy_region",
-           "swin_linear_pack_weight", "swin_linear_fwd",
+           "swin_linear_pack_weight", "swin_linear_fwd", "swin_ln_linear_pack_weight",
+           "swin_ln_linear_fwd",
            "swin_wattn_release", "swin_wattn_status_string")
 
 
@@ -54,6 +55,8 @@ for _n in ("swin_wattn_copy_index", "swin_wattn_copy_mask", "swin_wattn_copy_reg
     getattr(_lib, _n).argtypes = [_I, _I, _I, _I, _P, _P]
 _lib.swin_linear_pack_weight.argtypes = [_P, _P, _I, _I, _P]
 _lib.swin_linear_fwd.argtypes = [_P, _P, _P, _P, _P, ctypes.c_longlong, _I, _I, _P]
+_lib.swin_ln_linear_pack_weight.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _P]
+_lib.swin_ln_linear_fwd.argtypes = [_P, _P, _P, ctypes.c_float, _P, ctypes.c_longlong, _I, _I, _P]
 _lib.swin_wattn_release.argtypes = []
 _lib.swin_wattn_status_string.argtypes = [_I]
 _lib.swin_wattn_status_string.restype = ctypes.c_char_p
@@ -115,6 +118,18 @@ def swin_linear_fwd(x, packed_weight, bias, residual, y, T: int, K: int, N: int,
                     stream=None) -> int:
     return _lib.swin_linear_fwd(_addr(x), _addr(packed_weight), _addr(bias), _addr(residual),
                                 _addr(y), T, K, N, _stream(stream))
+
+
+def swin_ln_linear_pack_weight(weight, gamma, beta, bias, packed, consts, N: int, K: int,
+                               stream=None) -> int:
+    return _lib.swin_ln_linear_pack_weight(_addr(weight), _addr(gamma), _addr(beta), _addr(bias),
+                                           _addr(packed), _addr(consts), N, K, _stream(stream))
+
+
+def swin_ln_linear_fwd(x, packed_weight, consts, eps: float, y, T: int, K: int, N: int,
+                       stream=None) -> int:
+    return _lib.swin_ln_linear_fwd(_addr(x), _addr(packed_weight), _addr(consts), eps, _addr(y),
+                                   T, K, N, _stream(stream))
 
 
 def swin_wattn_release() -> int:

@@ -49,10 +49,31 @@ constexpr int kLinTiles = kLinRows / 16;
 // bytes per token of the fp32 output tile of a WAVES-wave workgroup (padded)
 constexpr int lin_out_stride(int waves) { return waves * 32 * 4 + 16; }
 
+// epilogue / prologue of the linear kernel
+enum LinMode { kLinPlain = 0, kLinResidual = 1, kLinLayerNorm = 2 };
+
+// sum over aligned groups of L = 4 or 8 lanes (DPP: lane ^ 1, lane ^ 2
+// within quads, then the mirror of each half row pairs the two quads)
+template <int L>
+SWA_INLINE float group_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  if constexpr (L == 8)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+  return v;
+}
+
+// LDS of the layer norm, after the x and output tiles: (mean, 1/sigma) of
+// the row block's tokens
+constexpr size_t lin_ln_lds_bytes() { return kLinRows * 8; }
+
 // WAVES waves per workgroup, one 32-column block each: the workgroup's
-// WAVES * 32 channels are WAVES / 2 whole 128-byte lines of every token
-template <int KS, bool RES, int WAVES>
+// WAVES * 32 channels are WAVES / 2 whole 128-byte lines of every token.
+// MODE kLinResidual adds a residual; kLinLayerNorm normalises every token
+// row of x (over its K channels) before the product.
+template <int KS, int MODE, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) {
+  constexpr bool RES = MODE == kLinResidual, LN = MODE == kLinLayerNorm;
   constexpr int kLinWaves = WAVES;
   constexpr int kLinCols = 32 * WAVES;
   constexpr int kOutStride = lin_out_stride(WAVES);
@@ -62,6 +83,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   extern __shared__ char s_lds[];
   char* s_x = s_lds;              // NB blocks of 1 KB: the row block of x
   char* s_o = s_lds + NB * 1024;  // kLinRows x kOutStride: the fp32 output tile
+  float2* s_stat = reinterpret_cast<float2*>(s_o + kLinRows * kOutStride);  // layer norm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,7 +141,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
       a[ks][1] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2 + 1) * 1024);
     }
   }
-  f32x4 bias[2][2];
+  f32x4 bias[2][2], csum[LN ? 2 : 1][2];  // layer norm: row sums of the packed weight
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     bias[j][0] = bias[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -127,7 +149,56 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
       bias[j][0] = *reinterpret_cast<const f32x4*>(p.bias + sch[j]);
       bias[j][1] = *reinterpret_cast<const f32x4*>(p.bias + sch[j] + 4);
     }
+    if constexpr (LN) {
+      csum[j][0] = csum[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s_active[j]) {
+        csum[j][0] = *reinterpret_cast<const f32x4*>(p.colsum + sch[j]);
+        csum[j][1] = *reinterpret_cast<const f32x4*>(p.colsum + sch[j] + 4);
+      }
+    }
   }
+
+  // Layer norm, folded into the weights: with z the unit-normalised row,
+  //   y_j = sum_c (z_c gamma_c + beta_c) W_jc + b_j
+  //       = (sum_c x_c W'_jc - mean s_j) / sigma + b'_j,
+  // W' = gamma o W (the packed weight), s_j = sum_c W'_jc, b' = b + W beta
+  // (prepared once with the packing).  The products run on the raw row
+  // block; the mean and 1/sigma of every token are only needed by the
+  // epilogue, so they are computed from LDS while the products are in
+  // flight: LL lanes per token, CPL 16-byte chunks of its row per lane
+  // (chunk q = ql + LL k: k-step q / 4, part q % 4), DPP sums over the group
+  // (mean first, then the biased variance about it).
+  constexpr int LL = KS % 2 == 0 ? 8 : 4;                 // lanes per token
+  constexpr int CPL = KS * 4 / LL;                        // chunks per lane
+  constexpr int TPW_LN = 64 / LL;                         // tokens per wave and pass
+  const int ql = lane % LL;
+  auto ln_stats = [&]() {
+    for (int t0 = wv * TPW_LN; t0 < kLinRows; t0 += kLinWaves * TPW_LN) {  // wave-uniform
+      const int t = t0 + lane / LL;
+      const char* row = s_x + (t >> 4) * KS * 1024 + (t & 15) * 64;
+      float v[CPL][8];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const int q = ql + LL * k;
+        const bf16x8 h = *reinterpret_cast<const bf16x8*>(row + (q >> 2) * 1024 + (q & 3) * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[k][e] = (float)h[e];
+      }
+      float s1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s1 += v[k][e];
+      const float mu = group_sum<LL>(s1) * (1.f / (KS * 32));
+      float s2 = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2 += (v[k][e] - mu) * (v[k][e] - mu);
+      const float rs = rsqrtf(group_sum<LL>(s2) * (1.f / (KS * 32)) + p.eps);
+      if (ql == 0) s_stat[t] = make_float2(mu, rs);
+    }
+  };
 
   // register-staged loads of row block rr: LDS block bi = tile * KS + k-step;
   // rows past the end load the last row (finite stand-in data, not stored)
@@ -188,6 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
           acc[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][1], b, acc[tt][1], 0, 0, 0);
         }
       }
+      if constexpr (LN) ln_stats();  // overlaps the products in flight
       // lane (g, c) holds channels 8g + 4i + q of the wave's block for
       // token c of each tile: 8 consecutive floats of the output tile
 #pragma unroll
@@ -196,6 +268,8 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
         *reinterpret_cast<f32x4*>(o) = acc[tt][0];
         *reinterpret_cast<f32x4*>(o + 16) = acc[tt][1];
       }
+    } else if constexpr (LN) {
+      ln_stats();
     }
     __syncthreads();  // output tile complete
 #pragma unroll
@@ -208,7 +282,15 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
         bf16x8 out;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float y0 = v0[q] + bias[j][0][q], y1 = v1[q] + bias[j][1][q];
+          float y0, y1;
+          if constexpr (LN) {
+            const float2 st = s_stat[srow[j]];  // (mean, 1/sigma) of the token
+            y0 = (v0[q] - st.x * csum[j][0][q]) * st.y + bias[j][0][q];
+            y1 = (v1[q] - st.x * csum[j][1][q]) * st.y + bias[j][1][q];
+          } else {
+            y0 = v0[q] + bias[j][0][q];
+            y1 = v1[q] + bias[j][1][q];
+          }
           if constexpr (RES) {
             y0 += (float)res[j][q];
             y1 += (float)res[j][4 + q];
@@ -224,7 +306,9 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
 }
 
 // packed[cb][ks][i][lane][s] = W[cb*32 + out_channel(i, lane % 16)][ks*32 + 8*(lane/16) + s]
-__global__ void linear_pack_kernel(const uint16_t* w, uint16_t* wp, int N, int K) {
+// (times gamma[column], rounded to bf16, when gamma is given)
+__global__ void linear_pack_kernel(const uint16_t* w, const float* gamma, uint16_t* wp, int N,
+                                   int K) {
   const int KS = K / 32;
   const long long total = (long long)(N / 32) * KS * 2 * 64;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
@@ -236,8 +320,33 @@ __global__ void linear_pack_kernel(const uint16_t* w, uint16_t* wp, int N, int K
     const int ks = (int)(cks % KS), cb = (int)(cks / KS);
     const int row = cb * 32 + out_channel(i, lane % 16);
     const int col = ks * 32 + 8 * (lane / 16);
-    *reinterpret_cast<u32x4*>(wp + e * 8) =
-        *reinterpret_cast<const u32x4*>(w + (size_t)row * K + col);
+    const u32x4 src = *reinterpret_cast<const u32x4*>(w + (size_t)row * K + col);
+    if (gamma) {
+      const bf16x8 h = __builtin_bit_cast(bf16x8, src);
+      bf16x8 o;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) o[s] = (__bf16)((float)h[s] * gamma[col + s]);
+      *reinterpret_cast<bf16x8*>(wp + e * 8) = o;
+    } else {
+      *reinterpret_cast<u32x4*>(wp + e * 8) = src;
+    }
+  }
+}
+
+// layer norm constants of output j: consts[j] = sum_c bf16(gamma_c W_jc)
+// (the row sums of the packed weight, rounded as the packing rounds), and
+// consts[N + j] = bias_j + sum_c beta_c W_jc; sums in fp64
+__global__ void linear_ln_consts_kernel(const uint16_t* w, const float* gamma, const float* beta,
+                                        const float* bias, float* consts, int N, int K) {
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < N; j += gridDim.x * blockDim.x) {
+    double s = 0.0, b = bias ? (double)bias[j] : 0.0;
+    for (int c = 0; c < K; ++c) {
+      const float wv = __builtin_bit_cast(float, (unsigned)w[(size_t)j * K + c] << 16);
+      s += (double)(float)(__bf16)(wv * gamma[c]);
+      b += (double)beta[c] * (double)wv;
+    }
+    consts[j] = (float)s;
+    consts[N + j] = (float)b;
   }
 }
 
@@ -246,10 +355,11 @@ __global__ void linear_pack_kernel(const uint16_t* w, uint16_t* wp, int N, int K
 int linear_waves(int ncb) { return ncb % 6 == 0 ? 6 : ncb % 4 == 0 ? 4 : 2; }
 
 size_t linear_lds_waves(int K, int waves) {
-  return (size_t)kLinTiles * (K / 32) * 1024 + (size_t)kLinRows * lin_out_stride(waves);
+  return (size_t)kLinTiles * (K / 32) * 1024 + (size_t)kLinRows * lin_out_stride(waves) +
+         lin_ln_lds_bytes();
 }
 
-template <int KS, bool RES, int WAVES>
+template <int KS, int MODE, int WAVES>
 int linear_blocks_per_cu(int dev) {
   static std::atomic<int> cache[kMaxDevices];
   const bool cacheable = dev >= 0 && dev < kMaxDevices;
@@ -258,7 +368,7 @@ int linear_blocks_per_cu(int dev) {
     if (v > 0) return v;
   }
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, linear_fwd_kernel<KS, RES, WAVES>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, linear_fwd_kernel<KS, MODE, WAVES>,
                                                    WAVES * 64, linear_lds_waves(KS * 32, WAVES)) !=
           hipSuccess ||
       per_cu < 1)
@@ -267,47 +377,57 @@ int linear_blocks_per_cu(int dev) {
   return per_cu;
 }
 
-template <int KS, bool RES, int WAVES>
+template <int KS, int MODE, int WAVES>
 hipError_t launch_linear_krw(LinearParams p, int dev, int cus, hipStream_t st) {
   p.ncg = (p.ncb + WAVES - 1) / WAVES;
   // a multiple of the column groups (each workgroup keeps one), and of
   // 8 x that when large enough (even XCD shares); never more than the units
   const long long units = (long long)p.blocks * p.ncg;
-  long long grid = (long long)cus * linear_blocks_per_cu<KS, RES, WAVES>(dev);
+  long long grid = (long long)cus * linear_blocks_per_cu<KS, MODE, WAVES>(dev);
   if (grid > units) grid = units;
   if (grid >= 8LL * p.ncg) grid -= grid % (8LL * p.ncg);
   else grid -= grid % p.ncg;
-  hipLaunchKernelGGL((linear_fwd_kernel<KS, RES, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64),
+  hipLaunchKernelGGL((linear_fwd_kernel<KS, MODE, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64),
                      linear_lds_waves(KS * 32, WAVES), st, p);
   return hipGetLastError();
 }
 
-template <int KS, bool RES>
+template <int KS, int MODE>
 hipError_t launch_linear_kr(const LinearParams& p, int dev, int cus, hipStream_t st) {
   switch (linear_waves(p.ncb)) {
-    case 6: return launch_linear_krw<KS, RES, 6>(p, dev, cus, st);
-    case 4: return launch_linear_krw<KS, RES, 4>(p, dev, cus, st);
-    default: return launch_linear_krw<KS, RES, 2>(p, dev, cus, st);
+    case 6: return launch_linear_krw<KS, MODE, 6>(p, dev, cus, st);
+    case 4: return launch_linear_krw<KS, MODE, 4>(p, dev, cus, st);
+    default: return launch_linear_krw<KS, MODE, 2>(p, dev, cus, st);
   }
 }
 
 template <int KS>
 hipError_t launch_linear_ks(const LinearParams& p, int dev, int cus, hipStream_t st) {
-  return p.res ? launch_linear_kr<KS, true>(p, dev, cus, st)
-               : launch_linear_kr<KS, false>(p, dev, cus, st);
+  if (p.colsum) return launch_linear_kr<KS, kLinLayerNorm>(p, dev, cus, st);
+  return p.res ? launch_linear_kr<KS, kLinResidual>(p, dev, cus, st)
+               : launch_linear_kr<KS, kLinPlain>(p, dev, cus, st);
 }
 
 }  // namespace
 
 size_t linear_lds_bytes(int K, int N) { return linear_lds_waves(K, linear_waves(N / 32)); }
 
-hipError_t launch_linear_pack(const void* w, void* wp, int N, int K, hipStream_t stream) {
+hipError_t launch_linear_ln_consts(const void* w, const float* gamma, const float* beta,
+                                  const float* bias, float* consts, int N, int K,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(linear_ln_consts_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(w), gamma, beta, bias, consts, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_pack(const void* w, const float* gamma, void* wp, int N, int K,
+                              hipStream_t stream) {
   const long long total = (long long)(N / 32) * (K / 32) * 2 * 64;
   long long blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(linear_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(w), static_cast<uint16_t*>(wp), N, K);
+                     static_cast<const uint16_t*>(w), gamma, static_cast<uint16_t*>(wp), N, K);
   return hipGetLastError();
 }
 

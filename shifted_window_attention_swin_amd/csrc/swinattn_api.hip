@@ -237,22 +237,49 @@ int swin_linear_pack_weight(const void* weight, void* packed, int N, int K, void
   if (K > kMaxLinearK) return SWIN_ERR_UNSUPPORTED;
   const size_t bytes = (size_t)N * K * 2;
   if (overlap(weight, bytes, packed, bytes)) return SWIN_ERR_INVALID_ARG;
-  return launch_linear_pack(weight, packed, N, K, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_linear_pack(weight, nullptr, packed, N, K, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
              ? SWIN_OK
              : SWIN_ERR_HIP;
 }
 
-int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
-                    const void* residual, void* y, long long T, int K, int N, void* stream) {
+int swin_ln_linear_pack_weight(const void* weight, const float* gamma, const float* beta,
+                               const float* bias, void* packed, float* consts, int N, int K,
+                               void* stream) {
+  if (!weight || !gamma || !beta || !packed || !consts) return SWIN_ERR_INVALID_ARG;
+  if (!aligned(weight, 16) || !aligned(packed, 16) || !aligned(consts, 16) || !aligned(gamma, 4) ||
+      !aligned(beta, 4) || (bias && !aligned(bias, 4)))
+    return SWIN_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return SWIN_ERR_INVALID_ARG;
+  if (K > kMaxLinearK) return SWIN_ERR_UNSUPPORTED;
+  const size_t wb = (size_t)N * K * 2, cb = (size_t)N * 8;
+  if (overlap(weight, wb, packed, wb) || overlap(consts, cb, packed, wb) ||
+      overlap(consts, cb, weight, wb) || overlap(consts, cb, gamma, (size_t)K * 4) ||
+      overlap(consts, cb, beta, (size_t)K * 4) || (bias && overlap(consts, cb, bias, (size_t)N * 4)))
+    return SWIN_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (launch_linear_pack(weight, gamma, packed, N, K, st) != hipSuccess) return SWIN_ERR_HIP;
+  return launch_linear_ln_consts(weight, gamma, beta, bias, consts, N, K, st) == hipSuccess
+             ? SWIN_OK
+             : SWIN_ERR_HIP;
+}
+
+namespace {
+
+int linear_common(const void* x, const float* colsum, float eps, const void* packed_weight,
+                  const float* bias, const void* residual, void* y, long long T, int K, int N,
+                  void* stream) {
   if (!x || !packed_weight || !y) return SWIN_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(packed_weight, 16) || !aligned(y, 16) ||
       (bias && !aligned(bias, 16)) || (residual && !aligned(residual, 16)))
     return SWIN_ERR_INVALID_ARG;
+  if (colsum && (!aligned(colsum, 16) || !(eps >= 0.f))) return SWIN_ERR_INVALID_ARG;
   if (T < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return SWIN_ERR_INVALID_ARG;
   if (K > kMaxLinearK) return SWIN_ERR_UNSUPPORTED;
   const size_t xb = (size_t)T * K * 2, yb = (size_t)T * N * 2, wb = (size_t)N * K * 2;
   if (overlap(y, yb, x, xb) || overlap(y, yb, packed_weight, wb) ||
-      (bias && overlap(y, yb, bias, (size_t)N * 4)))
+      (bias && overlap(y, yb, bias, (size_t)N * 4)) ||
+      (colsum && overlap(y, yb, colsum, (size_t)N * 4)))
     return SWIN_ERR_INVALID_ARG;
   // the residual may be y itself (in-place residual add), or lie apart from it
   if (residual && residual != y && overlap(y, yb, residual, yb)) return SWIN_ERR_INVALID_ARG;
@@ -263,6 +290,8 @@ int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
   LinearParams p;
   p.wp = packed_weight;
   p.bias = bias;
+  p.colsum = colsum;
+  p.eps = eps;
   p.K = K;
   p.N = N;
   p.ncb = N / 32;
@@ -277,6 +306,19 @@ int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
       return SWIN_ERR_HIP;
   }
   return SWIN_OK;
+}
+
+}  // namespace
+
+int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
+                    const void* residual, void* y, long long T, int K, int N, void* stream) {
+  return linear_common(x, nullptr, 0.f, packed_weight, bias, residual, y, T, K, N, stream);
+}
+
+int swin_ln_linear_fwd(const void* x, const void* packed_weight, const float* consts, float eps,
+                       void* y, long long T, int K, int N, void* stream) {
+  if (!consts || !aligned(consts, 16)) return SWIN_ERR_INVALID_ARG;
+  return linear_common(x, consts, eps, packed_weight, consts + N, nullptr, y, T, K, N, stream);
 }
 
 int swin_wattn_copy_index(int H, int W, int window, int shift, int32_t* dst, void* stream) {

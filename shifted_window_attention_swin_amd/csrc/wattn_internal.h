@@ -61,6 +61,8 @@ struct LinearParams {
   const void* wp;     // packed weight [N/32][K/32][2][64][8] bf16
   const float* bias;  // [N] or null
   const void* res;    // [T][N] bf16 or null
+  const float* colsum;  // layer norm: [N] row sums of the packed weight, or null
+  float eps;            // layer norm epsilon
   void* y;            // [T][N] bf16
   long long T;
   int K, N;
@@ -69,7 +71,13 @@ struct LinearParams {
   int blocks;  // row blocks (set by launch_linear)
 };
 size_t linear_lds_bytes(int K, int N);
-hipError_t launch_linear_pack(const void* w, void* wp, int N, int K, hipStream_t stream);
+// gamma null: plain packing; else the packed weight is gamma o W.
+hipError_t launch_linear_pack(const void* w, const float* gamma, void* wp, int N, int K,
+                              hipStream_t stream);
+// consts [2][N]: row sums of gamma o W (as packed), bias + W beta.
+hipError_t launch_linear_ln_consts(const void* w, const float* gamma, const float* beta,
+                                  const float* bias, float* consts, int N, int K,
+                                  hipStream_t stream);
 hipError_t launch_linear(const LinearParams& p, int dev, int cus, hipStream_t stream);
 
 }  // namespace swinattn

@@ -127,3 +127,23 @@ def test_linear_empty_is_a_no_op():
     assert swa.swin_linear_fwd(1 << 20, 2 << 20, None, None, 3 << 20, 0, 192, 576) == swa.SWIN_OK
     # in-place residual (residual == y) is accepted
     assert swa.swin_linear_fwd(1 << 20, 2 << 20, None, 3 << 20, 3 << 20, 0, 192, 192) == swa.SWIN_OK
+
+
+def test_ln_linear_rejects_invalid_arguments():
+    E, U = swa.SWIN_ERR_INVALID_ARG, swa.SWIN_ERR_UNSUPPORTED
+    a, b, c, k, g, be = 1 << 20, 2 << 20, 3 << 20, 6 << 20, 4 << 20, 5 << 20
+    assert swa.swin_ln_linear_fwd(a, b, 0, 1e-5, c, 64, 192, 576) == E          # null consts
+    assert swa.swin_ln_linear_fwd(a, b, k + 4, 1e-5, c, 64, 192, 576) == E      # misaligned consts
+    assert swa.swin_ln_linear_fwd(a, b, k, -1.0, c, 64, 192, 576) == E          # negative eps
+    assert swa.swin_ln_linear_fwd(a, b, k, float("nan"), c, 64, 192, 576) == E
+    assert swa.swin_ln_linear_fwd(a, b, k, 1e-5, c, 64, 100, 576) == E          # K % 32
+    assert swa.swin_ln_linear_fwd(a, b, k, 1e-5, c, 64, 416, 576) == U          # K > 384
+    assert swa.swin_ln_linear_fwd(a, b, k, 1e-5, k, 64, 192, 576) == E          # y overlaps consts
+    assert swa.swin_ln_linear_fwd(a, b, k, 1e-5, c, 0, 192, 576) == swa.SWIN_OK
+    assert swa.swin_ln_linear_pack_weight(a, 0, be, None, b, k, 576, 192) == E  # null gamma
+    assert swa.swin_ln_linear_pack_weight(a, g, 0, None, b, k, 576, 192) == E   # null beta
+    assert swa.swin_ln_linear_pack_weight(a, g, be, None, b, 0, 576, 192) == E  # null consts
+    assert swa.swin_ln_linear_pack_weight(a, g, be, None, b, k + 8, 576, 192) == E
+    assert swa.swin_ln_linear_pack_weight(a, g, be, None, b, b, 576, 192) == E  # consts overlap packed
+    assert swa.swin_ln_linear_pack_weight(a, g, be, None, b, k, 576, 100) == E
+    assert swa.swin_ln_linear_pack_weight(a, g, be, None, b, k, 576, 416) == U
