@@ -53,6 +53,8 @@ def lib():
         L.oracle_linear.restype = I
         L.oracle_layernorm.argtypes = [P, I, L64, I, P, P, ctypes.c_double, P]
         L.oracle_layernorm.restype = I
+        L.oracle_swin_wattn_bwd.argtypes = [P, I, P, P, I, I, I, I, I, I, I, I, I, P, P]
+        L.oracle_swin_wattn_bwd.restype = I
         _lib = L
     return _lib
 
@@ -212,3 +214,22 @@ def layernorm(x, gamma, beta, eps: float = 1e-5):
     if lib().oracle_layernorm(_ptr(xq), xc, T, C, _ptr(gamma), _ptr(beta), eps, _ptr(y)) < 0:
         raise ValueError("oracle rejected the arguments")
     return y
+
+
+def swin_wattn_bwd(qkv, table, dout, window: int, shift: int, nthreads: int = 0):
+    """Backward of the whole forward.  ``qkv [B,H,W,3,heads,head_dim]``,
+    ``dout [B,H,W,heads*head_dim]`` (uint16 = bfloat16 patterns, float32 or
+    float64), ``table`` float32.  Returns float64 ``(dqkv [B,H,W,3,heads,
+    head_dim], dtable [(2*window-1)**2, heads])``."""
+    q, code = _qkv_arg(qkv)
+    g, gcode = _qkv_arg(dout)
+    B, H, W, three, nh, d = q.shape
+    assert three == 3 and g.shape == (B, H, W, nh * d)
+    table = np.ascontiguousarray(table, dtype=np.float32)
+    dq = np.empty(q.shape, dtype=np.float64)
+    dt = np.empty(table.shape, dtype=np.float64)
+    used = lib().oracle_swin_wattn_bwd(_ptr(q), code, _ptr(table), _ptr(g), gcode, B, H, W, nh, d,
+                                       window, shift, nthreads, _ptr(dq), _ptr(dt))
+    if used < 0:
+        raise ValueError("oracle rejected the arguments")
+    return dq, dt

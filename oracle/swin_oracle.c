@@ -402,3 +402,156 @@ int oracle_layernorm(const void* x, int xdtype, long T, int C, const float* gamm
   }
   return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* backward of the window attention                                         */
+
+typedef struct {
+  const double* win_qkv;  /* [nWin][N][3C] */
+  const double* win_g;    /* [nWin][N][C]  gradient of the window outputs */
+  const float* table;
+  const double* mask;     /* [nW][N][N] or NULL */
+  const int32_t* rel;
+  long begin, end;
+  int nW, M, nh, d;
+  double* win_dqkv;       /* [nWin][N][3C] */
+  double* dtable;         /* [(2M-1)^2][nh], this job's partial sums */
+} bwd_job;
+
+static void* bwd_worker(void* arg) {
+  const bwd_job* J = (const bwd_job*)arg;
+  const int M = J->M, N = M * M, nh = J->nh, d = J->d;
+  const long C = (long)nh * d;
+  const double scale = 1.0 / sqrt((double)d);
+  double* S = (double*)malloc(sizeof(double) * (size_t)N * N);
+  double* dP = (double*)malloc(sizeof(double) * (size_t)N * N);
+  double* Dr = (double*)malloc(sizeof(double) * (size_t)N);
+  for (long n = J->begin; n < J->end; ++n) {
+    const double* x = J->win_qkv + n * N * 3 * C;
+    const double* g = J->win_g + n * N * C;
+    const double* mk = J->mask ? J->mask + (n % J->nW) * (long)N * N : NULL;
+    double* dx = J->win_dqkv + n * N * 3 * C;
+    for (int h = 0; h < nh; ++h) {
+#define Q_(t, e) x[(long)(t) * 3 * C + h * d + (e)]
+#define K_(t, e) x[(long)(t) * 3 * C + C + h * d + (e)]
+#define V_(t, e) x[(long)(t) * 3 * C + 2 * C + h * d + (e)]
+#define G_(t, e) g[(long)(t) * C + h * d + (e)]
+      /* recompute the attention weights P (stored in S) */
+      for (int i = 0; i < N; ++i) {
+        double m = -INFINITY;
+        for (int j = 0; j < N; ++j) {
+          double dot = 0.0;
+          for (int e = 0; e < d; ++e) dot += Q_(i, e) * K_(j, e);
+          double sc = dot * scale + (double)J->table[(long)J->rel[i * N + j] * nh + h];
+          if (mk) sc += mk[i * N + j];
+          S[i * N + j] = sc;
+          m = sc > m ? sc : m;
+        }
+        double sum = 0.0;
+        for (int j = 0; j < N; ++j) {
+          S[i * N + j] = exp(S[i * N + j] - m);
+          sum += S[i * N + j];
+        }
+        for (int j = 0; j < N; ++j) S[i * N + j] /= sum;
+      }
+      /* dP = dO V^T and D_i = sum_j P_ij dP_ij */
+      for (int i = 0; i < N; ++i) {
+        double Di = 0.0;
+        for (int j = 0; j < N; ++j) {
+          double acc = 0.0;
+          for (int e = 0; e < d; ++e) acc += G_(i, e) * V_(j, e);
+          dP[i * N + j] = acc;
+          Di += S[i * N + j] * acc;
+        }
+        Dr[i] = Di;
+      }
+      /* dS = P o (dP - D), kept in dP; the bias gradient */
+      for (int i = 0; i < N; ++i)
+        for (int j = 0; j < N; ++j) {
+          dP[i * N + j] = S[i * N + j] * (dP[i * N + j] - Dr[i]);
+          J->dtable[(long)J->rel[i * N + j] * nh + h] += dP[i * N + j];
+        }
+      /* dQ = dS K * scale, dK = dS^T Q * scale, dV = P^T dO */
+      for (int t = 0; t < N; ++t)
+        for (int e = 0; e < d; ++e) {
+          double aq = 0.0, ak = 0.0, av = 0.0;
+          for (int u = 0; u < N; ++u) {
+            aq += dP[t * N + u] * K_(u, e);
+            ak += dP[u * N + t] * Q_(u, e);
+            av += S[u * N + t] * G_(u, e);
+          }
+          dx[(long)t * 3 * C + h * d + e] = aq * scale;
+          dx[(long)t * 3 * C + C + h * d + e] = ak * scale;
+          dx[(long)t * 3 * C + 2 * C + h * d + e] = av;
+        }
+#undef Q_
+#undef K_
+#undef V_
+#undef G_
+    }
+  }
+  free(S);
+  free(dP);
+  free(Dr);
+  return NULL;
+}
+
+int oracle_swin_wattn_bwd(const void* qkv, int dtype, const float* table, const void* dout,
+                          int dout_dtype, int B, int H, int W, int nh, int d, int M, int s,
+                          int nthreads, double* dqkv, double* dtable) {
+  if (bad_args(B, H, W, nh, d, M, s, dtype) || dout_dtype < ORACLE_F64 || dout_dtype > ORACLE_BF16)
+    return -1;
+  const long C = (long)nh * d, C3 = 3 * C, HW = (long)H * W;
+  const long N = (long)M * M, nW = (long)(H / M) * (W / M), nWin = (long)B * nW;
+  const long T = (long)(2 * M - 1) * (2 * M - 1);
+  /* 1. qkv and dout through the roll by (-s, -s) and the partition */
+  double* a = (double*)malloc(sizeof(double) * (size_t)(B * HW * C3));
+  double* b = (double*)malloc(sizeof(double) * (size_t)(B * HW * C3));
+  for (long i = 0; i < B * HW * C3; ++i) a[i] = load_elem(qkv, dtype, i);
+  oracle_roll(a, B, H, W, (int)C3, -s, -s, b);
+  double* win_qkv = (double*)malloc(sizeof(double) * (size_t)(B * HW * C3));
+  oracle_window_partition(b, B, H, W, (int)C3, M, win_qkv);
+  for (long i = 0; i < B * HW * C; ++i) a[i] = load_elem(dout, dout_dtype, i);
+  oracle_roll(a, B, H, W, (int)C, -s, -s, b);
+  double* win_g = (double*)malloc(sizeof(double) * (size_t)(B * HW * C));
+  oracle_window_partition(b, B, H, W, (int)C, M, win_g);
+  double* mask = NULL;
+  if (s > 0) {
+    mask = (double*)malloc(sizeof(double) * (size_t)(nW * N * N));
+    oracle_shift_mask(H, W, M, s, mask);
+  }
+  int32_t* rel = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N * N));
+  oracle_rel_index(M, rel);
+  /* 2. gradients window by window; each thread keeps its own bias partial */
+  nthreads = resolve_threads(nthreads, nWin > 0 ? nWin : 1);
+  double* win_dqkv = (double*)malloc(sizeof(double) * (size_t)(B * HW * C3));
+  double* part = (double*)calloc((size_t)(nthreads * T * nh), sizeof(double));
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  bwd_job* jobs = (bwd_job*)malloc(sizeof(bwd_job) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    bwd_job J = {win_qkv, win_g, table, mask, rel, nWin * i / nthreads, nWin * (i + 1) / nthreads,
+                 (int)nW, M, nh, d, win_dqkv, part + (long)i * T * nh};
+    jobs[i] = J;
+    pthread_create(&th[i], NULL, bwd_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  for (long e = 0; e < T * nh; ++e) {
+    double acc = 0.0;
+    for (int i = 0; i < nthreads; ++i) acc += part[(long)i * T * nh + e];
+    dtable[e] = acc;
+  }
+  /* 3. window reverse and the roll back by (+s, +s) */
+  oracle_window_reverse(win_dqkv, B, H, W, (int)C3, M, a);
+  oracle_roll(a, B, H, W, (int)C3, s, s, dqkv);
+  free(a);
+  free(b);
+  free(win_qkv);
+  free(win_g);
+  free(win_dqkv);
+  free(mask);
+  free(rel);
+  free(part);
+  free(th);
+  free(jobs);
+  return nthreads;
+}

@@ -119,6 +119,20 @@ int oracle_linear(const void* x, int xdtype, long T, int K, const void* w, int w
 int oracle_layernorm(const void* x, int xdtype, long T, int C, const float* gamma,
                      const float* beta, double eps, double* y);
 
+/* Backward of oracle_swin_wattn_fwd: given dout = dL/d(out) [B][H][W][nh*d]
+ * (type dout_dtype), the gradients with respect to qkv, dqkv [B][H][W][3][nh][d]
+ * fp64, and to the bias table, dtable [(2M-1)^2][nh] fp64.  Per window and
+ * head, with S = Q K^T / sqrt(d) + bias + mask, P = softmax(S), O = P V:
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P o (dP - D),
+ *   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dtable[rel(i,j)][h] += dS_ij
+ * (summed over every window and image); dO is dout gathered through the
+ * same roll and partition as qkv, and dqkv goes back through the reverse
+ * maps.  The NVIDIA talk, section 2, fuses this backward for training.
+ * Returns the thread count used, or -1 on bad arguments. */
+int oracle_swin_wattn_bwd(const void* qkv, int dtype, const float* table, const void* dout,
+                          int dout_dtype, int B, int H, int W, int nh, int d, int M, int s,
+                          int nthreads, double* dqkv, double* dtable);
+
 #ifdef __cplusplus
 }
 #endif

@@ -160,6 +160,12 @@ def _torch_reference(qkv, table, M, s):
     torch scaled_dot_product_attention with the additive bias+mask, reverse,
     roll back.  Index and mask come from the separately pinned oracle maps."""
     x = torch.from_numpy(np.asarray(qkv, dtype=np.float64))
+    tb = torch.from_numpy(np.asarray(table, dtype=np.float64))
+    return _torch_forward(x, tb, M, s).numpy()
+
+
+def _torch_forward(x, tb, M, s):
+    """The composition of _torch_reference on float64 tensors (differentiable)."""
     B, H, W, _, nh, d = x.shape
     N, nWy, nWx = M * M, H // M, W // M
     xr = torch.roll(x, shifts=(-s, -s), dims=(1, 2))
@@ -167,7 +173,7 @@ def _torch_reference(qkv, table, M, s):
     win = win.reshape(B * nWy * nWx, N, 3, nh, d)
     q, k, v = (win[:, :, i].permute(0, 2, 1, 3) for i in range(3))  # [nWin, nh, N, d]
     idx = torch.from_numpy(oracle.rel_index(M).astype(np.int64))
-    bias = torch.from_numpy(np.asarray(table, dtype=np.float64))[idx]  # [N, N, nh]
+    bias = tb[idx]  # [N, N, nh]
     bias = bias.permute(2, 0, 1)[None]  # [1, nh, N, N]
     mask = torch.from_numpy(oracle.shift_mask(H, W, M, s)) if s > 0 else torch.zeros(1, N, N,
                                                                                      dtype=torch.float64)
@@ -175,7 +181,7 @@ def _torch_reference(qkv, table, M, s):
     o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=bias + mask)
     o = o.permute(0, 2, 1, 3).reshape(B, nWy, nWx, M, M, nh * d).permute(0, 1, 3, 2, 4, 5)
     o = o.reshape(B, H, W, nh * d)
-    return torch.roll(o, shifts=(s, s), dims=(1, 2)).numpy()
+    return torch.roll(o, shifts=(s, s), dims=(1, 2))
 
 
 @pytest.mark.parametrize("B,H,W,nh,d,M,s", [(2, 14, 14, 2, 32, 7, 3), (1, 14, 28, 3, 16, 7, 0),
@@ -453,3 +459,69 @@ def test_layernorm_bf16_read_exactly(oracle_lib):
     xb = synth.bf16_bits(rng.standard_normal((5, 96)).astype(np.float32))
     g, b = rng.standard_normal(96).astype(np.float32), rng.standard_normal(96).astype(np.float32)
     assert np.array_equal(oracle.layernorm(xb, g, b), oracle.layernorm(synth.bf16_to_f32(xb).astype(np.float64), g, b))
+
+
+
+# ---------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("B,H,W,nh,d,M,s", [(2, 14, 14, 2, 32, 7, 3), (1, 14, 28, 3, 16, 7, 0),
+                                            (1, 24, 24, 2, 32, 12, 6), (2, 8, 12, 1, 8, 4, 1)])
+def test_backward_matches_torch_autograd_float64(oracle_lib, B, H, W, nh, d, M, s):
+    """Special case reducing to a library routine: torch autograd of the
+    float64 composition, for the gradients of qkv and of the bias table."""
+    q, table = synth.make_inputs(B, H, W, nh, d, M, seed=78, dtype="f32", table_std=0.5)
+    g = _rng(79).standard_normal((B, H, W, nh * d))
+    dq, dt = oracle.swin_wattn_bwd(q, table, g, M, s)
+    x = torch.from_numpy(np.asarray(q, dtype=np.float64)).requires_grad_(True)
+    tb = torch.from_numpy(np.asarray(table, dtype=np.float64)).requires_grad_(True)
+    (_torch_forward(x, tb, M, s) * torch.from_numpy(g)).sum().backward()
+    assert np.max(np.abs(dq - x.grad.numpy())) < 1e-11
+    assert np.max(np.abs(dt - tb.grad.numpy())) < 1e-10
+
+
+def test_backward_finite_differences(oracle_lib):
+    """Brute force: central differences of L = sum(out * g) on a tiny case
+    (shifted, masked windows), for sampled qkv entries and every table entry."""
+    B, H, W, nh, d, M, s = 1, 4, 4, 2, 3, 2, 1
+    rng = _rng(80)
+    q = rng.standard_normal((B, H, W, 3, nh, d))
+    table = (rng.standard_normal(((2 * M - 1) ** 2, nh)) * 0.5).astype(np.float32)
+    g = rng.standard_normal((B, H, W, nh * d))
+    dq, dt = oracle.swin_wattn_bwd(q, table, g, M, s)
+    L = lambda qq, tt: float((oracle.swin_wattn_fwd(qq, tt, M, s) * g).sum())
+    h = 1e-6
+    flat = q.reshape(-1)
+    for i in rng.choice(flat.size, 40, replace=False):
+        qp, qm = flat.copy(), flat.copy()
+        qp[i] += h
+        qm[i] -= h
+        fd = (L(qp.reshape(q.shape), table) - L(qm.reshape(q.shape), table)) / (2 * h)
+        assert abs(fd - dq.reshape(-1)[i]) < 1e-6 * max(1.0, abs(fd))
+    # the table is fp32 in the oracle: a step of 2^-12 on entries of size < 2
+    # is exact in fp32, and the difference quotient is then accurate to ~1e-6
+    hs = 2.0 ** -12
+    for i in range(table.size):
+        tp, tm = table.copy().reshape(-1), table.copy().reshape(-1)
+        tp[i] += hs
+        tm[i] -= hs
+        fd = (L(q, tp.reshape(table.shape)) - L(q, tm.reshape(table.shape))) / (2 * hs)
+        assert abs(fd - dt.reshape(-1)[i]) < 1e-5 * max(1.0, abs(fd))
+
+
+def test_backward_invariants(oracle_lib):
+    """Every row of dS sums to zero (the softmax Jacobian annihilates
+    constants), so the table gradient of each head sums to zero; the
+    gradients are linear in dout; with v = 0, dP = dO V^T = 0, so dS = 0:
+    dQ, dK and the table gradient vanish while dV = P^T dO does not."""
+    B, H, W, nh, d, M, s = 2, 14, 14, 3, 8, 7, 3
+    q, table = synth.make_inputs(B, H, W, nh, d, M, seed=81, dtype="f32", table_std=0.3)
+    g = _rng(82).standard_normal((B, H, W, nh * d))
+    dq, dt = oracle.swin_wattn_bwd(q, table, g, M, s)
+    assert np.all(np.abs(dt.sum(axis=0)) < 1e-10)
+    dq2, dt2 = oracle.swin_wattn_bwd(q, table, 2 * g, M, s)
+    assert np.allclose(dq2, 2 * dq, rtol=1e-12, atol=1e-13) and np.allclose(dt2, 2 * dt, rtol=1e-12, atol=1e-13)
+    q0 = np.array(q, dtype=np.float64)
+    q0[:, :, :, 2] = 0.0
+    dq0, dt0 = oracle.swin_wattn_bwd(q0, table, g, M, s)
+    assert np.all(dq0[:, :, :, :2] == 0.0) and np.all(dt0 == 0.0)
+    assert np.any(dq0[:, :, :, 2] != 0.0)
