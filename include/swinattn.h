@@ -93,6 +93,28 @@ int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int 
 int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out, int B, int H,
                        int W, int heads, int head_dim, int window, int shift, void* stream);
 
+/* Backward of swin_wattn_fwd, for training (the NVIDIA talk, section 2,
+ * fuses the window attention's backward too).  Given dout = dL/d(out), with
+ * S = Q K^T / sqrt(d) + bias + mask, P = softmax(S) per window and head:
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P o (dP - D),
+ *   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),
+ *   d(table)[rel(i,j)][h] = sum over every window and image of dS_ij,
+ * where dO is dout gathered through the same shift and partition, and
+ * dQ, dK, dV go back through the reverse maps.  P is recomputed (exact
+ * float32 softmax) from qkv and the table; nothing of the forward is read.
+ *   qkv, rel_bias_table  as swin_wattn_fwd
+ *   dout    [B][H][W][heads*head_dim] bf16, image order, 16-byte aligned
+ *   dqkv    [B][H][W][3][heads][head_dim] bf16, written (q, k, v gradients);
+ *           16-byte aligned; must not overlap qkv, dout or dtable
+ *   dtable  [(2*window-1)^2][heads] float32, written (zeroed on the stream,
+ *           then accumulated with atomics: the order of the sum varies)
+ * head_dim must be 32 and window <= 8 (else SWIN_ERR_UNSUPPORTED); the
+ * three bias tables of the kernel must fit in 64 KiB of LDS.  B == 0 zeroes
+ * dtable.  No allocation, no host synchronisation. */
+int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dout, void* dqkv,
+                   float* dtable, int B, int H, int W, int heads, int head_dim, int window,
+                   int shift, void* stream);
+
 /* Linear layer on either side of the attention, bf16 with fp32 accumulation:
  *   y[t][j] = sum_c x[t][c] * W[j][c] + bias[j]  (+ residual[t][j])
  *  - QKV GEMM + bias (K = C, N = 3C): the output token row is [3][heads][d],

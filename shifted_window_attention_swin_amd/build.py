@@ -19,7 +19,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libswinattn.so")
-SOURCES = ["swinattn_api.hip", "wattn_kernels.hip", "wattn_persistent.hip", "linear_gemm.hip"]
+SOURCES = ["swinattn_api.hip", "wattn_kernels.hip", "wattn_persistent.hip", "linear_gemm.hip",
+           "wattn_backward.hip"]
 ARCH = "gfx950"
 
 

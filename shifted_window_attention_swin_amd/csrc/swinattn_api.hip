@@ -264,6 +264,80 @@ int swin_ln_linear_pack_weight(const void* weight, const float* gamma, const flo
              : SWIN_ERR_HIP;
 }
 
+int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dout, void* dqkv,
+                   float* dtable, int B, int H, int W, int heads, int head_dim, int window,
+                   int shift, void* stream) {
+  if (!qkv || !rel_bias_table || !dout || !dqkv || !dtable) return SWIN_ERR_INVALID_ARG;
+  if (!aligned(qkv, 16) || !aligned(dout, 16) || !aligned(dqkv, 16) || !aligned(rel_bias_table, 4) ||
+      !aligned(dtable, 4))
+    return SWIN_ERR_INVALID_ARG;
+  const int M = window, s = shift;
+  if (B < 0 || H <= 0 || W <= 0 || heads <= 0 || head_dim <= 0 || M <= 0) return SWIN_ERR_INVALID_ARG;
+  if (H % M != 0 || W % M != 0 || s < 0 || s >= M) return SWIN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || M > kMaxBwdWindow) return SWIN_ERR_UNSUPPORTED;
+  if (bwd_lds_bytes(M, heads) > (size_t)kMaxTableLds) return SWIN_ERR_UNSUPPORTED;
+  const long long nW = (long long)(H / M) * (W / M);
+  const long long C = (long long)heads * head_dim;
+  const long long image_bytes = (long long)H * W * 3 * C * 2;
+  if (image_bytes > kMaxChunkBytes) return SWIN_ERR_UNSUPPORTED;
+  const long long tokens = (long long)B * H * W;
+  const size_t qb = (size_t)(tokens * 3 * C * 2), gb = (size_t)(tokens * C * 2);
+  const size_t tb = (size_t)(2 * M - 1) * (2 * M - 1) * heads * 4;
+  if (overlap(dqkv, qb, qkv, qb) || overlap(dqkv, qb, dout, gb) || overlap(dqkv, qb, dtable, tb) ||
+      overlap(dtable, tb, qkv, qb) || overlap(dtable, tb, dout, gb) ||
+      overlap(dtable, tb, rel_bias_table, tb))
+    return SWIN_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SWIN_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the bias gradient is a sum over every window: zeroed, then accumulated
+  if (launch_fill(dtable, (long long)tb / 4, 0.f, st) != hipSuccess) return SWIN_ERR_HIP;
+  if (B == 0) return SWIN_OK;
+  BwdParams p;
+  p.table = rel_bias_table;
+  p.dtable = dtable;
+  p.H = H;
+  p.W = W;
+  p.nh = heads;
+  p.shift = s;
+  p.nWy = H / M;
+  p.nWx = W / M;
+  p.nW = (int)nW;
+  const double sd = sqrt((double)head_dim);
+  p.scale = (float)(1.0 / sd);
+  p.score_scale = (float)(1.4426950408889634 / sd);
+  p.inv_scale = (float)sd;
+  {
+    float rest = (float)(100.0 * sd);
+    for (int k = 0; k < 3; ++k) {
+      uint32_t u;
+      memcpy(&u, &rest, 4);
+      u &= 0xFFFF0000u;
+      float piece;
+      memcpy(&piece, &u, 4);
+      p.mask_pieces[k] = piece;
+      rest -= piece;
+    }
+  }
+  const int cus = compute_units(dev);
+  // images per launch: in-kernel byte offsets stay below 2^31, units below 2^31
+  long long per = kMaxChunkBytes / image_bytes;
+  if (per * nW * heads > 0x7fffffffLL) per = 0x7fffffffLL / (nW * heads);
+  const char* in = static_cast<const char*>(qkv);
+  const char* gin = static_cast<const char*>(dout);
+  char* o = static_cast<char*>(dqkv);
+  for (long long b0 = 0; b0 < B; b0 += per) {
+    const long long nb = B - b0 < per ? B - b0 : per;
+    p.qkv = in + b0 * image_bytes;
+    p.dout = gin + b0 * (image_bytes / 3);
+    p.dqkv = o + b0 * image_bytes;
+    p.B = (int)nb;
+    p.units = (int)(nb * nW * heads);
+    if (launch_bwd_bf16(M, p, dev, cus, st) != hipSuccess) return SWIN_ERR_HIP;
+  }
+  return SWIN_OK;
+}
+
 namespace {
 
 int linear_common(const void* x, const float* colsum, float eps, const void* packed_weight,

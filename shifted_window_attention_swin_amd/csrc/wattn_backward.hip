@@ -1,0 +1,457 @@
+// Backward of the fused shifted-window attention (bf16, windows up to 8:
+// 1 or 4 tiles of 16 tokens), for training.  The NVIDIA talk "Swin
+// Transformer training and inference optimization" (uticex.com 1598),
+// section 2, fuses the window attention's backward as it fuses the forward.
+//
+// Per window and head, with S = Q K^T / sqrt(d) + bias + mask, P = softmax(S)
+// and dO the output gradient gathered through the same shift and partition:
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P o (dP - D),
+//   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dtable[rel(i,j)] += dS_ij.
+//
+//   unit      (image, window, head): q, k, v and dO of the head, each 16-token
+//             tile a 1 KB LDS block (16 tokens x 64 B), staged like the
+//             forward's (register prefetch of the next unit).
+//   phase 1   one wave per query tile, in the forward's transposed layout
+//             (keys in a lane's accumulator rows, queries across lanes):
+//             S^T and P (fp32, exact softmax), dP^T = V dO^T, D, dS^T, and
+//             dQ^T = K^T dS^T (K^T from transposing LDS reads, as the
+//             forward's V^T); log2-sum-exp and D of every query go to LDS.
+//   phase 2   one wave per key tile, in the plain layout (queries in rows,
+//             keys across lanes): per query tile S, P = exp2(S - L), dP,
+//             dS; dV^T += dO^T P and dK^T += Q^T dS on 16x16x16 MFMAs (the C
+//             layout of P and dS is their B operand; dO^T and Q^T come from
+//             transposing reads); dS goes to an LDS copy of the bias
+//             gradient with LDS atomics, flushed to HBM with global atomics
+//             when the workgroup ends.
+//   output    dQ, dK, dV of a token leave as 16-byte stores of 8 channels.
+
+#include <atomic>
+
+#include "wattn_common.h"
+
+namespace swinattn {
+namespace {
+
+constexpr int kBwdWaves = 4;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+SWA_INLINE f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// sum over the four lane groups (lanes c, c+16, c+32, c+48)
+SWA_INLINE float sum_groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Window coordinates (row, column) of in-tile token u of tile t.
+template <int M>
+SWA_INLINE void btile_token(int t, int u, int& ty, int& tx) {
+  ty = 4 * (t / Win<M>::Q) + u / 4;
+  tx = 4 * (t % Win<M>::Q) + u % 4;
+}
+
+// Flattened image position of window token (ty, tx) of window (wy, wx),
+// shifted frame to image; tokens outside the window stand in for its first.
+SWA_INLINE unsigned bwd_pixel(const BwdParams& p, int M, int b, int wy, int wx, int ty, int tx,
+                              bool ok) {
+  int y = wy * M + (ok ? ty : 0) + p.shift, x = wx * M + (ok ? tx : 0) + p.shift;
+  y -= y >= p.H ? p.H : 0;
+  x -= x >= p.W ? p.W : 0;
+  return ((unsigned)b * p.H + y) * p.W + x;
+}
+
+// bias table -> LDS in plain order (divided by the score scale), then a
+// zero tail that padded queries may read
+template <int M>
+SWA_INLINE void stage_bias_plain(float* s, const float* table, int nh, float inv_scale) {
+  using S = Win<M>;
+  const int n = nh * S::T;
+  for (int e = threadIdx.x; e < n + S::TAIL; e += blockDim.x) {
+    float v = 0.f;
+    if (e < n) {
+      const int h = e / S::T, k = e - h * S::T;
+      v = table[k * nh + h] * inv_scale;
+    }
+    s[e] = v;
+  }
+}
+
+template <int M>
+__global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParams p) {
+  using S = Win<M>;
+  constexpr int NT = S::NT, NK = S::NK, T = S::T;
+  static_assert(NT <= 4, "windows of up to 4 tiles");
+  constexpr int BLOCK = 1024;
+  constexpr int SLICES = 4;  // q, k, v, dO
+  extern __shared__ float s_lds[];
+  const int nh = p.nh;
+  const int off_l2 = (3 * nh * T + 2 * S::TAIL + 3) & ~3;  // 16-byte aligned
+  float* s_brev = s_lds;                        // reversed table / scale (phase 1)
+  float* s_bfwd = s_brev + nh * T + S::TAIL;    // plain table / scale (phase 2)
+  float* s_dtab = s_bfwd + nh * T + S::TAIL;    // bias gradient of this workgroup [nh][T]
+  float* s_l2 = s_lds + off_l2;                 // [64] log2-sum-exp of the queries
+  float* s_dd = s_l2 + 64;                      // [64] D of the queries
+  char* s_unit = reinterpret_cast<char*>(s_dd + 64);  // 4 slices x NT blocks of 1 KB
+  auto block = [&](int sl, int t) { return s_unit + (sl * NT + t) * BLOCK; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gq = lane & 3, cq = lane >> 2;  // load layout: 16-byte part, token
+  const int g = lane >> 4, c = lane & 15;   // MFMA layout: lane group, token
+  const unsigned Cb = (unsigned)nh * kHeadDim * 2;  // bytes of one q (k, v, dO) row
+  const char* in = static_cast<const char*>(p.qkv);
+  const char* gin = static_cast<const char*>(p.dout);
+  char* dout3 = static_cast<char*>(p.dqkv);
+  const float scale = p.scale;
+
+  stage_bias<M>(s_brev, p.table, nh, p.inv_scale);
+  stage_bias_plain<M>(s_bfwd, p.table, nh, p.inv_scale);
+  for (int e = tid; e < nh * T; e += blockDim.x) s_dtab[e] = 0.f;
+
+  // units: (image, window, head), in grid order
+  struct Pos {
+    int h, b, wy, wx;
+  };
+  auto decode = [&](int uu) {
+    Pos q;
+    q.h = uu % nh;
+    const int bw = uu / nh;
+    q.b = bw / p.nW;
+    const int w = bw - q.b * p.nW;
+    q.wy = w / p.nWx;
+    q.wx = w - q.wy * p.nWx;
+    return q;
+  };
+  // tile wv of each slice: one token address per lane
+  using Regs = u32x4[SLICES];
+  auto issue = [&](Regs& R, const Pos& q) {
+    if (wv < NT) {
+      int ty, tx;
+      btile_token<M>(wv, cq, ty, tx);
+      const bool ok = ty < M && tx < M;
+      const unsigned pix = bwd_pixel(p, M, q.b, q.wy, q.wx, ty, tx, ok);
+      const char* src = in + pix * (3u * Cb) + (unsigned)q.h * kHeadDim * 2 + 16u * gq;
+#pragma unroll
+      for (int sl = 0; sl < 3; ++sl) R[sl] = *reinterpret_cast<const u32x4*>(src + sl * Cb);
+      R[3] = *reinterpret_cast<const u32x4*>(gin + pix * Cb + (unsigned)q.h * kHeadDim * 2 + 16u * gq);
+    }
+  };
+  auto write = [&](const Regs& R) {
+    if (wv < NT) {
+#pragma unroll
+      for (int sl = 0; sl < SLICES; ++sl)
+        *reinterpret_cast<u32x4*>(block(sl, wv) + lane * 16) = R[sl];
+    }
+  };
+  const bool g_ok = g < S::LG;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+  // local label of shifted-frame position (yy, xx) of a masked window
+  auto local_label = [&](int yy, int xx) {
+    return 2 * (yy >= p.H - p.shift) + (xx >= p.W - p.shift);
+  };
+  auto mask_key = [&](int loc) {  // [label == g] x_s
+    bf16x8 a = {};
+#pragma unroll
+    for (int k = 0; k < 3; ++k) a[k] = loc == g ? (__bf16)p.mask_pieces[k] : (__bf16)0.f;
+    return a;
+  };
+  auto mask_query = [&](int loc) {  // [label == g] - 1
+    bf16x8 a = {};
+#pragma unroll
+    for (int k = 0; k < 3; ++k) a[k] = loc == g ? (__bf16)0.f : (__bf16)-1.f;
+    return a;
+  };
+  // 16 bytes of token u (MFMA layout lane) of tile t of slice sl
+  auto tok16 = [&](int sl, int t) {
+    return *reinterpret_cast<const bf16x8*>(block(sl, t) + (4 * c + g) * 16);
+  };
+  // transposing read of tile t of slice sl, channel half hf: element k of
+  // lane (g, i) is channel out_channel(hf, i) of in-tile token 4g + k
+  auto tile_t = [&](int sl, int t, int hf) { return lds_read_tr(block(sl, t) + lane * 16 + 8 * hf); };
+  // 8 consecutive channels of a lane, from two accumulator tiles
+  auto pack8 = [&](const f32x4& lo, const f32x4& hi, float mul) {
+    bf16x8 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      o[r] = (__bf16)(lo[r] * mul);
+      o[4 + r] = (__bf16)(hi[r] * mul);
+    }
+    return o;
+  };
+
+  // ---- phase 1: query tile it = wv -----------------------------------------
+  auto phase1 = [&](const Pos& pos, bool masked) {
+    const int it = wv;
+    if (it >= NT) return;
+    const int h = pos.h;
+    int ty, tx;
+    btile_token<M>(it, c, ty, tx);
+    const bool ok = ty < M && tx < M;
+    const int qbase = h * T + T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
+    const bf16x8 q = tok16(0, it), go = tok16(3, it);
+    bf16x8 mq = {};
+    if (masked) mq = mask_query(local_label(pos.wy * M + ty, pos.wx * M + tx));
+    f32x4 sc[NT], dp[NT];
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!S::col_ok(jt, r)) {
+          acc[r] = -__builtin_inff();
+          continue;
+        }
+        float v = s_brev[qbase + S::E(jt) + r];
+        if (!S::rows_all(jt)) v = g_ok ? v : -__builtin_inff();
+        acc[r] = v;
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(1, jt), q, acc, 0, 0, 0);
+      if (masked) {
+        // key-side operand of this lane: key row (jt, 4g + r) is owned by
+        // lane group g, the key token is the lane's own token c of tile jt
+        int ky, kx;
+        btile_token<M>(jt, c, ky, kx);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            mask_key(local_label(pos.wy * M + ky, pos.wx * M + kx)), mq, acc, 0, 0, 0);
+      }
+      sc[jt] = acc;
+      dp[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(2, jt), go, z, 0, 0, 0);
+    }
+    // exact softmax in fp32: max, then the sum of exp2 about it
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (S::col_ok(jt, r)) m = fmaxf(m, sc[jt][r]);
+    m = max_groups(m) * p.score_scale;
+    float sum = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = S::col_ok(jt, r) ? fast_exp2(fmaf(sc[jt][r], p.score_scale, -m)) : 0.f;
+        sc[jt][r] = e;
+        sum += e;
+      }
+    sum = sum_groups(sum);
+    const float inv = fast_rcp(sum);
+    float dsum = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[jt][r] *= inv;
+        dsum += sc[jt][r] * dp[jt][r];
+      }
+    const float Dq = sum_groups(dsum);
+    // dS^T = P o (dP^T - D), packed as the B operand of the key contraction
+    bf16x8 pb[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pb[kk][r] = (__bf16)(sc[2 * kk][r] * (dp[2 * kk][r] - Dq));
+        pb[kk][4 + r] = (2 * kk + 1 < NT) ? (__bf16)(sc[2 * kk + 1][r] * (dp[2 * kk + 1][r] - Dq))
+                                          : (__bf16)0.f;
+      }
+    // dQ^T = K^T dS^T, K^T from transposing reads (odd tile counts: any
+    // finite data for the missing tile, its dS^T is zero)
+    f32x4 o0 = z, o1 = z;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const int t1 = 2 * kk + 1 < NT ? 2 * kk + 1 : 2 * kk;
+      const bf16x8 k0 = __builtin_shufflevector(tile_t(1, 2 * kk, 0), tile_t(1, t1, 0), 0, 1, 2, 3,
+                                                4, 5, 6, 7);
+      const bf16x8 k1 = __builtin_shufflevector(tile_t(1, 2 * kk, 1), tile_t(1, t1, 1), 0, 1, 2, 3,
+                                                4, 5, 6, 7);
+      o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, pb[kk], o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, pb[kk], o1, 0, 0, 0);
+    }
+    if (g == 0) {
+      s_l2[it * 16 + c] = ok ? m + __builtin_amdgcn_logf(sum) : 0.f;
+      s_dd[it * 16 + c] = ok ? Dq : 0.f;
+    }
+    if (ok) {
+      const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, ty, tx, true);
+      __builtin_nontemporal_store(
+          pack8(o0, o1, scale),
+          reinterpret_cast<bf16x8*>(dout3 + pix * (3u * Cb) + h * kHeadDim * 2 + 16 * g));
+    }
+  };
+
+  // ---- phase 2: key tile jk = wv ------------------------------------------
+  auto phase2 = [&](const Pos& pos, bool masked) {
+    const int jk = wv;
+    if (jk >= NT) return;
+    const int h = pos.h;
+    int ky, kx;
+    btile_token<M>(jk, c, ky, kx);
+    const bool kok = ky < M && kx < M;
+    const int kbase = h * T + S::C0 + S::D * g - (kok ? S::D * ky + kx : 0);
+    const bf16x8 kb = tok16(1, jk), vb = tok16(2, jk);
+    bf16x8 mk = {};
+    if (masked) mk = mask_key(local_label(pos.wy * M + ky, pos.wx * M + kx));
+    f32x4 dk0 = z, dk1 = z, dv0 = z, dv1 = z;
+#pragma unroll
+    for (int iq = 0; iq < NT; ++iq) {
+      // rows 4g + r: query (4 (iq/Q) + g, 4 (iq%Q) + r)
+      const bool row_ok = S::rows_all(iq) || g_ok;
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!S::col_ok(iq, r) || !row_ok || !kok) {
+          acc[r] = -__builtin_inff();
+          continue;
+        }
+        acc[r] = s_bfwd[kbase + S::E(iq) + r];
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(0, iq), kb, acc, 0, 0, 0);
+      if (masked) {
+        int qy, qx;
+        btile_token<M>(iq, c, qy, qx);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            mask_query(local_label(pos.wy * M + qy, pos.wx * M + qx)), mk, acc, 0, 0, 0);
+      }
+      const f32x4 dpq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(3, iq), vb, z, 0, 0, 0);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(s_l2 + iq * 16 + 4 * g);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(s_dd + iq * 16 + 4 * g);
+      bf16x4 pb, sb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = fast_exp2(fmaf(acc[r], p.score_scale, -l2[r]));
+        const float ds = pv * (dpq[r] - dd[r]);
+        pb[r] = (__bf16)pv;
+        sb[r] = (__bf16)ds;
+        if (S::col_ok(iq, r) && row_ok && kok) atomicAdd(&s_dtab[kbase + S::E(iq) + r], ds);
+      }
+      dv0 = mfma16(tile_t(3, iq, 0), pb, dv0);
+      dv1 = mfma16(tile_t(3, iq, 1), pb, dv1);
+      dk0 = mfma16(tile_t(0, iq, 0), sb, dk0);
+      dk1 = mfma16(tile_t(0, iq, 1), sb, dk1);
+    }
+    if (kok) {
+      const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, ky, kx, true);
+      char* dst = dout3 + pix * (3u * Cb) + h * kHeadDim * 2 + 16 * g;
+      __builtin_nontemporal_store(pack8(dk0, dk1, scale), reinterpret_cast<bf16x8*>(dst + Cb));
+      __builtin_nontemporal_store(pack8(dv0, dv1, 1.f), reinterpret_cast<bf16x8*>(dst + 2 * Cb));
+    }
+  };
+
+  // persistent walk over the units in grid order, the next unit's loads in
+  // flight while a unit is computed
+  int u = blockIdx.x;
+  const int u_step = gridDim.x;
+  Regs R;
+  Pos nxt = decode(u);
+  if (u < p.units) issue(R, nxt);
+  __syncthreads();  // tables staged
+  for (; u < p.units; u += u_step) {
+    write(R);
+    __syncthreads();  // unit visible to every wave
+    const Pos cur = nxt;
+    if (u + u_step < p.units) {
+      nxt = decode(u + u_step);
+      issue(R, nxt);
+    }
+    const bool masked = window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx);
+    phase1(cur, masked);
+    __syncthreads();  // log2-sum-exp and D of every query visible
+    phase2(cur, masked);
+    __syncthreads();  // every wave is done with the unit before it is overwritten
+  }
+  // this workgroup's bias gradient -> HBM
+  for (int e = tid; e < nh * T; e += blockDim.x) {
+    const int h = e / T, k = e - h * T;
+    const float v = s_dtab[e];
+    if (v != 0.f) atomicAdd(p.dtable + k * nh + h, v);
+  }
+}
+
+template <int M>
+size_t bwd_lds_m(int nh) {
+  using S = Win<M>;
+  return ((size_t)((3 * nh * S::T + 2 * S::TAIL + 3) & ~3) + 128) * sizeof(float) +
+         4 * S::NT * 1024;
+}
+
+template <int M>
+int bwd_blocks_per_cu(int dev, size_t lds) {
+  static std::atomic<long long> cache[kMaxDevices];
+  const bool cacheable = dev >= 0 && dev < kMaxDevices;
+  if (cacheable) {
+    const long long v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0 && (size_t)(v >> 8) == lds) return (int)(v & 255);
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_bwd_bf16_kernel<M>,
+                                                   kBwdWaves * 64, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (per_cu > 255) per_cu = 255;
+  if (cacheable) cache[dev].store(((long long)lds << 8) | per_cu, std::memory_order_relaxed);
+  return per_cu;
+}
+
+template <int M>
+hipError_t launch_bwd_m(const BwdParams& p, int dev, int cus, hipStream_t st) {
+  const size_t lds = bwd_lds_m<M>(p.nh);
+  long long grid = (long long)cus * bwd_blocks_per_cu<M>(dev, lds);
+  if (grid > p.units) grid = p.units;
+  hipLaunchKernelGGL(wattn_bwd_bf16_kernel<M>, dim3((unsigned)grid), dim3(kBwdWaves * 64), lds, st,
+                     p);
+  return hipGetLastError();
+}
+
+__global__ void fill_kernel(float* dst, long long n, float v) {
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x)
+    dst[e] = v;
+}
+
+}  // namespace
+
+size_t bwd_lds_bytes(int M, int nh) {
+  switch (M) {
+    case 1: return bwd_lds_m<1>(nh);
+    case 2: return bwd_lds_m<2>(nh);
+    case 3: return bwd_lds_m<3>(nh);
+    case 4: return bwd_lds_m<4>(nh);
+    case 5: return bwd_lds_m<5>(nh);
+    case 6: return bwd_lds_m<6>(nh);
+    case 7: return bwd_lds_m<7>(nh);
+    case 8: return bwd_lds_m<8>(nh);
+    default: return 0;
+  }
+}
+
+hipError_t launch_fill(float* dst, long long n, float v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dst, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(int M, const BwdParams& p, int dev, int cus, hipStream_t stream) {
+  switch (M) {
+    case 1: return launch_bwd_m<1>(p, dev, cus, stream);
+    case 2: return launch_bwd_m<2>(p, dev, cus, stream);
+    case 3: return launch_bwd_m<3>(p, dev, cus, stream);
+    case 4: return launch_bwd_m<4>(p, dev, cus, stream);
+    case 5: return launch_bwd_m<5>(p, dev, cus, stream);
+    case 6: return launch_bwd_m<6>(p, dev, cus, stream);
+    case 7: return launch_bwd_m<7>(p, dev, cus, stream);
+    case 8: return launch_bwd_m<8>(p, dev, cus, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swinattn

@@ -80,4 +80,25 @@ hipError_t launch_linear_ln_consts(const void* w, const float* gamma, const floa
                                   hipStream_t stream);
 hipError_t launch_linear(const LinearParams& p, int dev, int cus, hipStream_t stream);
 
+// Backward of the window attention, bf16 (wattn_backward.hip); windows up
+// to kMaxBwdWindow.
+constexpr int kMaxBwdWindow = 8;
+struct BwdParams {
+  const void* qkv;     // [B][H][W][3][nh][32] of this launch's images
+  const float* table;  // [(2M-1)^2][nh]
+  const void* dout;    // [B][H][W][nh*32]
+  void* dqkv;          // [B][H][W][3][nh][32]
+  float* dtable;       // [(2M-1)^2][nh], accumulated with atomics (zeroed by the host)
+  int B, H, W, nh, shift;
+  int nWy, nWx, nW;
+  int units;           // B * nW * nh
+  float scale;         // 1 / sqrt(head_dim)
+  float score_scale;   // log2(e) / sqrt(head_dim)
+  float inv_scale;     // sqrt(head_dim)
+  float mask_pieces[3];
+};
+size_t bwd_lds_bytes(int M, int nh);
+hipError_t launch_bwd_bf16(int M, const BwdParams& p, int dev, int cus, hipStream_t stream);
+hipError_t launch_fill(float* dst, long long n, float v, hipStream_t stream);
+
 }  // namespace swinattn

@@ -147,3 +147,35 @@ def test_ln_linear_rejects_invalid_arguments():
     assert swa.swin_ln_linear_pack_weight(a, g, be, None, b, b, 576, 192) == E  # consts overlap packed
     assert swa.swin_ln_linear_pack_weight(a, g, be, None, b, k, 576, 100) == E
     assert swa.swin_ln_linear_pack_weight(a, g, be, None, b, k, 576, 416) == U
+
+
+def _bwd(**kw):
+    a = dict(qkv=A16, table=A32, dout=A48, dqkv=4 << 20, dtable=5 << 20, B=2, H=14, W=14,
+             heads=3, head_dim=32, window=7, shift=3)
+    a.update(kw)
+    return swa.swin_wattn_bwd(a["qkv"], a["table"], a["dout"], a["dqkv"], a["dtable"], a["B"],
+                              a["H"], a["W"], a["heads"], a["head_dim"], a["window"], a["shift"], 0)
+
+
+def test_bwd_rejects_invalid_arguments():
+    E = swa.SWIN_ERR_INVALID_ARG
+    for k in ("qkv", "table", "dout", "dqkv", "dtable"):
+        assert _bwd(**{k: 0}) == E, k
+    assert _bwd(qkv=A16 + 8) == E              # not 16-byte aligned
+    assert _bwd(dout=A48 + 8) == E
+    assert _bwd(dqkv=(4 << 20) + 4) == E
+    assert _bwd(dtable=(5 << 20) + 2) == E     # not 4-byte aligned
+    assert _bwd(B=-1) == E
+    assert _bwd(H=15) == E
+    assert _bwd(shift=7) == E
+    assert _bwd(window=0) == E
+    assert _bwd(dqkv=A16) == E                 # dqkv overlaps qkv
+    assert _bwd(dtable=A48 + 64) == E          # dtable overlaps dout
+    assert _bwd(dtable=A32) == E               # dtable overlaps the table
+
+
+def test_bwd_reports_unsupported_configurations():
+    U = swa.SWIN_ERR_UNSUPPORTED
+    assert _bwd(head_dim=64) == U
+    assert _bwd(window=12, H=24, W=24, shift=6) == U        # windows beyond 8
+    assert _bwd(heads=48) == U                               # tables beyond 64 KiB of LDS

@@ -1,0 +1,120 @@
+"""GPU parity of the fused attention backward against the fp64 oracle,
+through the C ABI.
+
+Bar, per gradient (dq, dk, dv): max-abs error <= 2^-6 of the largest
+reference entry and mean-abs error <= 2^-8 of the mean reference magnitude.
+The GPU rounds P and dS to bf16 (unit roundoff 2^-8) before the key and
+value contractions, and the gradients to bf16 on output; the rest is fp32.
+The bias-table gradient (fp32 sums of fp32 dS over every window) is within
+1e-3 of its largest entry.  Inputs are seeded
+synth.py workloads, and dout is drawn like qkv.  Every case prints its name
+before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import shifted_window_attention_swin_amd as swa
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(_dev())
+
+
+def _dout(B, H, W, C, seed):
+    return synth.bf16_bits(synth.normal(synth.stream_key(seed, 7), B * H * W * C, 1.0)).reshape(B, H, W, C)
+
+
+def _run(qkv, table, dout, M, s):
+    B, H, W, _, nh, d = qkv.shape
+    q, g = _bf16_dev(qkv), _bf16_dev(dout)
+    t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.float32)).to(_dev())
+    dq = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=_dev())
+    dt = torch.full(t.shape, float("nan"), dtype=torch.float32, device=_dev())
+    swa.check(swa.swin_wattn_bwd(q, t, g, dq, dt, B, H, W, nh, d, M, s), "bwd")
+    torch.cuda.synchronize()
+    return dq.float().cpu().numpy().astype(np.float64), dt.cpu().numpy().astype(np.float64)
+
+
+def _check(qkv, table, dout, M, s, what):
+    dq, dt = _run(qkv, table, dout, M, s)
+    rq, rt = oracle.swin_wattn_bwd(qkv, table, dout, M, s)
+    assert np.isfinite(dq).all() and np.isfinite(dt).all(), what
+    et = np.abs(dt - rt)
+    lim_t = 1e-3 * np.abs(rt).max() + 1e-6
+    print(f"    {what}: dtable max_err={et.max():.3e} bound {lim_t:.3e}", flush=True)
+    bad = []
+    for i, name in enumerate("qkv"):
+        e = np.abs(dq[:, :, :, i] - rq[:, :, :, i])
+        ref = np.abs(rq[:, :, :, i])
+        lim_max, lim_mean = 2.0**-6 * ref.max() + 1e-6, 2.0**-8 * ref.mean() + 1e-7
+        print(f"      d{name}: max_abs={e.max():.3e} (bound {lim_max:.3e}) "
+              f"mean_abs={e.mean():.3e} (bound {lim_mean:.3e}) |ref| max {ref.max():.3f}", flush=True)
+        if e.max() > lim_max or e.mean() > lim_mean:
+            bad.append(name)
+    assert not bad, f"{what}: d{bad}"
+    assert et.max() <= lim_t, what
+
+
+@pytest.mark.parametrize("B,H,W,nh,M,s", [
+    (1, 14, 14, 1, 7, 0),     # one head, no shift
+    (2, 14, 14, 3, 7, 3),     # shifted: masked windows on the last row and column
+    (1, 16, 16, 2, 8, 4),     # window 8: full tiles
+    (2, 10, 15, 2, 5, 3),     # window 5: padded tiles, H != W
+    (1, 12, 12, 4, 6, 2),
+    (2, 8, 8, 2, 4, 2),       # window 4: one tile
+    (1, 6, 9, 2, 3, 1),       # window 3: one padded tile
+    (1, 4, 4, 1, 2, 1),
+    (1, 3, 5, 2, 1, 0),       # window 1: the output is v, so dv = dout, dq = dk = 0
+])
+def test_backward_matches_oracle(B, H, W, nh, M, s):
+    _say(f"bwd B={B} H={H} W={W} nh={nh} M={M} s={s}")
+    qkv, table = synth.make_inputs(B, H, W, nh, 32, M, seed=500 + M + s, table_std=0.3)
+    dout = _dout(B, H, W, nh * 32, seed=600 + M)
+    _check(qkv, table, dout, M, s, f"M={M} s={s}")
+
+
+@pytest.mark.parametrize("name", ["swin-t-s1", "swin-t-s3"])
+def test_backward_workloads(name):
+    w = synth.WORKLOADS[name]
+    B = min(w["B"], 8)
+    qkv, table = synth.workload_inputs(name, batch=B)
+    dout = _dout(B, w["H"], w["W"], w["heads"] * w["head_dim"], seed=w["seed"])
+    for s in w["shifts"]:
+        _say(f"bwd {name} B={B} shift={s}")
+        _check(qkv, table, dout, w["window"], s, f"{name} s={s}")
+
+
+def test_backward_swin_l_sampled_windows():
+    """Swin-L stage 1 at B=4 through the GPU; the oracle checks the whole
+    output (a few seconds on the host)."""
+    w = synth.WORKLOADS["swin-l-s1"]
+    qkv, table = synth.workload_inputs("swin-l-s1", batch=4)
+    dout = _dout(4, w["H"], w["W"], w["heads"] * 32, seed=w["seed"])
+    _say("bwd swin-l-s1 B=4 shift=3")
+    _check(qkv, table, dout, 7, 3, "swin-l-s1 B=4")
+
+
+def test_backward_zero_batch_zeroes_dtable():
+    _say("bwd B=0")
+    q = torch.empty(0, 14, 14, 3, 2, 32, dtype=torch.bfloat16, device=_dev())
+    g = torch.empty(0, 14, 14, 64, dtype=torch.bfloat16, device=_dev())
+    t = torch.zeros(169, 2, device=_dev())
+    dq = torch.empty(1, 14, 14, 3, 2, 32, dtype=torch.bfloat16, device=_dev())
+    dt = torch.full((169, 2), 5.0, device=_dev())
+    assert swa.swin_wattn_bwd(q.data_ptr() or 1 << 20, t, g.data_ptr() or 2 << 20, dq, dt, 0, 14, 14,
+                              2, 32, 7, 3) == swa.SWIN_OK
+    torch.cuda.synchronize()
+    assert bool((dt == 0).all())
