@@ -8,7 +8,9 @@ the working set of the timed region exceeds twice the 256 MB Infinity Cache
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-With --workload naming a linear-layer workload (qkv-l-s1, proj-l-s1, ...) a
+With --backward a step is one swin_wattn_bwd over the workload instead (the
+bias-gradient zero fill and the backward kernel).  With --workload naming a
+linear-layer workload (qkv-l-s1, proj-l-s1, ...) a
 step is one swin_linear_fwd over its tokens instead, and with a layer norm +
 QKV workload (lnqkv-l-s1, ...) one swin_ln_linear_fwd.
 """
@@ -36,6 +38,7 @@ CSRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc")
 KERNEL_SOURCES = {
     "wattn_fwd_bf16": ("wattn_internal.h", "wattn_common.h", "wattn_persistent.hip"),
     "linear_fwd": ("wattn_internal.h", "wattn_common.h", "linear_gemm.hip"),
+    "wattn_bwd_bf16": ("wattn_internal.h", "wattn_common.h", "wattn_backward.hip"),
 }
 
 
@@ -57,6 +60,16 @@ def algorithmic(B, H, W, heads, head_dim, window, elem=2):
     C = heads * head_dim
     N = window * window
     return 4 * C * T * elem, 4 * N * C * T
+
+
+def bwd_algorithmic(B, H, W, heads, head_dim, window, elem=2):
+    """Bytes: qkv and dout read once, dqkv written once (the bias table and
+    its gradient are a few KB).  FLOPs: five contractions of N x N x head_dim
+    per window and head (S, dP, dV, dK, dQ) over the unpadded N."""
+    T = B * H * W
+    C = heads * head_dim
+    N = window * window
+    return 7 * C * T * elem, 10 * N * C * T
 
 
 def fwd_kernel_name(window: int, heads: int) -> str:
@@ -111,6 +124,31 @@ def cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_re
             "kind": "oracle",
             "sample": f"{name}, first {sample_batch} of {w['B']} images, whole forward x{reps} "
                       f"({dt:.1f} s wall, fp64, {used} threads)"}
+
+
+def bwd_cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50):
+    """The fp64 oracle backward on the first `sample_batch` images, as
+    cpu_baseline does for the forward."""
+    import oracle
+    import synth
+    w = synth.WORKLOADS[name]
+    qkv, table = synth.workload_inputs(name, batch=sample_batch)
+    C = w["heads"] * w["head_dim"]
+    n = sample_batch * w["H"] * w["W"] * C
+    dout = synth.bf16_bits(synth.normal(synth.stream_key(w["seed"], 7), n, 1.0))
+    dout = dout.reshape(sample_batch, w["H"], w["W"], C)
+    reps, cores = 0, 0
+    t0 = time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        _, _, cores = oracle.swin_wattn_bwd(qkv, table, dout, w["window"], w["shifts"][0],
+                                            return_threads=True)
+        reps += 1
+    dt = time.perf_counter() - t0
+    nbytes, _ = bwd_algorithmic(sample_batch, w["H"], w["W"], w["heads"], w["head_dim"], w["window"])
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{name}, first {sample_batch} of {w['B']} images, whole backward x{reps} "
+                      f"({dt:.1f} s wall, fp64, {cores} threads)"}
 
 
 def time_steps(torch, step, K: int, warmup: int, stream, launches_per_step: int):
@@ -281,6 +319,73 @@ def linear_bench(args, torch, np) -> int:
     return 0
 
 
+def bwd_bench(args, torch, np) -> int:
+    """One swin_wattn_bwd per step over the whole workload (first shift)."""
+    import shifted_window_attention_swin_amd as swa
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    B, H, W, nh, d, M = w["B"], w["H"], w["W"], w["heads"], w["head_dim"], w["window"]
+    s = w["shifts"][0]
+    C = nh * d
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    qkv_np, table_np = synth.workload_inputs(args.workload)
+    q0, table = bf(qkv_np), torch.from_numpy(table_np).to(dev)
+    del qkv_np
+    g0 = bf(synth.bf16_bits(synth.normal(synth.stream_key(w["seed"], 7), B * H * W * C, 1.0)))
+    nbytes, nflops = bwd_algorithmic(B, H, W, nh, d, M)
+    sets = 1 if args.hot else 2 * MALL_BYTES // nbytes + 1
+    qs = [q0] + [q0.clone() for _ in range(sets - 1)]
+    gs = [g0] + [g0.clone() for _ in range(sets - 1)]
+    dqs = [torch.empty_like(q0) for _ in range(sets)]
+    dt = torch.empty_like(table)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        k = i % sets
+        swa.check(swa.swin_wattn_bwd(qs[k], table, gs[k], dqs[k], dt, B, H, W, nh, d, M, s, stream),
+                  "bwd")
+
+    K = args.steps
+    total_ms, avg_launch_s, isolated_s = time_steps(torch, step, K, args.warmup, stream, 1)
+    value = nbytes * K / (total_ms / 1e3) / 1e9
+    achieved = nbytes / avg_launch_s / 1e9
+    result = {
+        "metric": f"shifted-window attn bwd GB/s ({w['desc']}, bf16); % HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, qkv and dout ~ N(0,1), bias table ~ N(0,0.02))",
+        "config": {"workload": args.workload, "pass": "backward", "desc": w["desc"], "B": B, "H": H,
+                   "W": W, "heads": nh, "head_dim": d, "window": M, "shift": s,
+                   "buffer_sets": sets, "cache": "hot" if args.hot else "cold"},
+        "tflops": round(nflops * K / (total_ms / 1e3) / 1e12, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        # a step is two launches (the bias-gradient zero fill, then the
+        # backward kernel); the per-step time is charged to the backward kernel
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, "wattn_bwd_bf16"),
+                     "kernel": f"wattn_bwd_bf16_kernel<{M}>",
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "isolated_launch_us": round(isolated_s * 1e6, 3),
+                     "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
+                     "mfma_tflops": round(nflops / avg_launch_s / 1e12, 3),
+                     "mfma_peak_tflops": BF16_PEAK_TFLOPS},
+        "cpu_baseline": None if args.no_cpu_baseline else
+        bwd_cpu_baseline(args.workload, min(args.cpu_sample_batch, B, 8)),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +394,7 @@ def main() -> int:
     # launches reach steady speed: 1000 warmup launches are about 60 ms here
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="swin-l-s1")
+    ap.add_argument("--backward", action="store_true", help="time the attention backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batch", type=int, default=64)
     ap.add_argument("--hot", action="store_true", help="one buffer set (working set may sit in cache)")
@@ -320,6 +426,8 @@ def main() -> int:
 
     if args.workload in synth.LINEAR_WORKLOADS or args.workload in synth.LN_LINEAR_WORKLOADS:
         return linear_bench(args, torch, np)
+    if args.backward:
+        return bwd_bench(args, torch, np)
     w = synth.WORKLOADS[args.workload]
     if w["dtype"] != "bf16":
         print("bench.py: the benchmark times the bf16 path", file=sys.stderr)

@@ -108,9 +108,9 @@ int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out
  *           16-byte aligned; must not overlap qkv, dout or dtable
  *   dtable  [(2*window-1)^2][heads] float32, written (zeroed on the stream,
  *           then accumulated with atomics: the order of the sum varies)
- * head_dim must be 32 and window <= 8 (else SWIN_ERR_UNSUPPORTED); the
- * three bias tables of the kernel must fit in 64 KiB of LDS.  B == 0 zeroes
- * dtable.  No allocation, no host synchronisation. */
+ * head_dim must be 32 and window <= 8 (else SWIN_ERR_UNSUPPORTED); any
+ * number of heads.  B == 0 zeroes dtable.  No allocation, no host
+ * synchronisation. */
 int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dout, void* dqkv,
                    float* dtable, int B, int H, int W, int heads, int head_dim, int window,
                    int shift, void* stream);

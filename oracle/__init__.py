@@ -216,7 +216,8 @@ def layernorm(x, gamma, beta, eps: float = 1e-5):
     return y
 
 
-def swin_wattn_bwd(qkv, table, dout, window: int, shift: int, nthreads: int = 0):
+def swin_wattn_bwd(qkv, table, dout, window: int, shift: int, nthreads: int = 0,
+                   return_threads: bool = False):
     """Backward of the whole forward.  ``qkv [B,H,W,3,heads,head_dim]``,
     ``dout [B,H,W,heads*head_dim]`` (uint16 = bfloat16 patterns, float32 or
     float64), ``table`` float32.  Returns float64 ``(dqkv [B,H,W,3,heads,
@@ -232,4 +233,4 @@ def swin_wattn_bwd(qkv, table, dout, window: int, shift: int, nthreads: int = 0)
                                        window, shift, nthreads, _ptr(dq), _ptr(dt))
     if used < 0:
         raise ValueError("oracle rejected the arguments")
-    return dq, dt
+    return (dq, dt, used) if return_threads else (dq, dt)

@@ -275,7 +275,6 @@ int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dou
   if (B < 0 || H <= 0 || W <= 0 || heads <= 0 || head_dim <= 0 || M <= 0) return SWIN_ERR_INVALID_ARG;
   if (H % M != 0 || W % M != 0 || s < 0 || s >= M) return SWIN_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || M > kMaxBwdWindow) return SWIN_ERR_UNSUPPORTED;
-  if (bwd_lds_bytes(M, heads) > (size_t)kMaxTableLds) return SWIN_ERR_UNSUPPORTED;
   const long long nW = (long long)(H / M) * (W / M);
   const long long C = (long long)heads * head_dim;
   const long long image_bytes = (long long)H * W * 3 * C * 2;
@@ -320,9 +319,8 @@ int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dou
     }
   }
   const int cus = compute_units(dev);
-  // images per launch: in-kernel byte offsets stay below 2^31, units below 2^31
-  long long per = kMaxChunkBytes / image_bytes;
-  if (per * nW * heads > 0x7fffffffLL) per = 0x7fffffffLL / (nW * heads);
+  // images per launch: in-kernel byte offsets stay below 2^31
+  const long long per = kMaxChunkBytes / image_bytes;
   const char* in = static_cast<const char*>(qkv);
   const char* gin = static_cast<const char*>(dout);
   char* o = static_cast<char*>(dqkv);
@@ -332,7 +330,7 @@ int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dou
     p.dout = gin + b0 * (image_bytes / 3);
     p.dqkv = o + b0 * image_bytes;
     p.B = (int)nb;
-    p.units = (int)(nb * nW * heads);
+    p.windows = (int)(nb * nW);
     if (launch_bwd_bf16(M, p, dev, cus, st) != hipSuccess) return SWIN_ERR_HIP;
   }
   return SWIN_OK;

@@ -11,6 +11,10 @@
 //   unit      (image, window, head): q, k, v and dO of the head, each 16-token
 //             tile a 1 KB LDS block (16 tokens x 64 B), staged like the
 //             forward's (register prefetch of the next unit).
+//   streams   a workgroup keeps one head and walks a contiguous run of
+//             windows; the nh workgroups of one run (its nh heads) sit on
+//             one XCD and walk it in step, so the 128-byte lines that hold
+//             two heads of a token are fetched into one L2.
 //   phase 1   one wave per query tile, in the forward's transposed layout
 //             (keys in a lane's accumulator rows, queries across lanes):
 //             S^T and P (fp32, exact softmax), dP^T = V dO^T, D, dS^T, and
@@ -20,9 +24,12 @@
 //             keys across lanes): per query tile S, P = exp2(S - L), dP,
 //             dS; dV^T += dO^T P and dK^T += Q^T dS on 16x16x16 MFMAs (the C
 //             layout of P and dS is their B operand; dO^T and Q^T come from
-//             transposing reads); dS goes to an LDS copy of the bias
-//             gradient with LDS atomics, flushed to HBM with global atomics
-//             when the workgroup ends.
+//             transposing reads).
+//   bias grad the (query, key) pair of an accumulator slot of a lane is the
+//             same in every window, hence so is its table row: each lane
+//             sums dS in 16 registers over all its workgroup's windows (one
+//             head), then adds them once into an LDS copy of the head's table
+//             gradient (LDS atomics), which goes to HBM with global atomics.
 //   output    dQ, dK, dV of a token leave as 16-byte stores of 8 channels.
 
 #include <atomic>
@@ -66,19 +73,20 @@ SWA_INLINE unsigned bwd_pixel(const BwdParams& p, int M, int b, int wy, int wx, 
   return ((unsigned)b * p.H + y) * p.W + x;
 }
 
-// bias table -> LDS in plain order (divided by the score scale), then a
-// zero tail that padded queries may read
+// bias table of head h -> LDS, divided by the score scale: reversed (rows
+// T-1 .. 0, then a zero tail that padded keys may read) and in plain order
 template <int M>
-SWA_INLINE void stage_bias_plain(float* s, const float* table, int nh, float inv_scale) {
+SWA_INLINE void stage_head_tables(float* s_rev, float* s_fwd, const float* table, int nh, int h,
+                                  float inv_scale) {
   using S = Win<M>;
-  const int n = nh * S::T;
-  for (int e = threadIdx.x; e < n + S::TAIL; e += blockDim.x) {
-    float v = 0.f;
-    if (e < n) {
-      const int h = e / S::T, k = e - h * S::T;
-      v = table[k * nh + h] * inv_scale;
+  for (int e = threadIdx.x; e < S::T + S::TAIL; e += blockDim.x) {
+    float v = 0.f, f = 0.f;
+    if (e < S::T) {
+      v = table[(S::T - 1 - e) * nh + h] * inv_scale;
+      f = table[e * nh + h] * inv_scale;
     }
-    s[e] = v;
+    s_rev[e] = v;
+    s_fwd[e] = f;
   }
 }
 
@@ -91,10 +99,10 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
   constexpr int SLICES = 4;  // q, k, v, dO
   extern __shared__ float s_lds[];
   const int nh = p.nh;
-  const int off_l2 = (3 * nh * T + 2 * S::TAIL + 3) & ~3;  // 16-byte aligned
+  constexpr int off_l2 = (3 * T + 2 * S::TAIL + 3) & ~3;  // 16-byte aligned
   float* s_brev = s_lds;                        // reversed table / scale (phase 1)
-  float* s_bfwd = s_brev + nh * T + S::TAIL;    // plain table / scale (phase 2)
-  float* s_dtab = s_bfwd + nh * T + S::TAIL;    // bias gradient of this workgroup [nh][T]
+  float* s_bfwd = s_brev + T + S::TAIL;         // plain table / scale (phase 2)
+  float* s_dtab = s_bfwd + T + S::TAIL;         // bias gradient of this workgroup's head [T]
   float* s_l2 = s_lds + off_l2;                 // [64] log2-sum-exp of the queries
   float* s_dd = s_l2 + 64;                      // [64] D of the queries
   char* s_unit = reinterpret_cast<char*>(s_dd + 64);  // 4 slices x NT blocks of 1 KB
@@ -110,18 +118,32 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
   char* dout3 = static_cast<char*>(p.dqkv);
   const float scale = p.scale;
 
-  stage_bias<M>(s_brev, p.table, nh, p.inv_scale);
-  stage_bias_plain<M>(s_bfwd, p.table, nh, p.inv_scale);
-  for (int e = tid; e < nh * T; e += blockDim.x) s_dtab[e] = 0.f;
+  // this workgroup's head and run of windows: workgroup id -> (XCD x, slot
+  // k); the nh heads of run 8 (k / nh) + x are slots nh (k / nh) .. + nh-1
+  // of XCD x (workgroups are dealt to the XCDs round-robin)
+  int head, run;
+  const int id = blockIdx.x;
+  if (p.xcd_streams) {
+    const int k = id >> 3;
+    head = k % nh;
+    run = (k / nh) * 8 + (id & 7);
+  } else {
+    head = id % nh;
+    run = id / nh;
+  }
+  const int runs = gridDim.x / nh;
+  const int w_lo = (int)((long long)run * p.windows / runs);
+  const int w_hi = (int)((long long)(run + 1) * p.windows / runs);
 
-  // units: (image, window, head), in grid order
+  stage_head_tables<M>(s_brev, s_bfwd, p.table, nh, head, p.inv_scale);
+  for (int e = tid; e < T; e += blockDim.x) s_dtab[e] = 0.f;
+
   struct Pos {
     int h, b, wy, wx;
   };
-  auto decode = [&](int uu) {
+  auto decode = [&](int bw) {
     Pos q;
-    q.h = uu % nh;
-    const int bw = uu / nh;
+    q.h = head;
     q.b = bw / p.nW;
     const int w = bw - q.b * p.nW;
     q.wy = w / p.nWx;
@@ -194,7 +216,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
     int ty, tx;
     btile_token<M>(it, c, ty, tx);
     const bool ok = ty < M && tx < M;
-    const int qbase = h * T + T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
+    const int qbase = T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
     const bf16x8 q = tok16(0, it), go = tok16(3, it);
     bf16x8 mq = {};
     if (masked) mq = mask_query(local_label(pos.wy * M + ty, pos.wx * M + tx));
@@ -288,14 +310,18 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
   };
 
   // ---- phase 2: key tile jk = wv ------------------------------------------
+  // key token of this lane and the table row of its slot (iq, r) less E(iq) + r
+  int ky, kx;
+  btile_token<M>(wv < NT ? wv : 0, c, ky, kx);
+  const bool kok = ky < M && kx < M;
+  const int kbase = S::C0 + S::D * g - (kok ? S::D * ky + kx : 0);
+  f32x4 dta[NT];  // dS of each slot summed over the windows
+#pragma unroll
+  for (int iq = 0; iq < NT; ++iq) dta[iq] = z;
   auto phase2 = [&](const Pos& pos, bool masked) {
     const int jk = wv;
     if (jk >= NT) return;
     const int h = pos.h;
-    int ky, kx;
-    btile_token<M>(jk, c, ky, kx);
-    const bool kok = ky < M && kx < M;
-    const int kbase = h * T + S::C0 + S::D * g - (kok ? S::D * ky + kx : 0);
     const bf16x8 kb = tok16(1, jk), vb = tok16(2, jk);
     bf16x8 mk = {};
     if (masked) mk = mask_key(local_label(pos.wy * M + ky, pos.wx * M + kx));
@@ -330,7 +356,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
         const float ds = pv * (dpq[r] - dd[r]);
         pb[r] = (__bf16)pv;
         sb[r] = (__bf16)ds;
-        if (S::col_ok(iq, r) && row_ok && kok) atomicAdd(&s_dtab[kbase + S::E(iq) + r], ds);
+        dta[iq][r] += ds;  // zero for padded queries and keys (P = 0)
       }
       dv0 = mfma16(tile_t(3, iq, 0), pb, dv0);
       dv1 = mfma16(tile_t(3, iq, 1), pb, dv1);
@@ -345,20 +371,18 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
     }
   };
 
-  // persistent walk over the units in grid order, the next unit's loads in
-  // flight while a unit is computed
-  int u = blockIdx.x;
-  const int u_step = gridDim.x;
+  // walk over the run's windows, the next window's loads in flight while a
+  // window is computed
   Regs R;
-  Pos nxt = decode(u);
-  if (u < p.units) issue(R, nxt);
+  Pos nxt = decode(w_lo);
+  if (w_lo < w_hi) issue(R, nxt);
   __syncthreads();  // tables staged
-  for (; u < p.units; u += u_step) {
+  for (int bw = w_lo; bw < w_hi; ++bw) {
     write(R);
     __syncthreads();  // unit visible to every wave
     const Pos cur = nxt;
-    if (u + u_step < p.units) {
-      nxt = decode(u + u_step);
+    if (bw + 1 < w_hi) {
+      nxt = decode(bw + 1);
       issue(R, nxt);
     }
     const bool masked = window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx);
@@ -367,19 +391,26 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
     phase2(cur, masked);
     __syncthreads();  // every wave is done with the unit before it is overwritten
   }
-  // this workgroup's bias gradient -> HBM
-  for (int e = tid; e < nh * T; e += blockDim.x) {
-    const int h = e / T, k = e - h * T;
+  // this workgroup's bias gradient -> LDS -> HBM
+  if (wv < NT && kok) {
+#pragma unroll
+    for (int iq = 0; iq < NT; ++iq)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (S::col_ok(iq, r) && (S::rows_all(iq) || g_ok))
+          atomicAdd(&s_dtab[kbase + S::E(iq) + r], dta[iq][r]);
+  }
+  __syncthreads();
+  for (int e = tid; e < T; e += blockDim.x) {
     const float v = s_dtab[e];
-    if (v != 0.f) atomicAdd(p.dtable + k * nh + h, v);
+    if (v != 0.f) atomicAdd(p.dtable + e * nh + head, v);
   }
 }
 
 template <int M>
-size_t bwd_lds_m(int nh) {
+size_t bwd_lds_m() {
   using S = Win<M>;
-  return ((size_t)((3 * nh * S::T + 2 * S::TAIL + 3) & ~3) + 128) * sizeof(float) +
-         4 * S::NT * 1024;
+  return ((size_t)((3 * S::T + 2 * S::TAIL + 3) & ~3) + 128) * sizeof(float) + 4 * S::NT * 1024;
 }
 
 template <int M>
@@ -400,11 +431,21 @@ int bwd_blocks_per_cu(int dev, size_t lds) {
   return per_cu;
 }
 
+// Grid: nh workgroups (one per head) per run of windows, as many runs as
+// the chip holds at the kernel's occupancy (at most one per window); with 8
+// runs or more, a multiple of 8 runs, laid out per XCD.
 template <int M>
-hipError_t launch_bwd_m(const BwdParams& p, int dev, int cus, hipStream_t st) {
-  const size_t lds = bwd_lds_m<M>(p.nh);
-  long long grid = (long long)cus * bwd_blocks_per_cu<M>(dev, lds);
-  if (grid > p.units) grid = p.units;
+hipError_t launch_bwd_m(const BwdParams& p_in, int dev, int cus, hipStream_t st) {
+  BwdParams p = p_in;
+  const size_t lds = bwd_lds_m<M>();
+  const long long slots = (long long)cus * bwd_blocks_per_cu<M>(dev, lds);
+  long long runs = slots / p.nh;
+  if (runs > p.windows) runs = p.windows;
+  if (runs < 1) runs = 1;
+  p.xcd_streams = runs >= 8 ? 1 : 0;
+  if (p.xcd_streams) runs -= runs % 8;
+  const long long grid = runs * p.nh;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(wattn_bwd_bf16_kernel<M>, dim3((unsigned)grid), dim3(kBwdWaves * 64), lds, st,
                      p);
   return hipGetLastError();
@@ -418,16 +459,16 @@ __global__ void fill_kernel(float* dst, long long n, float v) {
 
 }  // namespace
 
-size_t bwd_lds_bytes(int M, int nh) {
+size_t bwd_lds_bytes(int M) {
   switch (M) {
-    case 1: return bwd_lds_m<1>(nh);
-    case 2: return bwd_lds_m<2>(nh);
-    case 3: return bwd_lds_m<3>(nh);
-    case 4: return bwd_lds_m<4>(nh);
-    case 5: return bwd_lds_m<5>(nh);
-    case 6: return bwd_lds_m<6>(nh);
-    case 7: return bwd_lds_m<7>(nh);
-    case 8: return bwd_lds_m<8>(nh);
+    case 1: return bwd_lds_m<1>();
+    case 2: return bwd_lds_m<2>();
+    case 3: return bwd_lds_m<3>();
+    case 4: return bwd_lds_m<4>();
+    case 5: return bwd_lds_m<5>();
+    case 6: return bwd_lds_m<6>();
+    case 7: return bwd_lds_m<7>();
+    case 8: return bwd_lds_m<8>();
     default: return 0;
   }
 }

@@ -91,13 +91,14 @@ struct BwdParams {
   float* dtable;       // [(2M-1)^2][nh], accumulated with atomics (zeroed by the host)
   int B, H, W, nh, shift;
   int nWy, nWx, nW;
-  int units;           // B * nW * nh
+  int windows;         // B * nW
+  int xcd_streams;     // grid is a multiple of 8 * nh: streams laid out per XCD
   float scale;         // 1 / sqrt(head_dim)
   float score_scale;   // log2(e) / sqrt(head_dim)
   float inv_scale;     // sqrt(head_dim)
   float mask_pieces[3];
 };
-size_t bwd_lds_bytes(int M, int nh);
+size_t bwd_lds_bytes(int M);
 hipError_t launch_bwd_bf16(int M, const BwdParams& p, int dev, int cus, hipStream_t stream);
 hipError_t launch_fill(float* dst, long long n, float v, hipStream_t stream);
 

@@ -78,6 +78,8 @@ def _check(qkv, table, dout, M, s, what):
     (1, 6, 9, 2, 3, 1),       # window 3: one padded tile
     (1, 4, 4, 1, 2, 1),
     (1, 3, 5, 2, 1, 0),       # window 1: the output is v, so dv = dout, dq = dk = 0
+    (1, 7, 14, 48, 7, 3),     # 48 heads, two windows: one window per run
+    (3, 14, 14, 5, 7, 3),     # 12 windows, 5 heads: uneven runs
 ])
 def test_backward_matches_oracle(B, H, W, nh, M, s):
     _say(f"bwd B={B} H={H} W={W} nh={nh} M={M} s={s}")
