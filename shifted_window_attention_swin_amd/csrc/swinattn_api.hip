@@ -331,6 +331,7 @@ int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dou
     p.dqkv = o + b0 * image_bytes;
     p.B = (int)nb;
     p.windows = (int)(nb * nW);
+    p.dqkv_bytes = (unsigned)(nb * image_bytes);
     if (launch_bwd_bf16(M, p, dev, cus, st) != hipSuccess) return SWIN_ERR_HIP;
   }
   return SWIN_OK;

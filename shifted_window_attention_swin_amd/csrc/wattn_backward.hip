@@ -19,17 +19,18 @@
 //             (keys in a lane's accumulator rows, queries across lanes):
 //             S^T and P (fp32, exact softmax), dP^T = V dO^T, D, dS^T, and
 //             dQ^T = K^T dS^T (K^T from transposing LDS reads, as the
-//             forward's V^T); log2-sum-exp and D of every query go to LDS.
-//   phase 2   one wave per key tile, in the plain layout (queries in rows,
-//             keys across lanes): per query tile S, P = exp2(S - L), dP,
-//             dS; dV^T += dO^T P and dK^T += Q^T dS on 16x16x16 MFMAs (the C
-//             layout of P and dS is their B operand; dO^T and Q^T come from
-//             transposing reads).
-//   bias grad the (query, key) pair of an accumulator slot of a lane is the
-//             same in every window, hence so is its table row: each lane
-//             sums dS in 16 registers over all its workgroup's windows (one
-//             head), then adds them once into an LDS copy of the head's table
-//             gradient (LDS atomics), which goes to HBM with global atomics.
+//             forward's V^T).  P and dS go to LDS in bf16 as 16 x 16 blocks
+//             [query][key], one per (query tile, key tile).
+//   phase 2   one wave per key tile: dV^T += dO^T P and dK^T += Q^T dS on
+//             16x16x16 MFMAs, their B operands read out of the P and dS
+//             blocks with transposing LDS reads (4 queries of a key per
+//             lane), dO^T and Q^T from transposing reads of the unit.
+//   bias grad the (query, key) pair of a phase-1 accumulator slot of a lane
+//             is the same in every window, hence so is its table row: each
+//             lane sums the fp32 dS of its 16 slots in registers over all its
+//             workgroup's windows (one head), then adds them once into an
+//             LDS copy of the head's table gradient (LDS atomics), which goes
+//             to HBM with global atomics.
 //   output    dQ, dK, dV of a token leave as 16-byte stores of 8 channels.
 
 #include <atomic>
@@ -73,50 +74,64 @@ SWA_INLINE unsigned bwd_pixel(const BwdParams& p, int M, int b, int wy, int wx, 
   return ((unsigned)b * p.H + y) * p.W + x;
 }
 
-// bias table of head h -> LDS, divided by the score scale: reversed (rows
-// T-1 .. 0, then a zero tail that padded keys may read) and in plain order
+// bias table of head h -> LDS, divided by the score scale and reversed
+// (rows T-1 .. 0), then a zero tail that padded keys may read
 template <int M>
-SWA_INLINE void stage_head_tables(float* s_rev, float* s_fwd, const float* table, int nh, int h,
-                                  float inv_scale) {
+SWA_INLINE void stage_head_table(float* s_rev, const float* table, int nh, int h,
+                                 float inv_scale) {
   using S = Win<M>;
-  for (int e = threadIdx.x; e < S::T + S::TAIL; e += blockDim.x) {
-    float v = 0.f, f = 0.f;
-    if (e < S::T) {
-      v = table[(S::T - 1 - e) * nh + h] * inv_scale;
-      f = table[e * nh + h] * inv_scale;
-    }
-    s_rev[e] = v;
-    s_fwd[e] = f;
-  }
+  for (int e = threadIdx.x; e < S::T + S::TAIL; e += blockDim.x)
+    s_rev[e] = e < S::T ? table[(S::T - 1 - e) * nh + h] * inv_scale : 0.f;
 }
+
+template <int M>
+struct BwdLds {
+  using S = Win<M>;
+  static constexpr int UNIT = 4 * S::NT * 1024;           // q, k, v, dO tiles
+  static constexpr int PBLK = 512;                         // 16 x 16 bf16
+  static constexpr int OFF_UNIT = ((2 * S::T + S::TAIL) * 4 + 15) / 16 * 16;
+  static constexpr int OFF_P = OFF_UNIT + UNIT;
+  static constexpr int OFF_DS = OFF_P + S::NT * S::NT * PBLK;
+  static constexpr int BYTES = OFF_DS + S::NT * S::NT * PBLK;
+};
 
 template <int M>
 __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParams p) {
   using S = Win<M>;
+  using L = BwdLds<M>;
   constexpr int NT = S::NT, NK = S::NK, T = S::T;
-  static_assert(NT <= 4, "windows of up to 4 tiles");
+  static_assert(NT <= kBwdWaves, "one wave per tile");
   constexpr int BLOCK = 1024;
   constexpr int SLICES = 4;  // q, k, v, dO
   extern __shared__ float s_lds[];
   const int nh = p.nh;
-  constexpr int off_l2 = (3 * T + 2 * S::TAIL + 3) & ~3;  // 16-byte aligned
-  float* s_brev = s_lds;                        // reversed table / scale (phase 1)
-  float* s_bfwd = s_brev + T + S::TAIL;         // plain table / scale (phase 2)
-  float* s_dtab = s_bfwd + T + S::TAIL;         // bias gradient of this workgroup's head [T]
-  float* s_l2 = s_lds + off_l2;                 // [64] log2-sum-exp of the queries
-  float* s_dd = s_l2 + 64;                      // [64] D of the queries
-  char* s_unit = reinterpret_cast<char*>(s_dd + 64);  // 4 slices x NT blocks of 1 KB
+  float* s_brev = s_lds;               // reversed table of the head / scale [T + TAIL]
+  float* s_dtab = s_brev + T + S::TAIL;  // bias gradient of the head [T]
+  char* s_base = reinterpret_cast<char*>(s_lds);
+  char* s_unit = s_base + L::OFF_UNIT;   // 4 slices x NT blocks of 1 KB
   auto block = [&](int sl, int t) { return s_unit + (sl * NT + t) * BLOCK; };
+  // P and dS of query tile iq and key tile jk: [query 16][key 16] bf16
+  auto pblock = [&](int off, int iq, int jk) { return s_base + off + (iq * NT + jk) * L::PBLK; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wv >= 0 && wv < kBwdWaves);
   const int gq = lane & 3, cq = lane >> 2;  // load layout: 16-byte part, token
   const int g = lane >> 4, c = lane & 15;   // MFMA layout: lane group, token
   const unsigned Cb = (unsigned)nh * kHeadDim * 2;  // bytes of one q (k, v, dO) row
   const char* in = static_cast<const char*>(p.qkv);
   const char* gin = static_cast<const char*>(p.dout);
-  char* dout3 = static_cast<char*>(p.dqkv);
   const float scale = p.scale;
+  // gradients leave through raw buffer stores that every lane issues: the
+  // lanes of padded tokens aim past the end of the buffer, where the
+  // hardware drops the write.  With no branch around the stores, the wait
+  // for the next window's loads does not also wait for them to complete.
+  const __amdgpu_buffer_rsrc_t out_rs =
+      __builtin_amdgcn_make_buffer_rsrc(p.dqkv, 0, (int)p.dqkv_bytes, 0x00020000);
+  auto store16 = [&](bool valid, unsigned off, const bf16x8& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), out_rs,
+                                           valid ? (int)off : (int)0xFFFFFFF0u, 0, 2 /* nt */);
+  };
 
   // this workgroup's head and run of windows: workgroup id -> (XCD x, slot
   // k); the nh heads of run 8 (k / nh) + x are slots nh (k / nh) .. + nh-1
@@ -135,15 +150,14 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
   const int w_lo = (int)((long long)run * p.windows / runs);
   const int w_hi = (int)((long long)(run + 1) * p.windows / runs);
 
-  stage_head_tables<M>(s_brev, s_bfwd, p.table, nh, head, p.inv_scale);
+  stage_head_table<M>(s_brev, p.table, nh, head, p.inv_scale);
   for (int e = tid; e < T; e += blockDim.x) s_dtab[e] = 0.f;
 
   struct Pos {
-    int h, b, wy, wx;
+    int b, wy, wx;
   };
   auto decode = [&](int bw) {
     Pos q;
-    q.h = head;
     q.b = bw / p.nW;
     const int w = bw - q.b * p.nW;
     q.wy = w / p.nWx;
@@ -158,10 +172,10 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
       btile_token<M>(wv, cq, ty, tx);
       const bool ok = ty < M && tx < M;
       const unsigned pix = bwd_pixel(p, M, q.b, q.wy, q.wx, ty, tx, ok);
-      const char* src = in + pix * (3u * Cb) + (unsigned)q.h * kHeadDim * 2 + 16u * gq;
+      const char* src = in + pix * (3u * Cb) + (unsigned)head * kHeadDim * 2 + 16u * gq;
 #pragma unroll
       for (int sl = 0; sl < 3; ++sl) R[sl] = *reinterpret_cast<const u32x4*>(src + sl * Cb);
-      R[3] = *reinterpret_cast<const u32x4*>(gin + pix * Cb + (unsigned)q.h * kHeadDim * 2 + 16u * gq);
+      R[3] = *reinterpret_cast<const u32x4*>(gin + pix * Cb + (unsigned)head * kHeadDim * 2 + 16u * gq);
     }
   };
   auto write = [&](const Regs& R) {
@@ -208,15 +222,21 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
     return o;
   };
 
+  // phase-1 lane geometry: query token c of tile wv; its slot (jt, r) is
+  // key token 4g + r of tile jt, table row rbase - E(jt) - r
+  int ty, tx;
+  btile_token<M>(wv < NT ? wv : 0, c, ty, tx);
+  const bool ok = ty < M && tx < M;
+  const int qbase = T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
+  const int rbase = T - 1 - qbase;
+  f32x4 dta[NT];  // fp32 dS of each slot summed over the windows
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) dta[jt] = z;
+
   // ---- phase 1: query tile it = wv -----------------------------------------
   auto phase1 = [&](const Pos& pos, bool masked) {
     const int it = wv;
     if (it >= NT) return;
-    const int h = pos.h;
-    int ty, tx;
-    btile_token<M>(it, c, ty, tx);
-    const bool ok = ty < M && tx < M;
-    const int qbase = T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
     const bf16x8 q = tok16(0, it), go = tok16(3, it);
     bf16x8 mq = {};
     if (masked) mq = mask_query(local_label(pos.wy * M + ty, pos.wx * M + tx));
@@ -264,7 +284,8 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
         sum += e;
       }
     sum = sum_groups(sum);
-    const float inv = fast_rcp(sum);
+    // padded queries: P = 0, so their dS, P and dQ vanish
+    const float inv = ok ? fast_rcp(sum) : 0.f;
     float dsum = 0.f;
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt)
@@ -274,16 +295,28 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
         dsum += sc[jt][r] * dp[jt][r];
       }
     const float Dq = sum_groups(dsum);
-    // dS^T = P o (dP^T - D), packed as the B operand of the key contraction
+    // dS^T = P o (dP^T - D): fp32 into the table sums; bf16 as the B
+    // operand of the key contraction and, with P, into the LDS blocks
     bf16x8 pb[NK];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
+    for (int jt = 0; jt < NT; ++jt) {
+      bf16x4 pt, st;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pb[kk][r] = (__bf16)(sc[2 * kk][r] * (dp[2 * kk][r] - Dq));
-        pb[kk][4 + r] = (2 * kk + 1 < NT) ? (__bf16)(sc[2 * kk + 1][r] * (dp[2 * kk + 1][r] - Dq))
-                                          : (__bf16)0.f;
+        const float ds = sc[jt][r] * (dp[jt][r] - Dq);
+        dta[jt][r] += ds;
+        st[r] = (__bf16)ds;
+        pt[r] = (__bf16)sc[jt][r];
+        pb[jt / 2][4 * (jt % 2) + r] = st[r];
       }
+      // P[query c][keys 4g .. 4g+3] of block (it, jt)
+      *reinterpret_cast<bf16x4*>(pblock(L::OFF_P, it, jt) + 32 * c + 8 * g) = pt;
+      *reinterpret_cast<bf16x4*>(pblock(L::OFF_DS, it, jt) + 32 * c + 8 * g) = st;
+    }
+    if constexpr (NT % 2 == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[NK - 1][4 + r] = (__bf16)0.f;
+    }
     // dQ^T = K^T dS^T, K^T from transposing reads (odd tile counts: any
     // finite data for the missing tile, its dS^T is zero)
     f32x4 o0 = z, o1 = z;
@@ -297,108 +330,66 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
       o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, pb[kk], o0, 0, 0, 0);
       o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, pb[kk], o1, 0, 0, 0);
     }
-    if (g == 0) {
-      s_l2[it * 16 + c] = ok ? m + __builtin_amdgcn_logf(sum) : 0.f;
-      s_dd[it * 16 + c] = ok ? Dq : 0.f;
-    }
-    if (ok) {
-      const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, ty, tx, true);
-      __builtin_nontemporal_store(
-          pack8(o0, o1, scale),
-          reinterpret_cast<bf16x8*>(dout3 + pix * (3u * Cb) + h * kHeadDim * 2 + 16 * g));
-    }
+    const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, ty, tx, ok);
+    store16(ok, pix * (3u * Cb) + head * kHeadDim * 2 + 16 * g, pack8(o0, o1, scale));
   };
 
   // ---- phase 2: key tile jk = wv ------------------------------------------
-  // key token of this lane and the table row of its slot (iq, r) less E(iq) + r
-  int ky, kx;
-  btile_token<M>(wv < NT ? wv : 0, c, ky, kx);
-  const bool kok = ky < M && kx < M;
-  const int kbase = S::C0 + S::D * g - (kok ? S::D * ky + kx : 0);
-  f32x4 dta[NT];  // dS of each slot summed over the windows
-#pragma unroll
-  for (int iq = 0; iq < NT; ++iq) dta[iq] = z;
-  auto phase2 = [&](const Pos& pos, bool masked) {
+  auto phase2 = [&](const Pos& pos) {
     const int jk = wv;
     if (jk >= NT) return;
-    const int h = pos.h;
-    const bf16x8 kb = tok16(1, jk), vb = tok16(2, jk);
-    bf16x8 mk = {};
-    if (masked) mk = mask_key(local_label(pos.wy * M + ky, pos.wx * M + kx));
     f32x4 dk0 = z, dk1 = z, dv0 = z, dv1 = z;
 #pragma unroll
     for (int iq = 0; iq < NT; ++iq) {
-      // rows 4g + r: query (4 (iq/Q) + g, 4 (iq%Q) + r)
-      const bool row_ok = S::rows_all(iq) || g_ok;
-      f32x4 acc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (!S::col_ok(iq, r) || !row_ok || !kok) {
-          acc[r] = -__builtin_inff();
-          continue;
-        }
-        acc[r] = s_bfwd[kbase + S::E(iq) + r];
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(0, iq), kb, acc, 0, 0, 0);
-      if (masked) {
-        int qy, qx;
-        btile_token<M>(iq, c, qy, qx);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            mask_query(local_label(pos.wy * M + qy, pos.wx * M + qx)), mk, acc, 0, 0, 0);
-      }
-      const f32x4 dpq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(3, iq), vb, z, 0, 0, 0);
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(s_l2 + iq * 16 + 4 * g);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(s_dd + iq * 16 + 4 * g);
-      bf16x4 pb, sb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = fast_exp2(fmaf(acc[r], p.score_scale, -l2[r]));
-        const float ds = pv * (dpq[r] - dd[r]);
-        pb[r] = (__bf16)pv;
-        sb[r] = (__bf16)ds;
-        dta[iq][r] += ds;  // zero for padded queries and keys (P = 0)
-      }
+      // element k of lane (g, c): P (dS) of query 4g + k of tile iq, key c
+      const bf16x4 pb = lds_read_tr(pblock(L::OFF_P, iq, jk) + 8 * lane);
+      const bf16x4 sb = lds_read_tr(pblock(L::OFF_DS, iq, jk) + 8 * lane);
       dv0 = mfma16(tile_t(3, iq, 0), pb, dv0);
       dv1 = mfma16(tile_t(3, iq, 1), pb, dv1);
       dk0 = mfma16(tile_t(0, iq, 0), sb, dk0);
       dk1 = mfma16(tile_t(0, iq, 1), sb, dk1);
     }
-    if (kok) {
-      const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, ky, kx, true);
-      char* dst = dout3 + pix * (3u * Cb) + h * kHeadDim * 2 + 16 * g;
-      __builtin_nontemporal_store(pack8(dk0, dk1, scale), reinterpret_cast<bf16x8*>(dst + Cb));
-      __builtin_nontemporal_store(pack8(dv0, dv1, 1.f), reinterpret_cast<bf16x8*>(dst + 2 * Cb));
-    }
+    int ky, kx;
+    btile_token<M>(jk, c, ky, kx);
+    const bool kok = ky < M && kx < M;
+    const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, ky, kx, kok);
+    const unsigned dst = pix * (3u * Cb) + head * kHeadDim * 2 + 16 * g;
+    store16(kok, dst + Cb, pack8(dk0, dk1, scale));
+    store16(kok, dst + 2 * Cb, pack8(dv0, dv1, 1.f));
   };
 
   // walk over the run's windows, the next window's loads in flight while a
-  // window is computed
+  // window is computed; they go to LDS at the end of the iteration, after
+  // the window's stores were issued
   Regs R;
   Pos nxt = decode(w_lo);
-  if (w_lo < w_hi) issue(R, nxt);
-  __syncthreads();  // tables staged
-  for (int bw = w_lo; bw < w_hi; ++bw) {
+  if (w_lo < w_hi) {
+    issue(R, nxt);
     write(R);
-    __syncthreads();  // unit visible to every wave
+  }
+  __syncthreads();  // table and first unit staged
+  for (int bw = w_lo; bw < w_hi; ++bw) {
     const Pos cur = nxt;
-    if (bw + 1 < w_hi) {
+    const bool more = bw + 1 < w_hi;
+    if (more) {
       nxt = decode(bw + 1);
       issue(R, nxt);
     }
-    const bool masked = window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx);
-    phase1(cur, masked);
-    __syncthreads();  // log2-sum-exp and D of every query visible
-    phase2(cur, masked);
+    phase1(cur, window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx));
+    __syncthreads();  // P and dS blocks visible
+    phase2(cur);
     __syncthreads();  // every wave is done with the unit before it is overwritten
+    write(R);         // after the last window: stale data, never read
+    __syncthreads();  // next unit visible to every wave
   }
   // this workgroup's bias gradient -> LDS -> HBM
-  if (wv < NT && kok) {
+  if (wv < NT && ok) {
 #pragma unroll
-    for (int iq = 0; iq < NT; ++iq)
+    for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (S::col_ok(iq, r) && (S::rows_all(iq) || g_ok))
-          atomicAdd(&s_dtab[kbase + S::E(iq) + r], dta[iq][r]);
+        if (S::col_ok(jt, r) && (S::rows_all(jt) || g_ok))
+          atomicAdd(&s_dtab[rbase - S::E(jt) - r], dta[jt][r]);
   }
   __syncthreads();
   for (int e = tid; e < T; e += blockDim.x) {
@@ -409,8 +400,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
 
 template <int M>
 size_t bwd_lds_m() {
-  using S = Win<M>;
-  return ((size_t)((3 * S::T + 2 * S::TAIL + 3) & ~3) + 128) * sizeof(float) + 4 * S::NT * 1024;
+  return BwdLds<M>::BYTES;
 }
 
 template <int M>

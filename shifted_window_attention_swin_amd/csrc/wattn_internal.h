@@ -93,6 +93,7 @@ struct BwdParams {
   int nWy, nWx, nW;
   int windows;         // B * nW
   int xcd_streams;     // grid is a multiple of 8 * nh: streams laid out per XCD
+  unsigned dqkv_bytes; // bytes of dqkv in this launch (at most 2^31)
   float scale;         // 1 / sqrt(head_dim)
   float score_scale;   // log2(e) / sqrt(head_dim)
   float inv_scale;     // sqrt(head_dim)
