@@ -37,8 +37,8 @@ CSRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc")
 # the sources that define each kernel family's device code
 KERNEL_SOURCES = {
     "wattn_fwd_bf16": ("wattn_internal.h", "wattn_common.h", "wattn_persistent.hip"),
-    "linear_fwd": ("wattn_internal.h", "wattn_common.h", "linear_gemm.hip"),
-    "wattn_bwd_bf16": ("wattn_internal.h", "wattn_common.h", "wattn_backward.hip"),
+    "linear_fwd": ("wattn_internal.h", "wattn_common.h", "linear_internal.h", "linear_gemm.hip"),
+    "wattn_bwd_bf16": ("wattn_internal.h", "wattn_common.h", "bwd_internal.h", "wattn_backward.hip"),
 }
 
 

@@ -39,6 +39,7 @@
 
 #include <atomic>
 
+#include "linear_internal.h"
 #include "wattn_common.h"
 
 namespace swinattn {

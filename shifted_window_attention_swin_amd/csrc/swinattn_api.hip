@@ -16,6 +16,8 @@
 #include <vector>
 
 #include "../../include/swinattn.h"
+#include "bwd_internal.h"
+#include "linear_internal.h"
 #include "wattn_internal.h"
 
 using namespace swinattn;

@@ -35,6 +35,7 @@
 
 #include <atomic>
 
+#include "bwd_internal.h"
 #include "wattn_common.h"
 
 namespace swinattn {

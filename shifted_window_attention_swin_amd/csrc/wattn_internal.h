@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI front (swinattn_api.hip) and the
-// kernels (wattn_kernels.hip).  Not installed, not part of the ABI.
+// forward attention kernels, and the limits the kernel families share.
+// Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,56 +52,5 @@ constexpr int kMaxPersistentWindow = 12;
 hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
                                       hipStream_t stream);
 size_t persistent_lds_bytes(int M, int HG, int nh);
-
-// Linear layer y = x W^T + bias (+ residual), bf16 in and out, fp32 bias
-// (linear_gemm.hip).  K and N are multiples of 32, K <= kMaxLinearK.
-constexpr int kMaxLinearK = 384;
-constexpr long long kMaxLinearTokens = 1LL << 30;  // tokens per launch (32-bit indices)
-struct LinearParams {
-  const void* x;      // [T][K] bf16
-  const void* wp;     // packed weight [N/32][K/32][2][64][8] bf16
-  const float* bias;  // [N] or null
-  const void* res;    // [T][N] bf16 or null
-  const float* colsum;  // layer norm: [N] row sums of the packed weight, or null
-  float eps;            // layer norm epsilon
-  void* y;            // [T][N] bf16
-  long long T;
-  int K, N;
-  int ncb;     // N / 32 column blocks
-  int ncg;     // column groups, one per workgroup (set by launch_linear)
-  int blocks;  // row blocks (set by launch_linear)
-};
-size_t linear_lds_bytes(int K, int N);
-// gamma null: plain packing; else the packed weight is gamma o W.
-hipError_t launch_linear_pack(const void* w, const float* gamma, void* wp, int N, int K,
-                              hipStream_t stream);
-// consts [2][N]: row sums of gamma o W (as packed), bias + W beta.
-hipError_t launch_linear_ln_consts(const void* w, const float* gamma, const float* beta,
-                                  const float* bias, float* consts, int N, int K,
-                                  hipStream_t stream);
-hipError_t launch_linear(const LinearParams& p, int dev, int cus, hipStream_t stream);
-
-// Backward of the window attention, bf16 (wattn_backward.hip); windows up
-// to kMaxBwdWindow.
-constexpr int kMaxBwdWindow = 8;
-struct BwdParams {
-  const void* qkv;     // [B][H][W][3][nh][32] of this launch's images
-  const float* table;  // [(2M-1)^2][nh]
-  const void* dout;    // [B][H][W][nh*32]
-  void* dqkv;          // [B][H][W][3][nh][32]
-  float* dtable;       // [(2M-1)^2][nh], accumulated with atomics (zeroed by the host)
-  int B, H, W, nh, shift;
-  int nWy, nWx, nW;
-  int windows;         // B * nW
-  int xcd_streams;     // grid is a multiple of 8 * nh: streams laid out per XCD
-  unsigned dqkv_bytes; // bytes of dqkv in this launch (at most 2^31)
-  float scale;         // 1 / sqrt(head_dim)
-  float score_scale;   // log2(e) / sqrt(head_dim)
-  float inv_scale;     // sqrt(head_dim)
-  float mask_pieces[3];
-};
-size_t bwd_lds_bytes(int M);
-hipError_t launch_bwd_bf16(int M, const BwdParams& p, int dev, int cus, hipStream_t stream);
-hipError_t launch_fill(float* dst, long long n, float v, hipStream_t stream);
 
 }  // namespace swinattn
