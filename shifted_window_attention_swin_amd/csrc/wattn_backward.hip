@@ -75,50 +75,56 @@ SWA_INLINE unsigned bwd_pixel(const BwdParams& p, int M, int b, int wy, int wx, 
   return ((unsigned)b * p.H + y) * p.W + x;
 }
 
-// bias table of head h -> LDS, divided by the score scale and reversed
-// (rows T-1 .. 0), then a zero tail that padded keys may read
-template <int M>
-SWA_INLINE void stage_head_table(float* s_rev, const float* table, int nh, int h,
-                                 float inv_scale) {
-  using S = Win<M>;
-  for (int e = threadIdx.x; e < S::T + S::TAIL; e += blockDim.x)
-    s_rev[e] = e < S::T ? table[(S::T - 1 - e) * nh + h] * inv_scale : 0.f;
-}
-
-template <int M>
+template <int M, int HP>
 struct BwdLds {
   using S = Win<M>;
-  static constexpr int UNIT = 4 * S::NT * 1024;           // q, k, v, dO tiles
-  static constexpr int PBLK = 512;                         // 16 x 16 bf16
-  static constexpr int OFF_UNIT = ((2 * S::T + S::TAIL) * 4 + 15) / 16 * 16;
-  static constexpr int OFF_P = OFF_UNIT + UNIT;
-  static constexpr int OFF_DS = OFF_P + S::NT * S::NT * PBLK;
-  static constexpr int BYTES = OFF_DS + S::NT * S::NT * PBLK;
+  static constexpr int TAB = S::T + S::TAIL;    // floats of one head's reversed table
+  static constexpr int UNIT = 4 * S::NT * 1024;  // q, k, v, dO tiles of one head
+  static constexpr int PBLK = 512;               // 16 x 16 bf16
+  static constexpr int PHEAD = S::NT * S::NT * PBLK;  // P (or dS) blocks of one head
+  static constexpr int OFF_UNIT = ((HP * TAB + HP * S::T) * 4 + 15) / 16 * 16;
+  static constexpr int OFF_P = OFF_UNIT + HP * UNIT;
+  static constexpr int OFF_DS = OFF_P + HP * PHEAD;
+  static constexpr int BYTES = OFF_DS + HP * PHEAD;
 };
 
-template <int M>
-__global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParams p) {
+// HP = 1: a workgroup of 4 waves keeps one head.  HP = 2: 8 waves keep the
+// pair of heads (2k, 2k+1) whose 64-byte rows share the 128-byte lines of
+// a token, wave 4 hl + t on tile t of head 2k + hl, and the gradients of both
+// heads leave through LDS tiles [tile][16 tokens][128 B] so that every store
+// instruction writes whole lines (8 tokens x 128 B): dQ through the k tiles
+// (free once the query phase is done), dK and dV through the P and dS blocks
+// (free once the key phase is done).
+template <int M, int HP>
+__global__ __launch_bounds__(kBwdWaves * 64 * HP) void wattn_bwd_bf16_kernel(BwdParams p) {
   using S = Win<M>;
-  using L = BwdLds<M>;
+  using L = BwdLds<M, HP>;
   constexpr int NT = S::NT, NK = S::NK, T = S::T;
   static_assert(NT <= kBwdWaves, "one wave per tile");
+  static_assert(HP == 1 || (HP == 2 && NT == kBwdWaves), "head pairs for 4-tile windows");
   constexpr int BLOCK = 1024;
   constexpr int SLICES = 4;  // q, k, v, dO
   extern __shared__ float s_lds[];
   const int nh = p.nh;
-  float* s_brev = s_lds;               // reversed table of the head / scale [T + TAIL]
-  float* s_dtab = s_brev + T + S::TAIL;  // bias gradient of the head [T]
-  char* s_base = reinterpret_cast<char*>(s_lds);
-  char* s_unit = s_base + L::OFF_UNIT;   // 4 slices x NT blocks of 1 KB
-  auto block = [&](int sl, int t) { return s_unit + (sl * NT + t) * BLOCK; };
-  // P and dS of query tile iq and key tile jk: [query 16][key 16] bf16
-  auto pblock = [&](int off, int iq, int jk) { return s_base + off + (iq * NT + jk) * L::PBLK; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __builtin_assume(wv >= 0 && wv < kBwdWaves);
+  __builtin_assume(wv >= 0 && wv < kBwdWaves * HP);
+  const int hl = wv / kBwdWaves;  // head of the wave within the workgroup
+  const int tw = wv % kBwdWaves;  // tile of the wave
   const int gq = lane & 3, cq = lane >> 2;  // load layout: 16-byte part, token
   const int g = lane >> 4, c = lane & 15;   // MFMA layout: lane group, token
+
+  float* s_brev = s_lds + hl * L::TAB;      // reversed table of the wave's head / scale
+  float* s_dtab = s_lds + HP * L::TAB;      // bias gradients of the heads [HP][T]
+  char* s_base = reinterpret_cast<char*>(s_lds);
+  char* s_unit = s_base + L::OFF_UNIT;      // [slice][head][tile] blocks of 1 KB
+  auto block = [&](int sl, int t) { return s_unit + ((sl * HP + hl) * NT + t) * BLOCK; };
+  // P and dS of the wave's head, query tile iq and key tile jk: [query 16][key 16] bf16
+  auto pblock = [&](int off, int iq, int jk) {
+    return s_base + off + hl * L::PHEAD + (iq * NT + jk) * L::PBLK;
+  };
+
   const unsigned Cb = (unsigned)nh * kHeadDim * 2;  // bytes of one q (k, v, dO) row
   const char* in = static_cast<const char*>(p.qkv);
   const char* gin = static_cast<const char*>(p.dout);
@@ -134,25 +140,32 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
                                            valid ? (int)off : (int)0xFFFFFFF0u, 0, 2 /* nt */);
   };
 
-  // this workgroup's head and run of windows: workgroup id -> (XCD x, slot
-  // k); the nh heads of run 8 (k / nh) + x are slots nh (k / nh) .. + nh-1
-  // of XCD x (workgroups are dealt to the XCDs round-robin)
-  int head, run;
+  // this workgroup's heads and run of windows: workgroup id -> (XCD x, slot
+  // k); the nh/HP head groups of run 8 (k / groups) + x are slots
+  // groups (k / groups) .. + groups-1 of XCD x (workgroups are dealt to the
+  // XCDs round-robin)
+  const int groups = nh / HP;
+  int grp, run;
   const int id = blockIdx.x;
   if (p.xcd_streams) {
     const int k = id >> 3;
-    head = k % nh;
-    run = (k / nh) * 8 + (id & 7);
+    grp = k % groups;
+    run = (k / groups) * 8 + (id & 7);
   } else {
-    head = id % nh;
-    run = id / nh;
+    grp = id % groups;
+    run = id / groups;
   }
-  const int runs = gridDim.x / nh;
+  const int h0 = grp * HP;       // first head of the workgroup
+  const int head = h0 + hl;      // head of the wave
+  const int runs = gridDim.x / groups;
   const int w_lo = (int)((long long)run * p.windows / runs);
   const int w_hi = (int)((long long)(run + 1) * p.windows / runs);
 
-  stage_head_table<M>(s_brev, p.table, nh, head, p.inv_scale);
-  for (int e = tid; e < T; e += blockDim.x) s_dtab[e] = 0.f;
+  for (int e = tid; e < HP * L::TAB; e += blockDim.x) {
+    const int eh = e / L::TAB, k = e - eh * L::TAB;
+    s_lds[e] = k < T ? p.table[(T - 1 - k) * nh + h0 + eh] * p.inv_scale : 0.f;
+  }
+  for (int e = tid; e < HP * T; e += blockDim.x) s_dtab[e] = 0.f;
 
   struct Pos {
     int b, wy, wx;
@@ -165,25 +178,26 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
     q.wx = w - q.wy * p.nWx;
     return q;
   };
-  // tile wv of each slice: one token address per lane
+  // tile tw of each slice of the wave's head: one token address per lane
   using Regs = u32x4[SLICES];
   auto issue = [&](Regs& R, const Pos& q) {
-    if (wv < NT) {
-      int ty, tx;
-      btile_token<M>(wv, cq, ty, tx);
-      const bool ok = ty < M && tx < M;
-      const unsigned pix = bwd_pixel(p, M, q.b, q.wy, q.wx, ty, tx, ok);
-      const char* src = in + pix * (3u * Cb) + (unsigned)head * kHeadDim * 2 + 16u * gq;
+    if (tw < NT) {
+      int uy, ux;
+      btile_token<M>(tw, cq, uy, ux);
+      const bool uok = uy < M && ux < M;
+      const unsigned pix = bwd_pixel(p, M, q.b, q.wy, q.wx, uy, ux, uok);
+      const unsigned hoff = (unsigned)head * kHeadDim * 2 + 16u * gq;
+      const char* src = in + pix * (3u * Cb) + hoff;
 #pragma unroll
       for (int sl = 0; sl < 3; ++sl) R[sl] = *reinterpret_cast<const u32x4*>(src + sl * Cb);
-      R[3] = *reinterpret_cast<const u32x4*>(gin + pix * Cb + (unsigned)head * kHeadDim * 2 + 16u * gq);
+      R[3] = *reinterpret_cast<const u32x4*>(gin + pix * Cb + hoff);
     }
   };
   auto write = [&](const Regs& R) {
-    if (wv < NT) {
+    if (tw < NT) {
 #pragma unroll
       for (int sl = 0; sl < SLICES; ++sl)
-        *reinterpret_cast<u32x4*>(block(sl, wv) + lane * 16) = R[sl];
+        *reinterpret_cast<u32x4*>(block(sl, tw) + lane * 16) = R[sl];
     }
   };
   const bool g_ok = g < S::LG;
@@ -222,11 +236,28 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
     }
     return o;
   };
+  // head pairs: gradient tile of tile t in LDS ([16 tokens][128 B], this
+  // head's half at 64 hl), written by both heads' waves of tile t
+  auto stage_put = [&](char* st, const bf16x8& v) {
+    *reinterpret_cast<bf16x8*>(st + c * 128 + 64 * hl + 16 * g) = v;
+  };
+  // ... and read back by this wave as whole lines: tokens 8 hl .. 8 hl + 7
+  // of tile t, 8 lanes per token, to the slice at byte offset `slice` of a
+  // token row
+  auto stage_store = [&](const char* st, const Pos& pos, unsigned slice) {
+    const int u = 8 * hl + (lane >> 3);
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + u * 128 + 16 * (lane & 7));
+    int uy, ux;
+    btile_token<M>(tw, u, uy, ux);
+    const bool uok = uy < M && ux < M;
+    const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, uy, ux, uok);
+    store16(uok, pix * (3u * Cb) + slice + (unsigned)h0 * kHeadDim * 2 + 16 * (lane & 7), v);
+  };
 
-  // phase-1 lane geometry: query token c of tile wv; its slot (jt, r) is
+  // phase-1 lane geometry: query token c of tile tw; its slot (jt, r) is
   // key token 4g + r of tile jt, table row rbase - E(jt) - r
   int ty, tx;
-  btile_token<M>(wv < NT ? wv : 0, c, ty, tx);
+  btile_token<M>(tw < NT ? tw : 0, c, ty, tx);
   const bool ok = ty < M && tx < M;
   const int qbase = T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
   const int rbase = T - 1 - qbase;
@@ -234,10 +265,9 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) dta[jt] = z;
 
-  // ---- phase 1: query tile it = wv -----------------------------------------
-  auto phase1 = [&](const Pos& pos, bool masked) {
-    const int it = wv;
-    if (it >= NT) return;
+  // ---- phase 1: query tile it = tw; returns the lane's dQ ------------------
+  auto phase1 = [&](const Pos& pos, bool masked) -> bf16x8 {
+    const int it = tw;
     const bf16x8 q = tok16(0, it), go = tok16(3, it);
     bf16x8 mq = {};
     if (masked) mq = mask_query(local_label(pos.wy * M + ty, pos.wx * M + tx));
@@ -331,14 +361,12 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
       o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, pb[kk], o0, 0, 0, 0);
       o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, pb[kk], o1, 0, 0, 0);
     }
-    const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, ty, tx, ok);
-    store16(ok, pix * (3u * Cb) + head * kHeadDim * 2 + 16 * g, pack8(o0, o1, scale));
+    return pack8(o0, o1, scale);
   };
 
-  // ---- phase 2: key tile jk = wv ------------------------------------------
-  auto phase2 = [&](const Pos& pos) {
-    const int jk = wv;
-    if (jk >= NT) return;
+  // ---- phase 2: key tile jk = tw; dK and dV of the lane's key -----------------
+  auto phase2 = [&](bf16x8& dk, bf16x8& dv) {
+    const int jk = tw;
     f32x4 dk0 = z, dk1 = z, dv0 = z, dv1 = z;
 #pragma unroll
     for (int iq = 0; iq < NT; ++iq) {
@@ -350,61 +378,80 @@ __global__ __launch_bounds__(kBwdWaves * 64) void wattn_bwd_bf16_kernel(BwdParam
       dk0 = mfma16(tile_t(0, iq, 0), sb, dk0);
       dk1 = mfma16(tile_t(0, iq, 1), sb, dk1);
     }
-    int ky, kx;
-    btile_token<M>(jk, c, ky, kx);
-    const bool kok = ky < M && kx < M;
-    const unsigned pix = bwd_pixel(p, M, pos.b, pos.wy, pos.wx, ky, kx, kok);
-    const unsigned dst = pix * (3u * Cb) + head * kHeadDim * 2 + 16 * g;
-    store16(kok, dst + Cb, pack8(dk0, dk1, scale));
-    store16(kok, dst + 2 * Cb, pack8(dv0, dv1, 1.f));
+    dk = pack8(dk0, dk1, scale);
+    dv = pack8(dv0, dv1, 1.f);
+  };
+  // this lane's own token (MFMA layout) of tile tw: image offset of its row
+  auto own_row = [&](const Pos& pos, bool& vok) {
+    int uy, ux;
+    btile_token<M>(tw, c, uy, ux);
+    vok = uy < M && ux < M;
+    return bwd_pixel(p, M, pos.b, pos.wy, pos.wx, uy, ux, vok) * (3u * Cb) +
+           (unsigned)head * kHeadDim * 2 + 16 * g;
   };
 
   // walk over the run's windows, the next window's loads in flight while a
   // window is computed; they go to LDS at the end of the iteration, after
   // the window's stores were issued
   Regs R;
-  Pos nxt = decode(w_lo);
   if (w_lo < w_hi) {
-    issue(R, nxt);
+    issue(R, decode(w_lo));
     write(R);
   }
-  __syncthreads();  // table and first unit staged
+  __syncthreads();  // tables and first unit staged
   for (int bw = w_lo; bw < w_hi; ++bw) {
-    const Pos cur = nxt;
-    const bool more = bw + 1 < w_hi;
-    if (more) {
-      nxt = decode(bw + 1);
-      issue(R, nxt);
+    const Pos cur = decode(bw);
+    if (bw + 1 < w_hi) issue(R, decode(bw + 1));
+    bf16x8 dq = {}, dk = {}, dv = {};
+    if (tw < NT) dq = phase1(cur, window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx));
+    if constexpr (HP == 1) {
+      bool vok;
+      const unsigned row = own_row(cur, vok);
+      if (tw < NT) store16(vok, row, dq);
+      __syncthreads();  // P and dS blocks visible
+      if (tw < NT) {
+        phase2(dk, dv);
+        store16(vok, row + Cb, dk);
+        store16(vok, row + 2 * Cb, dv);
+      }
+      __syncthreads();  // every wave is done with the unit before it is overwritten
+    } else {
+      // dQ tile of tile tw: 2 KB of the k tiles of both heads (slice 1)
+      char* st_q = s_unit + (1 * HP * NT) * BLOCK + tw * 2 * BLOCK;
+      __syncthreads();  // P and dS blocks visible; the k tiles are free
+      stage_put(st_q, dq);
+      phase2(dk, dv);
+      __syncthreads();  // dQ tiles complete; P and dS blocks are free
+      char* st_k = s_base + L::OFF_P + tw * 2 * BLOCK;  // dK tiles, then dV tiles
+      char* st_v = st_k + NT * 2 * BLOCK;
+      stage_put(st_k, dk);
+      stage_put(st_v, dv);
+      stage_store(st_q, cur, 0);
+      __syncthreads();  // dK and dV tiles complete
+      stage_store(st_k, cur, Cb);
+      stage_store(st_v, cur, 2 * Cb);
     }
-    phase1(cur, window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx));
-    __syncthreads();  // P and dS blocks visible
-    phase2(cur);
-    __syncthreads();  // every wave is done with the unit before it is overwritten
     write(R);         // after the last window: stale data, never read
     __syncthreads();  // next unit visible to every wave
   }
-  // this workgroup's bias gradient -> LDS -> HBM
-  if (wv < NT && ok) {
+  // this workgroup's bias gradients -> LDS -> HBM
+  if (tw < NT && ok) {
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (S::col_ok(jt, r) && (S::rows_all(jt) || g_ok))
-          atomicAdd(&s_dtab[rbase - S::E(jt) - r], dta[jt][r]);
+          atomicAdd(&s_dtab[hl * T + rbase - S::E(jt) - r], dta[jt][r]);
   }
   __syncthreads();
-  for (int e = tid; e < T; e += blockDim.x) {
+  for (int e = tid; e < HP * T; e += blockDim.x) {
     const float v = s_dtab[e];
-    if (v != 0.f) atomicAdd(p.dtable + e * nh + head, v);
+    const int eh = e / T, k = e - eh * T;
+    if (v != 0.f) atomicAdd(p.dtable + k * nh + h0 + eh, v);
   }
 }
 
-template <int M>
-size_t bwd_lds_m() {
-  return BwdLds<M>::BYTES;
-}
-
-template <int M>
+template <int M, int HP>
 int bwd_blocks_per_cu(int dev, size_t lds) {
   static std::atomic<long long> cache[kMaxDevices];
   const bool cacheable = dev >= 0 && dev < kMaxDevices;
@@ -413,8 +460,8 @@ int bwd_blocks_per_cu(int dev, size_t lds) {
     if (v > 0 && (size_t)(v >> 8) == lds) return (int)(v & 255);
   }
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_bwd_bf16_kernel<M>,
-                                                   kBwdWaves * 64, lds) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_bwd_bf16_kernel<M, HP>,
+                                                   kBwdWaves * 64 * HP, lds) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   if (per_cu > 255) per_cu = 255;
@@ -422,24 +469,40 @@ int bwd_blocks_per_cu(int dev, size_t lds) {
   return per_cu;
 }
 
-// Grid: nh workgroups (one per head) per run of windows, as many runs as
-// the chip holds at the kernel's occupancy (at most one per window); with 8
-// runs or more, a multiple of 8 runs, laid out per XCD.
-template <int M>
-hipError_t launch_bwd_m(const BwdParams& p_in, int dev, int cus, hipStream_t st) {
+// Grid: nh / HP workgroups (one per head group) per run of windows, as many
+// runs as the chip holds at the kernel's occupancy (at most one per
+// window); with 8 runs or more, a multiple of 8 runs, laid out per XCD.
+template <int M, int HP>
+hipError_t launch_bwd_mh(const BwdParams& p_in, int dev, int cus, hipStream_t st) {
   BwdParams p = p_in;
-  const size_t lds = bwd_lds_m<M>();
-  const long long slots = (long long)cus * bwd_blocks_per_cu<M>(dev, lds);
-  long long runs = slots / p.nh;
+  const size_t lds = BwdLds<M, HP>::BYTES;
+  const int groups = p.nh / HP;
+  const long long slots = (long long)cus * bwd_blocks_per_cu<M, HP>(dev, lds);
+  long long runs = slots / groups;
   if (runs > p.windows) runs = p.windows;
   if (runs < 1) runs = 1;
   p.xcd_streams = runs >= 8 ? 1 : 0;
   if (p.xcd_streams) runs -= runs % 8;
-  const long long grid = runs * p.nh;
+  const long long grid = runs * groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(wattn_bwd_bf16_kernel<M>, dim3((unsigned)grid), dim3(kBwdWaves * 64), lds, st,
-                     p);
+  hipLaunchKernelGGL((wattn_bwd_bf16_kernel<M, HP>), dim3((unsigned)grid),
+                     dim3(kBwdWaves * 64 * HP), lds, st, p);
   return hipGetLastError();
+}
+
+// head pairs for 4-tile windows (5..8) when the head count is even
+template <int M>
+hipError_t launch_bwd_m(const BwdParams& p, int dev, int cus, hipStream_t st) {
+  if constexpr (Win<M>::NT == kBwdWaves) {
+    if (p.nh % 2 == 0) return launch_bwd_mh<M, 2>(p, dev, cus, st);
+  }
+  return launch_bwd_mh<M, 1>(p, dev, cus, st);
+}
+
+template <int M>
+size_t bwd_lds_m() {
+  if constexpr (Win<M>::NT == kBwdWaves) return BwdLds<M, 2>::BYTES;
+  return BwdLds<M, 1>::BYTES;
 }
 
 __global__ void fill_kernel(float* dst, long long n, float v) {
