@@ -120,3 +120,30 @@ def test_backward_zero_batch_zeroes_dtable():
                               2, 32, 7, 3) == swa.SWIN_OK
     torch.cuda.synchronize()
     assert bool((dt == 0).all())
+
+
+def test_backward_full_size_bench_config():
+    """Swin-L stage 1 at the benchmark's full batch (B=64) and launch
+    configuration: the oracle computes the whole backward; dq, dk, dv are
+    compared on three sampled images, the table gradient (a sum over all 64
+    images) in full."""
+    name = "swin-l-s1"
+    w = synth.WORKLOADS[name]
+    B, H, W, nh, M = w["B"], w["H"], w["W"], w["heads"], w["window"]
+    qkv, table = synth.workload_inputs(name)
+    dout = _dout(B, H, W, nh * 32, seed=w["seed"])
+    _say(f"bwd {name} full B={B} shift=3")
+    dq, dt = _run(qkv, table, dout, M, 3)
+    rq, rt = oracle.swin_wattn_bwd(qkv, table, dout, M, 3)
+    assert np.isfinite(dt).all()
+    lim_t = 1e-3 * np.abs(rt).max() + 1e-6
+    et = np.abs(dt - rt).max()
+    print(f"    dtable max_err={et:.3e} bound {lim_t:.3e}", flush=True)
+    assert et <= lim_t
+    for b in (0, 37, B - 1):
+        for i, comp in enumerate("qkv"):
+            e = np.abs(dq[b, :, :, i] - rq[b, :, :, i])
+            ref = np.abs(rq[b, :, :, i])
+            print(f"    image {b} d{comp}: max_abs={e.max():.3e} mean_abs={e.mean():.3e}", flush=True)
+            assert np.isfinite(dq[b]).all()
+            assert e.max() <= 2.0**-6 * ref.max() + 1e-6 and e.mean() <= 2.0**-8 * ref.mean() + 1e-7
