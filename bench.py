@@ -373,7 +373,7 @@ def bwd_bench(args, torch, np) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload, "wattn_bwd_bf16"),
-                     "kernel": f"wattn_bwd_bf16_kernel<{M}>",
+                     "kernel": f"wattn_bwd_bf16_kernel<{M}, {2 if (M + 3) // 4 == 2 and nh % 2 == 0 else 1}>",
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "isolated_launch_us": round(isolated_s * 1e6, 3),
                      "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,

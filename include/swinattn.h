@@ -108,7 +108,7 @@ int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out
  *           16-byte aligned; must not overlap qkv, dout or dtable
  *   dtable  [(2*window-1)^2][heads] float32, written (zeroed on the stream,
  *           then accumulated with atomics: the order of the sum varies)
- * head_dim must be 32 and window <= 8 (else SWIN_ERR_UNSUPPORTED); any
+ * head_dim must be 32 and window <= 12 (else SWIN_ERR_UNSUPPORTED); any
  * number of heads.  B == 0 zeroes dtable.  No allocation, no host
  * synchronisation. */
 int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dout, void* dqkv,

@@ -8,7 +8,7 @@ namespace swinattn {
 
 // Backward of the window attention, bf16 (wattn_backward.hip); windows up
 // to kMaxBwdWindow.
-constexpr int kMaxBwdWindow = 8;
+constexpr int kMaxBwdWindow = 12;
 struct BwdParams {
   const void* qkv;     // [B][H][W][3][nh][32] of this launch's images
   const float* table;  // [(2M-1)^2][nh]

@@ -41,7 +41,12 @@
 namespace swinattn {
 namespace {
 
-constexpr int kBwdWaves = 4;
+// waves per head: one per 16-token tile, at least 4 (windows of up to 8
+// have 1 or 4 tiles, windows of 9 to 12 have 9)
+template <int M>
+constexpr int bwd_waves() {
+  return Win<M>::NT > 4 ? Win<M>::NT : 4;
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -96,12 +101,13 @@ struct BwdLds {
 // (free once the query phase is done), dK and dV through the P and dS blocks
 // (free once the key phase is done).
 template <int M, int HP>
-__global__ __launch_bounds__(kBwdWaves * 64 * HP) void wattn_bwd_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kernel(BwdParams p) {
   using S = Win<M>;
   using L = BwdLds<M, HP>;
   constexpr int NT = S::NT, NK = S::NK, T = S::T;
-  static_assert(NT <= kBwdWaves, "one wave per tile");
-  static_assert(HP == 1 || (HP == 2 && NT == kBwdWaves), "head pairs for 4-tile windows");
+  constexpr int WV = bwd_waves<M>();  // waves per head
+  static_assert(NT <= WV, "one wave per tile");
+  static_assert(HP == 1 || (HP == 2 && NT == 4), "head pairs for 4-tile windows");
   constexpr int BLOCK = 1024;
   constexpr int SLICES = 4;  // q, k, v, dO
   extern __shared__ float s_lds[];
@@ -109,9 +115,9 @@ __global__ __launch_bounds__(kBwdWaves * 64 * HP) void wattn_bwd_bf16_kernel(Bwd
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __builtin_assume(wv >= 0 && wv < kBwdWaves * HP);
-  const int hl = wv / kBwdWaves;  // head of the wave within the workgroup
-  const int tw = wv % kBwdWaves;  // tile of the wave
+  __builtin_assume(wv >= 0 && wv < WV * HP);
+  const int hl = wv / WV;  // head of the wave within the workgroup
+  const int tw = wv % WV;  // tile of the wave
   const int gq = lane & 3, cq = lane >> 2;  // load layout: 16-byte part, token
   const int g = lane >> 4, c = lane & 15;   // MFMA layout: lane group, token
 
@@ -461,7 +467,7 @@ int bwd_blocks_per_cu(int dev, size_t lds) {
   }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_bwd_bf16_kernel<M, HP>,
-                                                   kBwdWaves * 64 * HP, lds) != hipSuccess ||
+                                                   bwd_waves<M>() * 64 * HP, lds) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   if (per_cu > 255) per_cu = 255;
@@ -486,14 +492,14 @@ hipError_t launch_bwd_mh(const BwdParams& p_in, int dev, int cus, hipStream_t st
   const long long grid = runs * groups;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((wattn_bwd_bf16_kernel<M, HP>), dim3((unsigned)grid),
-                     dim3(kBwdWaves * 64 * HP), lds, st, p);
+                     dim3(bwd_waves<M>() * 64 * HP), lds, st, p);
   return hipGetLastError();
 }
 
 // head pairs for 4-tile windows (5..8) when the head count is even
 template <int M>
 hipError_t launch_bwd_m(const BwdParams& p, int dev, int cus, hipStream_t st) {
-  if constexpr (Win<M>::NT == kBwdWaves) {
+  if constexpr (Win<M>::NT == 4) {
     if (p.nh % 2 == 0) return launch_bwd_mh<M, 2>(p, dev, cus, st);
   }
   return launch_bwd_mh<M, 1>(p, dev, cus, st);
@@ -501,7 +507,7 @@ hipError_t launch_bwd_m(const BwdParams& p, int dev, int cus, hipStream_t st) {
 
 template <int M>
 size_t bwd_lds_m() {
-  if constexpr (Win<M>::NT == kBwdWaves) return BwdLds<M, 2>::BYTES;
+  if constexpr (Win<M>::NT == 4) return BwdLds<M, 2>::BYTES;
   return BwdLds<M, 1>::BYTES;
 }
 
@@ -523,6 +529,10 @@ size_t bwd_lds_bytes(int M) {
     case 6: return bwd_lds_m<6>();
     case 7: return bwd_lds_m<7>();
     case 8: return bwd_lds_m<8>();
+    case 9: return bwd_lds_m<9>();
+    case 10: return bwd_lds_m<10>();
+    case 11: return bwd_lds_m<11>();
+    case 12: return bwd_lds_m<12>();
     default: return 0;
   }
 }
@@ -545,6 +555,10 @@ hipError_t launch_bwd_bf16(int M, const BwdParams& p, int dev, int cus, hipStrea
     case 6: return launch_bwd_m<6>(p, dev, cus, stream);
     case 7: return launch_bwd_m<7>(p, dev, cus, stream);
     case 8: return launch_bwd_m<8>(p, dev, cus, stream);
+    case 9: return launch_bwd_m<9>(p, dev, cus, stream);
+    case 10: return launch_bwd_m<10>(p, dev, cus, stream);
+    case 11: return launch_bwd_m<11>(p, dev, cus, stream);
+    case 12: return launch_bwd_m<12>(p, dev, cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

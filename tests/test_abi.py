@@ -177,4 +177,4 @@ def test_bwd_rejects_invalid_arguments():
 def test_bwd_reports_unsupported_configurations():
     U = swa.SWIN_ERR_UNSUPPORTED
     assert _bwd(head_dim=64) == U
-    assert _bwd(window=12, H=24, W=24, shift=6) == U        # windows beyond 8
+    assert _bwd(window=13, H=26, W=26, shift=6) == U        # windows beyond 12

@@ -80,6 +80,11 @@ def _check(qkv, table, dout, M, s, what):
     (1, 3, 5, 2, 1, 0),       # window 1: the output is v, so dv = dout, dq = dk = 0
     (1, 7, 14, 48, 7, 3),     # 48 heads, two windows: one window per run
     (3, 14, 14, 5, 7, 3),     # 12 windows, 5 heads: uneven runs
+    (1, 24, 24, 2, 12, 6),    # window 12: nine full tiles, one wave per tile
+    (2, 24, 36, 3, 12, 5),    # window 12, H != W, odd shift
+    (1, 20, 20, 2, 10, 0),    # window 10: padded tiles, no shift
+    (1, 18, 27, 1, 9, 4),     # window 9: one padded token row and column per tile row
+    (1, 22, 11, 2, 11, 7),    # window 11
 ])
 def test_backward_matches_oracle(B, H, W, nh, M, s):
     _say(f"bwd B={B} H={H} W={W} nh={nh} M={M} s={s}")
@@ -109,6 +114,16 @@ def test_backward_swin_l_sampled_windows():
     _check(qkv, table, dout, 7, 3, "swin-l-s1 B=4")
 
 
+def test_backward_swin_l_384():
+    """Swin-L at 384 px (window 12, shift 6) at B=2: nine tiles per window;
+    the oracle checks the whole output."""
+    w = synth.WORKLOADS["swin-l-384"]
+    qkv, table = synth.workload_inputs("swin-l-384", batch=2)
+    dout = _dout(2, w["H"], w["W"], w["heads"] * 32, seed=w["seed"])
+    _say("bwd swin-l-384 B=2 shift=6")
+    _check(qkv, table, dout, 12, 6, "swin-l-384 B=2")
+
+
 def test_backward_zero_batch_zeroes_dtable():
     _say("bwd B=0")
     q = torch.empty(0, 14, 14, 3, 2, 32, dtype=torch.bfloat16, device=_dev())
@@ -122,25 +137,26 @@ def test_backward_zero_batch_zeroes_dtable():
     assert bool((dt == 0).all())
 
 
-def test_backward_full_size_bench_config():
-    """Swin-L stage 1 at the benchmark's full batch (B=64) and launch
-    configuration: the oracle computes the whole backward; dq, dk, dv are
-    compared on three sampled images, the table gradient (a sum over all 64
-    images) in full."""
-    name = "swin-l-s1"
+@pytest.mark.parametrize("name", ["swin-l-s1", "swin-l-384"])
+def test_backward_full_size(name):
+    """Swin-L stage 1 (B=64, the benchmark's batch and launch configuration)
+    and Swin-L at 384 px (B=16, window 12) at full size: the oracle computes
+    the whole backward; dq, dk, dv are compared on three sampled images, the
+    table gradient (a sum over every image) in full."""
     w = synth.WORKLOADS[name]
     B, H, W, nh, M = w["B"], w["H"], w["W"], w["heads"], w["window"]
+    s = w["shifts"][-1]
     qkv, table = synth.workload_inputs(name)
     dout = _dout(B, H, W, nh * 32, seed=w["seed"])
-    _say(f"bwd {name} full B={B} shift=3")
-    dq, dt = _run(qkv, table, dout, M, 3)
-    rq, rt = oracle.swin_wattn_bwd(qkv, table, dout, M, 3)
+    _say(f"bwd {name} full B={B} shift={s}")
+    dq, dt = _run(qkv, table, dout, M, s)
+    rq, rt = oracle.swin_wattn_bwd(qkv, table, dout, M, s)
     assert np.isfinite(dt).all()
     lim_t = 1e-3 * np.abs(rt).max() + 1e-6
     et = np.abs(dt - rt).max()
     print(f"    dtable max_err={et:.3e} bound {lim_t:.3e}", flush=True)
     assert et <= lim_t
-    for b in (0, 37, B - 1):
+    for b in (0, B // 2 + 5, B - 1):
         for i, comp in enumerate("qkv"):
             e = np.abs(dq[b, :, :, i] - rq[b, :, :, i])
             ref = np.abs(rq[b, :, :, i])
