@@ -33,6 +33,7 @@
 // The attention math per item is the one described in wattn_kernels.hip.
 
 #include <atomic>
+#include <type_traits>
 
 #include "wattn_common.h"
 
@@ -59,6 +60,10 @@ struct Unit {
   static constexpr bool HEAD_INNER = HG > 1 && IPW % HG == 0;
   // every wave's items belong to one head: key / value tiles load once
   static constexpr bool ONE_HEAD = !HEAD_INNER && ITEMS % kWaves == 0 && NT % IPW == 0;
+  // items that do not divide evenly over the waves (9 query tiles of one
+  // head at windows 9 to 12) leave the last wave short; the short wave
+  // rotates from unit to unit so that no SIMD sits out all the math
+  static constexpr bool ROTATE = ITEMS % kWaves != 0;
   static constexpr int BLOCK = 1024;                       // 16 tokens x 64 bytes
   // windows of up to 4 tiles keep key tiles, V^T and mask operands in
   // registers for all items of a wave; larger windows re-read them from LDS
@@ -199,9 +204,11 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   for (int s = 0; s < 8; ++s) ones[s] = (__bf16)1.f;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
-  // the math of one unit, out of LDS
-  auto process = [&](const Pos& pos) {
+  // the math of one unit, out of LDS; `rot` selects which wave takes which
+  // share of the items
+  auto process = [&](const Pos& pos, int rot) {
     const int hg = pos.hg, b = pos.b, wy = pos.wy, wx = pos.wx;
+    const int wq = U::ROTATE ? (wv + rot) & (kWaves - 1) : wv;
     const bool masked = window_masked(p.shift, wy, wx, p.nWy, p.nWx);
     // key-side mask operand of key tile t for this lane (see
     // LaneWindow::init_labels): it depends on the lane only, not the head
@@ -252,18 +259,18 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     };
     int cur = -1;
     if (U::ONE_HEAD) {
-      cur = wv * U::IPW / NT;
+      cur = wq * U::IPW / NT;
       load_head(cur);
     }
     bf16x8 ovs[HG];  // head-inner: outputs of the query tile's heads, stored together
 #pragma unroll
     for (int i = 0; i < U::IPW; ++i) {
-      const int item = wv * U::IPW + i;
+      const int item = wq * U::IPW + i;
       if (item >= U::ITEMS) break;
       int hl, it;
       if constexpr (U::HEAD_INNER) {
         hl = i % HG;
-        it = wv * (U::IPW / HG) + i / HG;
+        it = wq * (U::IPW / HG) + i / HG;
       } else {
         hl = item / NT;
         it = item - hl * NT;
@@ -286,31 +293,46 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
         for (int k = 0; k < 3; ++k) mask_b[k] = loc == g ? (__bf16)0.f : (__bf16)-1.f;
       }
 
+      // score tiles.  MASKED: 0 no mask, 1 mask, 2 the window's flag tested
+      // per tile.  Nine-tile windows take the flag once per item, outside
+      // the tile loop, so that the bias reads and MFMAs of all key tiles are
+      // scheduled together (the loop unrolls into one block); smaller
+      // windows keep the per-tile test, whose code needs fewer registers
+      // and keeps four workgroups per CU
       f32x4 sc[NT];
+      auto score_tiles = [&](auto masked_c) {
+        constexpr int MASKED = decltype(masked_c)::value;
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt) {
-        f32x4 acc;
+        for (int jt = 0; jt < NT; ++jt) {
+          f32x4 acc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (!S::col_ok(jt, r)) {
-            acc[r] = -__builtin_inff();
-            continue;
+          for (int r = 0; r < 4; ++r) {
+            if (!S::col_ok(jt, r)) {
+              acc[r] = -__builtin_inff();
+              continue;
+            }
+            float v = s_bias[qbase + S::E(jt) + r];
+            if (!S::rows_all(jt)) v = g_ok ? v : -__builtin_inff();
+            acc[r] = v;
           }
-          float v = s_bias[qbase + S::E(jt) + r];
-          if (!S::rows_all(jt)) v = g_ok ? v : -__builtin_inff();
-          acc[r] = v;
+          bf16x8 kj;
+          if constexpr (U::HOLD) kj = kt[jt];
+          else kj = key_tile(hl, jt);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kj, q, acc, 0, 0, 0);
+          if (MASKED == 1 || (MASKED == 2 && masked)) {
+            bf16x8 mj;
+            if constexpr (U::HOLD) mj = mask_a[jt];
+            else mj = *reinterpret_cast<const bf16x8*>(s_unit + U::mask_block(jt) + lane * 16);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mj, mask_b, acc, 0, 0, 0);
+          }
+          sc[jt] = acc;
         }
-        bf16x8 kj;
-        if constexpr (U::HOLD) kj = kt[jt];
-        else kj = key_tile(hl, jt);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kj, q, acc, 0, 0, 0);
-        if (masked) {
-          bf16x8 mj;
-          if constexpr (U::HOLD) mj = mask_a[jt];
-          else mj = *reinterpret_cast<const bf16x8*>(s_unit + U::mask_block(jt) + lane * 16);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mj, mask_b, acc, 0, 0, 0);
-        }
-        sc[jt] = acc;
+      };
+      if constexpr (U::HOLD) {
+        score_tiles(std::integral_constant<int, 2>{});
+      } else {
+        if (masked) score_tiles(std::integral_constant<int, 1>{});
+        else score_tiles(std::integral_constant<int, 0>{});
       }
       softmax_numerators<M>(sc, p.score_scale);
       bf16x8 pb[NK];
@@ -367,6 +389,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   // while a unit is written to LDS and computed
   if (kDepth == 1) {
     Regs R;
+    int rot = 0;
     Pos nxt = decode(u);
     if (u < u_end) issue_loads(R, nxt);
     // the bias table (reversed, divided by the scale) is staged while the
@@ -382,7 +405,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
         nxt = decode(u + u_step);
         issue_loads(R, nxt);
       }
-      process(cur);
+      process(cur, rot++);
       __syncthreads();  // every wave is done with the unit before it is overwritten
     }
   } else {
@@ -401,7 +424,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
         p0 = decode(u + 2 * u_step);
         issue_loads(R0, p0);
       }
-      process(cur);
+      process(cur, 0);
       __syncthreads();
       u += u_step;
       if (u >= u_end) break;
@@ -413,7 +436,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
         p1 = decode(u + 2 * u_step);
         issue_loads(R1, p1);
       }
-      process(cur);
+      process(cur, 1);
       __syncthreads();
       u += u_step;
     }
