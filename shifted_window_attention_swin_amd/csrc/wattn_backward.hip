@@ -1,5 +1,5 @@
-// Backward of the fused shifted-window attention (bf16, windows up to 8:
-// 1 or 4 tiles of 16 tokens), for training.  The NVIDIA talk "Swin
+// Backward of the fused shifted-window attention (bf16, windows up to 12:
+// 1, 4 or 9 tiles of 16 tokens), for training.  The NVIDIA talk "Swin
 // Transformer training and inference optimization" (uticex.com 1598),
 // section 2, fuses the window attention's backward as it fuses the forward.
 //
@@ -15,6 +15,9 @@
 //             windows; the nh workgroups of one run (its nh heads) sit on
 //             one XCD and walk it in step, so the 128-byte lines that hold
 //             two heads of a token are fetched into one L2.
+//   waves     one per 16-token tile of the head: 4 per head for windows up
+//             to 8 (1 or 4 tiles), 9 for windows of 9 to 12 (whose P and dS
+//             blocks, 81 KB, leave room for one workgroup per CU)
 //   phase 1   one wave per query tile, in the forward's transposed layout
 //             (keys in a lane's accumulator rows, queries across lanes):
 //             S^T and P (fp32, exact softmax), dP^T = V dO^T, D, dS^T, and
@@ -27,7 +30,7 @@
 //             lane), dO^T and Q^T from transposing reads of the unit.
 //   bias grad the (query, key) pair of a phase-1 accumulator slot of a lane
 //             is the same in every window, hence so is its table row: each
-//             lane sums the fp32 dS of its 16 slots in registers over all its
+//             lane sums the fp32 dS of its 4 x tiles slots in registers over all its
 //             workgroup's windows (one head), then adds them once into an
 //             LDS copy of the head's table gradient (LDS atomics), which goes
 //             to HBM with global atomics.
