@@ -129,9 +129,22 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
   char* s_base = reinterpret_cast<char*>(s_lds);
   char* s_unit = s_base + L::OFF_UNIT;      // [slice][head][tile] blocks of 1 KB
   auto block = [&](int sl, int t) { return s_unit + ((sl * HP + hl) * NT + t) * BLOCK; };
+  // byte offset of 16-byte part `part` of in-tile token u in a 1 KB block:
+  // the part is XORed with bits 1-2 of the token, so that the tokens 4
+  // apart that a lane group reads together sit in different banks
+  auto uchunk = [&](int u, int part) {
+    return 64 * u + 16 * (part ^ ((u >> 1) & 3));
+  };
   // P and dS of the wave's head, query tile iq and key tile jk: [query 16][key 16] bf16
   auto pblock = [&](int off, int iq, int jk) {
     return s_base + off + hl * L::PHEAD + (iq * NT + jk) * L::PBLK;
+  };
+  // byte offset of the 8-byte chunk (query row, key group kg) of a block:
+  // the key group is XORed with bits 2-3 of the row, so that the 16 rows a
+  // lane group writes (32 bytes apart) spread over the banks; the 16 chunks
+  // a lane group reads back (4 whole rows) stay one contiguous 128 bytes
+  auto pchunk = [&](int row, int kg) {
+    return 32 * row + 8 * (kg ^ ((row >> 2) & 3));
   };
 
   const unsigned Cb = (unsigned)nh * kHeadDim * 2;  // bytes of one q (k, v, dO) row
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
     if (tw < NT) {
 #pragma unroll
       for (int sl = 0; sl < SLICES; ++sl)
-        *reinterpret_cast<u32x4*>(block(sl, tw) + lane * 16) = R[sl];
+        *reinterpret_cast<u32x4*>(block(sl, tw) + uchunk(lane >> 2, lane & 3)) = R[sl];
     }
   };
   const bool g_ok = g < S::LG;
@@ -230,11 +243,13 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
   };
   // 16 bytes of token u (MFMA layout lane) of tile t of slice sl
   auto tok16 = [&](int sl, int t) {
-    return *reinterpret_cast<const bf16x8*>(block(sl, t) + (4 * c + g) * 16);
+    return *reinterpret_cast<const bf16x8*>(block(sl, t) + uchunk(c, g));
   };
   // transposing read of tile t of slice sl, channel half hf: element k of
   // lane (g, i) is channel out_channel(hf, i) of in-tile token 4g + k
-  auto tile_t = [&](int sl, int t, int hf) { return lds_read_tr(block(sl, t) + lane * 16 + 8 * hf); };
+  auto tile_t = [&](int sl, int t, int hf) {
+    return lds_read_tr(block(sl, t) + uchunk(lane >> 2, lane & 3) + 8 * hf);
+  };
   // 8 consecutive channels of a lane, from two accumulator tiles
   auto pack8 = [&](const f32x4& lo, const f32x4& hi, float mul) {
     bf16x8 o;
@@ -246,16 +261,20 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
     return o;
   };
   // head pairs: gradient tile of tile t in LDS ([16 tokens][128 B], this
-  // head's half at 64 hl), written by both heads' waves of tile t
+  // head's half at chunks 4 hl .. 4 hl + 3), written by both heads' waves of
+  // tile t.  16-byte chunk k of token row u sits at chunk k ^ (u & 7) of the
+  // row, so that the 16 tokens a lane group writes (rows 128 bytes apart)
+  // fall in different banks
+  auto swz = [&](int u, int k) { return k ^ (u & 7); };
   auto stage_put = [&](char* st, const bf16x8& v) {
-    *reinterpret_cast<bf16x8*>(st + c * 128 + 64 * hl + 16 * g) = v;
+    *reinterpret_cast<bf16x8*>(st + c * 128 + 16 * swz(c, 4 * hl + g)) = v;
   };
   // ... and read back by this wave as whole lines: tokens 8 hl .. 8 hl + 7
   // of tile t, 8 lanes per token, to the slice at byte offset `slice` of a
   // token row
   auto stage_store = [&](const char* st, const Pos& pos, unsigned slice) {
     const int u = 8 * hl + (lane >> 3);
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + u * 128 + 16 * (lane & 7));
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + u * 128 + 16 * swz(u, lane & 7));
     int uy, ux;
     btile_token<M>(tw, u, uy, ux);
     const bool uok = uy < M && ux < M;
@@ -350,8 +369,8 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
         pb[jt / 2][4 * (jt % 2) + r] = st[r];
       }
       // P[query c][keys 4g .. 4g+3] of block (it, jt)
-      *reinterpret_cast<bf16x4*>(pblock(L::OFF_P, it, jt) + 32 * c + 8 * g) = pt;
-      *reinterpret_cast<bf16x4*>(pblock(L::OFF_DS, it, jt) + 32 * c + 8 * g) = st;
+      *reinterpret_cast<bf16x4*>(pblock(L::OFF_P, it, jt) + pchunk(c, g)) = pt;
+      *reinterpret_cast<bf16x4*>(pblock(L::OFF_DS, it, jt) + pchunk(c, g)) = st;
     }
     if constexpr (NT % 2 == 1) {
 #pragma unroll
@@ -380,8 +399,8 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
 #pragma unroll
     for (int iq = 0; iq < NT; ++iq) {
       // element k of lane (g, c): P (dS) of query 4g + k of tile iq, key c
-      const bf16x4 pb = lds_read_tr(pblock(L::OFF_P, iq, jk) + 8 * lane);
-      const bf16x4 sb = lds_read_tr(pblock(L::OFF_DS, iq, jk) + 8 * lane);
+      const bf16x4 pb = lds_read_tr(pblock(L::OFF_P, iq, jk) + pchunk(lane >> 2, lane & 3));
+      const bf16x4 sb = lds_read_tr(pblock(L::OFF_DS, iq, jk) + pchunk(lane >> 2, lane & 3));
       dv0 = mfma16(tile_t(3, iq, 0), pb, dv0);
       dv1 = mfma16(tile_t(3, iq, 1), pb, dv1);
       dk0 = mfma16(tile_t(0, iq, 0), sb, dk0);

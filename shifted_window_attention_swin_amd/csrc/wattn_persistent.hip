@@ -104,6 +104,12 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = lane & 3, cq = lane >> 2;    // load layout: 16-byte part, token
+  // byte offset of 16-byte part `part` of in-tile token u in a 1 KB block:
+  // the part is XORed with bits 1-2 of the token, so that the tokens 4
+  // apart that a lane group reads together sit in different banks
+  auto uchunk = [](int u, int part) {
+    return 64 * u + 16 * (part ^ ((u >> 1) & 3));
+  };
   const int g = lane >> 4, c = lane & 15;     // MFMA layout: lane group, token
   const int nh = p.nh;
   const unsigned Cb = (unsigned)nh * kHeadDim * 2;  // bytes of one q (k, v, out) row
@@ -193,7 +199,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       if (t < NT) {
 #pragma unroll
         for (int s = 0; s < U::SLICES; ++s)
-          *reinterpret_cast<u32x4*>(s_unit + U::block(s, t) + lane * 16) = R[s][k];
+          *reinterpret_cast<u32x4*>(s_unit + U::block(s, t) + uchunk(lane >> 2, lane & 3)) = R[s][k];
       }
     }
   };
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     constexpr int NH = U::HOLD ? NT : 1, NKH = U::HOLD ? NK : 1;
     bf16x8 kt[NH], va[2][NKH];
     auto key_tile = [&](int hl, int t) {
-      return *reinterpret_cast<const bf16x8*>(s_unit + U::block(HG + hl, t) + (4 * c + g) * 16);
+      return *reinterpret_cast<const bf16x8*>(s_unit + U::block(HG + hl, t) + uchunk(c, g));
     };
     // V^T straight from LDS with the transposing read: in each group of 16
     // lanes, lane i receives element i%4 of the 8-byte chunks read by lanes
@@ -243,8 +249,9 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     // A-operand slots of key tile t.
     auto value_t = [&](int hl, int kk, int hf) {
       const int t1 = 2 * kk + 1 < NT ? 2 * kk + 1 : 2 * kk;  // odd tile count: any finite data
-      const bf16x4 lo = lds_read_tr(s_unit + U::block(2 * HG + hl, 2 * kk) + lane * 16 + 8 * hf);
-      const bf16x4 hi = lds_read_tr(s_unit + U::block(2 * HG + hl, t1) + lane * 16 + 8 * hf);
+      const int own = uchunk(lane >> 2, lane & 3) + 8 * hf;
+      const bf16x4 lo = lds_read_tr(s_unit + U::block(2 * HG + hl, 2 * kk) + own);
+      const bf16x4 hi = lds_read_tr(s_unit + U::block(2 * HG + hl, t1) + own);
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto load_head = [&](int hl) {
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
         load_head(hl);
       }
       // the query tile and what the lane needs about its query token
-      const bf16x8 q = *reinterpret_cast<const bf16x8*>(s_unit + U::block(hl, it) + (4 * c + g) * 16);
+      const bf16x8 q = *reinterpret_cast<const bf16x8*>(s_unit + U::block(hl, it) + uchunk(c, g));
       int ty, tx;
       tile_token<M>(it, c, ty, tx);
       const bool ok = ty < M && tx < M;
