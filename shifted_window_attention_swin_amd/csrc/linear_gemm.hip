@@ -17,8 +17,9 @@
 // ridge of about 310): the kernel is built to stream x and y at HBM speed.
 //
 //   row block  32 tokens x K, staged in LDS as 1 KB blocks of 16 tokens x 64
-//              bytes (32 input channels), read in the conflict-free order the
-//              MFMA B operand wants; the next block waits in registers.
+//              bytes (32 input channels, the 16-byte parts of a token
+//              permuted so that the MFMA B operand reads are free of bank
+//              conflicts); the next block waits in registers.
 //   workgroup  6, 4 or 2 waves (the widest that divides N / 32), persistent,
 //              owning one column group (a 32-channel block per wave: whole
 //              128-byte lines of every token) for the whole launch and
@@ -92,6 +93,10 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   const int T = (int)p.T;                   // the host keeps T below 2^31
   const int gq = lane & 3, cq = lane >> 2;  // load layout: 16-byte part, token
   const int g = lane >> 4, c = lane & 15;   // MFMA layout: lane group, token
+  // byte offset of 16-byte part `part` of token u in a 1 KB block of x: the
+  // part is XORed with bits 1-2 of the token, so that the tokens 4 apart
+  // that a lane group reads together sit in different banks
+  auto uchunk = [](int u, int part) { return 64 * u + 16 * (part ^ ((u >> 1) & 3)); };
   const char* xb = static_cast<const char*>(p.x);
   const char* rb = static_cast<const char*>(p.res);
   char* yb = static_cast<char*>(p.y);
@@ -176,12 +181,13 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   auto ln_stats = [&]() {
     for (int t0 = wv * TPW_LN; t0 < kLinRows; t0 += kLinWaves * TPW_LN) {  // wave-uniform
       const int t = t0 + lane / LL;
-      const char* row = s_x + (t >> 4) * KS * 1024 + (t & 15) * 64;
+      const char* tile = s_x + (t >> 4) * KS * 1024;
       float v[CPL][8];
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
         const int q = ql + LL * k;
-        const bf16x8 h = *reinterpret_cast<const bf16x8*>(row + (q >> 2) * 1024 + (q & 3) * 16);
+        const bf16x8 h =
+            *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * 1024 + uchunk(t & 15, q & 3));
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[k][e] = (float)h[e];
       }
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
       const int bi = wv + kLinWaves * k;
-      if (bi < NB) *reinterpret_cast<u32x4*>(s_x + bi * 1024 + lane * 16) = R[k];
+      if (bi < NB) *reinterpret_cast<u32x4*>(s_x + bi * 1024 + uchunk(cq, gq)) = R[k];
     }
   };
 
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
 #pragma unroll
         for (int tt = 0; tt < kLinTiles; ++tt) {
           const bf16x8 b =
-              *reinterpret_cast<const bf16x8*>(s_x + (tt * KS + ks) * 1024 + (4 * c + g) * 16);
+              *reinterpret_cast<const bf16x8*>(s_x + (tt * KS + ks) * 1024 + uchunk(c, g));
           acc[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][0], b, acc[tt][0], 0, 0, 0);
           acc[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][1], b, acc[tt][1], 0, 0, 0);
         }
