@@ -429,7 +429,12 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
   __syncthreads();  // tables and first unit staged
   for (int bw = w_lo; bw < w_hi; ++bw) {
     const Pos cur = decode(bw);
-    if (bw + 1 < w_hi) issue(R, decode(bw + 1));
+    if (bw + 1 < w_hi) {
+      // the loads leave ahead of the other waves' math on the SIMD
+      __builtin_amdgcn_s_setprio(3);
+      issue(R, decode(bw + 1));
+      __builtin_amdgcn_s_setprio(0);
+    }
     bf16x8 dq = {}, dk = {}, dv = {};
     if (tw < NT) dq = phase1(cur, window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx));
     if constexpr (HP == 1) {

@@ -410,7 +410,10 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       const Pos cur = nxt;
       if (u + u_step < u_end) {
         nxt = decode(u + u_step);
+        // the loads leave ahead of the other workgroups' math on the SIMD
+        __builtin_amdgcn_s_setprio(3);
         issue_loads(R, nxt);
+        __builtin_amdgcn_s_setprio(0);
       }
       process(cur, rot++);
       __syncthreads();  // every wave is done with the unit before it is overwritten
