@@ -138,6 +138,7 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
   // a unit's per-token slice is hg * 64 bytes: with odd hg and several head
   // groups, neighbouring units of a window share 128-byte lines
   p.xcd_ranges = (hg % 2 == 1 && p.nhg > 1) ? 1 : 0;
+  p.own_bias = 0;  // chosen per launch by the persistent kernel's launcher
   // per-window kernels: heads are dealt round-robin to the waves of a
   // workgroup, preferably 2-3 heads per wave
   int waves = 1;

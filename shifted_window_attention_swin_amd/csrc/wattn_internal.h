@@ -26,6 +26,7 @@ struct FwdParams {
   int units;                // B * nW * nhg (work units of the persistent kernel)
   int nhg;                  // head groups per window (persistent kernel)
   int xcd_ranges;           // persistent kernel: one contiguous unit range per XCD
+  int own_bias;             // persistent kernel: stage only the workgroup's head group's tables
   float score_scale;        // log2(e) / sqrt(head_dim)
   float inv_scale;          // sqrt(head_dim): bias and mask are pre-divided by the scale
   float mask_value;         // -100 * sqrt(head_dim)

@@ -11,10 +11,12 @@
 //              743345, section 2, WindowAttention case) describes the fused
 //              module as tiles moving through the memory hierarchy of HBM,
 //              shared memory and registers; this is that pipeline on gfx950.
-//   workgroup  4 waves, persistent: the grid walks the units in order, so
-//              the units in flight are one compact stretch of the batch;
-//              when the units of a window share cache lines, each XCD
-//              instead walks its own contiguous range (one L2 per line).
+//   workgroup  4 waves (3 for 9-tile windows), persistent: the grid walks
+//              the units in order, so the units in flight are one compact
+//              stretch of the batch; when the units of a window share cache
+//              lines, each XCD instead walks its own contiguous range (one
+//              L2 per line).  A workgroup whose units all belong to one head
+//              group stages only that group's bias tables.
 //   pipeline   the next unit's 16-byte loads are issued into registers right
 //              after the current unit is written to LDS, and stay in flight
 //              while the current unit is computed out of LDS.
@@ -40,7 +42,13 @@
 namespace swinattn {
 namespace {
 
-constexpr int kWaves = 4;  // waves per workgroup
+// waves per workgroup: 4, or 3 for windows of 9 tiles (their 9 query tiles
+// then split evenly, and 4 workgroups of 3 waves per CU leave each wave 168
+// VGPRs)
+template <int M>
+constexpr int fwd_waves() {
+  return Win<M>::NT > 4 ? 3 : 4;
+}
 #ifndef SWA_PF_DEPTH
 #define SWA_PF_DEPTH 1
 #endif
@@ -49,6 +57,7 @@ constexpr int kDepth = SWA_PF_DEPTH;  // units whose loads are in flight during 
 template <int M, int HG>
 struct Unit {
   using S = Win<M>;
+  static constexpr int kWaves = fwd_waves<M>();
   static constexpr int NT = S::NT;
   static constexpr int SLICES = 3 * HG;                    // q, k, v of HG heads
   static constexpr int TPW = (NT + kWaves - 1) / kWaves;   // tiles loaded per wave
@@ -91,14 +100,34 @@ SWA_INLINE unsigned token_pixel(const FwdParams& p, int M, int b, int wy, int wx
   return ((unsigned)b * p.H + y) * p.W + x;
 }
 
+// Stages the bias tables of heads h0 .. h0 + count - 1, each reversed and
+// divided by the scale, followed by the zero tail read by padded keys.
+template <int M>
+SWA_INLINE void stage_bias_heads(float* s_bias, const float* table, int nh, int h0, int count,
+                                 float inv_scale) {
+  using S = Win<M>;
+  const int n = count * S::T;
+  for (int e = threadIdx.x; e < n + S::TAIL; e += blockDim.x) {
+    float v = 0.f;
+    if (e < n) {
+      const int h = e / S::T, k = e - h * S::T;
+      v = table[(S::T - 1 - k) * nh + h0 + h] * inv_scale;
+    }
+    s_bias[e] = v;
+  }
+}
+
 template <int M, int HG>
-__global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
+__global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_waves<M>() == 3 ? 3 : 1)) void wattn_fwd_bf16_persistent(FwdParams p) {
   using S = Win<M>;
   using U = Unit<M, HG>;
   constexpr int NT = S::NT, NK = S::NK;
   extern __shared__ float s_lds[];
   float* s_bias = s_lds;
-  const int bias_floats = p.nh * S::T + S::TAIL;
+  constexpr int kWaves = U::kWaves;
+  // bias tables staged: every head, or (own_bias) only the HG heads of the
+  // workgroup's head group, which is the same in all its units
+  const int bias_floats = (p.own_bias ? HG : p.nh) * S::T + S::TAIL;
   char* s_unit = reinterpret_cast<char*>(s_lds) + ((bias_floats * 4 + 15) & ~15);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -135,6 +164,10 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     u_step = G;
     u_end = units;
   }
+  // first head of the workgroup's head group when its bias tables alone are
+  // staged (the host sets own_bias only for grids that keep u_step a
+  // multiple of the head-group count)
+  const int hbase = p.own_bias ? (u % p.nhg) * HG : 0;
 
 
   // unit u -> (head group, image, window); decoded once, used for the loads
@@ -214,7 +247,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
   // share of the items
   auto process = [&](const Pos& pos, int rot) {
     const int hg = pos.hg, b = pos.b, wy = pos.wy, wx = pos.wx;
-    const int wq = U::ROTATE ? (wv + rot) & (kWaves - 1) : wv;
+    const int wq = U::ROTATE ? (wv + rot) % kWaves : wv;
     const bool masked = window_masked(p.shift, wy, wx, p.nWy, p.nWx);
     // key-side mask operand of key tile t for this lane (see
     // LaneWindow::init_labels): it depends on the lane only, not the head
@@ -292,7 +325,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
       int ty, tx;
       tile_token<M>(it, c, ty, tx);
       const bool ok = ty < M && tx < M;
-      const int qbase = h * S::T + S::T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
+      const int qbase = (h - hbase) * S::T + S::T - 1 - S::C0 - (ok ? S::D * ty + tx : 0) + S::D * g;
       bf16x8 mask_b = {};
       if (masked) {
         const int loc = 2 * (wy * M + ty >= p.H - p.shift) + (wx * M + tx >= p.W - p.shift);
@@ -401,7 +434,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     if (u < u_end) issue_loads(R, nxt);
     // the bias table (reversed, divided by the scale) is staged while the
     // first unit's loads are in flight
-    stage_bias<M>(s_bias, p.table, nh, p.inv_scale);
+    stage_bias_heads<M>(s_bias, p.table, nh, hbase, p.own_bias ? HG : nh, p.inv_scale);
     __syncthreads();  // bias table visible
     for (; u < u_end; u += u_step) {
       write_unit(R);
@@ -423,7 +456,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_persistent(FwdParams p) {
     Pos p0 = decode(u), p1 = decode(u + u_step);
     if (u < u_end) issue_loads(R0, p0);
     if (u + u_step < u_end) issue_loads(R1, p1);
-    stage_bias<M>(s_bias, p.table, nh, p.inv_scale);
+    stage_bias_heads<M>(s_bias, p.table, nh, hbase, p.own_bias ? HG : nh, p.inv_scale);
     __syncthreads();  // bias table visible
     while (u < u_end) {
       write_unit(R0);
@@ -462,30 +495,62 @@ size_t lds_bytes_mh(int nh) {
 // workgroups of wattn_fwd_bf16_persistent<M, HG> resident per CU for `lds`
 // bytes of dynamic LDS; cached per device as (lds << 8 | blocks)
 template <int M, int HG>
-int blocks_per_cu(int dev, size_t lds) {
-  static std::atomic<long long> cache[kMaxDevices];
+int blocks_per_cu(int dev, size_t lds, int slot) {
+  static std::atomic<long long> cache[kMaxDevices][2];
   const bool cacheable = dev >= 0 && dev < kMaxDevices;
   if (cacheable) {
-    const long long c = cache[dev].load(std::memory_order_relaxed);
+    const long long c = cache[dev][slot].load(std::memory_order_relaxed);
     if (c > 0 && (size_t)(c >> 8) == lds) return (int)(c & 255);
   }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_fwd_bf16_persistent<M, HG>,
-                                                   kWaves * 64, lds) != hipSuccess || per_cu < 1)
+                                                   Unit<M, HG>::kWaves * 64, lds) != hipSuccess ||
+      per_cu < 1)
     per_cu = 1;
   if (per_cu > 255) per_cu = 255;
-  if (cacheable) cache[dev].store(((long long)lds << 8) | per_cu, std::memory_order_relaxed);
+  if (cacheable) cache[dev][slot].store(((long long)lds << 8) | per_cu, std::memory_order_relaxed);
   return per_cu;
 }
 
+// Grid for `lds` bytes per workgroup: CUs x resident workgroups, at most
+// one per unit, whole rounds of the 8 XCDs.
 template <int M, int HG>
-hipError_t launch_mh(const FwdParams& p, int dev, int cus, hipStream_t st) {
-  const size_t lds = lds_bytes_mh<M, HG>(p.nh);
-  long long grid = (long long)cus * blocks_per_cu<M, HG>(dev, lds);
+long long fwd_grid(const FwdParams& p, int dev, int cus, size_t lds, int slot) {
+  long long grid = (long long)cus * blocks_per_cu<M, HG>(dev, lds, slot);
   if (grid > p.units) grid = p.units;
   if (grid >= 8) grid &= ~7LL;  // whole XCD rounds (equal share per XCD)
-  hipLaunchKernelGGL((wattn_fwd_bf16_persistent<M, HG>), dim3((unsigned)grid), dim3(kWaves * 64),
-                     lds, st, p);
+  return grid;
+}
+
+template <int M, int HG>
+hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
+  FwdParams p = p_in;
+  p.own_bias = 0;
+  size_t lds = lds_bytes_mh<M, HG>(p.nh);
+  long long grid = -1;
+  if constexpr (Win<M>::NT > 4) {
+    // 9-tile windows: when a workgroup's units all share one head group it
+    // stages only that group's bias tables (one head's table instead of
+    // nh), which leaves LDS for one more workgroup per CU.  A workgroup
+    // steps through units by the grid (grid order) or by the grid / 8 (XCD
+    // ranges), so the grid is cut to a multiple of nhg (8 nhg): at most
+    // 8 nhg - 8 workgroups fewer, e.g. 1008 instead of 1024 at 6 heads.
+    if (p.nhg > 1) {
+      const size_t small = lds_bytes_mh<M, HG>(HG);
+      long long g = fwd_grid<M, HG>(p, dev, cus, small, 1);
+      const bool xcd = p.xcd_ranges && g % 8 == 0;
+      const long long q = xcd ? 8LL * p.nhg : p.nhg;
+      if (g >= q) g -= g % q;
+      if (g % q == 0) {
+        grid = g;
+        lds = small;
+        p.own_bias = 1;
+      }
+    }
+  }
+  if (grid < 0) grid = fwd_grid<M, HG>(p, dev, cus, lds, 0);
+  hipLaunchKernelGGL((wattn_fwd_bf16_persistent<M, HG>), dim3((unsigned)grid),
+                     dim3(Unit<M, HG>::kWaves * 64), lds, st, p);
   return hipGetLastError();
 }
 
