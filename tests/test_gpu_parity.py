@@ -153,8 +153,11 @@ def test_bf16_workloads_full_size_sampled(name):
     (2, 28, 14, 6, 7, 3),
     (1, 7, 7, 2, 7, 0),      # one window covers the image, no shift
     (1, 7, 7, 2, 7, 3),      # one window with shift: every region in one window
-    (1, 12, 12, 6, 12, 0),
-    (2, 24, 24, 6, 12, 6),
+    (1, 12, 12, 6, 12, 0),   # 6 units on 6 workgroups (grid order), one head's bias each
+    (2, 24, 24, 6, 12, 6),   # 48 units, XCD ranges: every workgroup keeps one head
+    (3, 24, 24, 5, 12, 6),   # 60 units: the grid is cut from 56 to 40 to keep one head
+    (1, 20, 30, 7, 10, 3),   # 42 units, grid 40 < 8 x 7: every head's bias staged
+    (2, 12, 24, 1, 12, 5),   # one head
     (3, 8, 8, 1, 4, 2),      # N = 16: one full tile
     (2, 16, 16, 4, 8, 4),    # N = 64: four full tiles
     (2, 10, 10, 5, 5, 2),    # odd head count
