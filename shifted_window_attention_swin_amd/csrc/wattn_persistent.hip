@@ -26,8 +26,11 @@
 //              tokens x 64 contiguous bytes.
 //   compute    (head, query tile) items are spread over the waves, a
 //              wave's items being all heads of its query tiles; operands
-//              come from LDS with conflict-free ds_read_b128 (a 1 KB block is
-//              read by the 64 lanes in the order the MFMA layout wants).
+//              come from LDS with ds_read_b128 out of 1 KB blocks whose
+//              16-byte parts are swizzled against bank conflicts.  Units of
+//              one or two heads re-read key tiles and V^T for every item,
+//              which keeps them at 5 workgroups per CU (at most 102 VGPRs);
+//              units of 3-4 heads of small windows keep them in registers.
 //   stores     the HG heads of a token leave one wave back to back as
 //              non-temporal 16-byte stores: whole output cache lines, which
 //              the output never re-reads.
@@ -74,9 +77,15 @@ struct Unit {
   // rotates from unit to unit so that no SIMD sits out all the math
   static constexpr bool ROTATE = ITEMS % kWaves != 0;
   static constexpr int BLOCK = 1024;                       // 16 tokens x 64 bytes
-  // windows of up to 4 tiles keep key tiles, V^T and mask operands in
-  // registers for all items of a wave; larger windows re-read them from LDS
-  static constexpr bool HOLD = NT <= 4;
+  // LEAN: windows of up to 4 tiles with units of one or two heads re-read
+  // key tiles, V^T and mask operands from LDS for every item, so that 5
+  // workgroups fit per CU (at most 102 VGPRs; their one-head-group bias
+  // tables keep 5 units within the LDS)
+  static constexpr bool LEAN = NT <= 4 && HG <= 2;
+  // units of 3 or 4 heads of windows up to 4 tiles keep key tiles, V^T and
+  // mask operands in registers for all items of a wave; the others re-read
+  // them from LDS
+  static constexpr bool HOLD = NT <= 4 && !LEAN;
   static constexpr int MASK_BYTES = HOLD ? 0 : NT * BLOCK;  // key-side mask operands
   static constexpr int BYTES = SLICES * NT * BLOCK + MASK_BYTES;
   static constexpr int block(int s, int t) { return (s * NT + t) * BLOCK; }
@@ -117,8 +126,14 @@ SWA_INLINE void stage_bias_heads(float* s_bias, const float* table, int nh, int 
   }
 }
 
+// waves per SIMD the register allocation must leave room for
 template <int M, int HG>
-__global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_waves<M>() == 3 ? 3 : 1)) void wattn_fwd_bf16_persistent(FwdParams p) {
+constexpr int fwd_minw() {
+  return fwd_waves<M>() == 3 ? 3 : Unit<M, HG>::LEAN ? 5 : 1;
+}
+
+template <int M, int HG>
+__global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void wattn_fwd_bf16_persistent(FwdParams p) {
   using S = Win<M>;
   using U = Unit<M, HG>;
   constexpr int NT = S::NT, NK = S::NK;
@@ -528,7 +543,7 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
   p.own_bias = 0;
   size_t lds = lds_bytes_mh<M, HG>(p.nh);
   long long grid = -1;
-  if constexpr (Win<M>::NT > 4) {
+  if constexpr (Win<M>::NT > 4 || Unit<M, HG>::LEAN) {
     // 9-tile windows: when a workgroup's units all share one head group it
     // stages only that group's bias tables (one head's table instead of
     // nh), which leaves LDS for one more workgroup per CU.  A workgroup
@@ -539,7 +554,7 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
       const size_t small = lds_bytes_mh<M, HG>(HG);
       long long g = fwd_grid<M, HG>(p, dev, cus, small, 1);
       const bool xcd = p.xcd_ranges && g % 8 == 0;
-      const long long q = xcd ? 8LL * p.nhg : p.nhg;
+      const long long q = xcd || Unit<M, HG>::LEAN ? 8LL * p.nhg : p.nhg;
       if (g >= q) g -= g % q;
       if (g % q == 0) {
         grid = g;
