@@ -86,7 +86,9 @@ def fwd_kernel_name(window: int, heads: int) -> str:
     t = (2 * window - 1) ** 2
     tail = 2 * window * (4 * q - window)
     bias = ((heads * t + tail) * 4 + 15) // 16 * 16
-    unit = 3 * hg * nt * 1024 + (nt * 1024 if nt > 4 else 0)
+    # key-side mask operands are staged for 9-tile windows and for units of
+    # one or two heads (which re-read their operands from LDS)
+    unit = 3 * hg * nt * 1024 + (nt * 1024 if nt > 4 or hg <= 2 else 0)
     if bias + unit <= 64 * 1024:
         return f"wattn_fwd_bf16_persistent<{window}, {hg}>"
     return f"wattn_fwd_bf16_kernel<{window}>"
