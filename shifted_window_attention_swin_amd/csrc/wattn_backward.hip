@@ -151,6 +151,11 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
   const char* in = static_cast<const char*>(p.qkv);
   const char* gin = static_cast<const char*>(p.dout);
   const float scale = p.scale;
+  // non-temporal stores (2), except for 9-tile windows, whose one-head
+  // workgroups write 64-byte halves of lines: plain stores let L2 join the
+  // halves of a line (192.9 against 196.8 us at window 12; at window 7 the
+  // one-head path is faster with non-temporal stores, 50.3 against 52.6)
+  constexpr int kStorePolicy = NT > 4 ? 0 : 2;
   // gradients leave through raw buffer stores that every lane issues: the
   // lanes of padded tokens aim past the end of the buffer, where the
   // hardware drops the write.  With no branch around the stores, the wait
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
       __builtin_amdgcn_make_buffer_rsrc(p.dqkv, 0, (int)p.dqkv_bytes, 0x00020000);
   auto store16 = [&](bool valid, unsigned off, const bf16x8& v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), out_rs,
-                                           valid ? (int)off : (int)0xFFFFFFF0u, 0, 2 /* nt */);
+                                           valid ? (int)off : (int)0xFFFFFFF0u, 0, kStorePolicy);
   };
 
   // this workgroup's heads and run of windows: workgroup id -> (XCD x, slot
