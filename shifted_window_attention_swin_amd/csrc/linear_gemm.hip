@@ -147,22 +147,20 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
       a[ks][1] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2 + 1) * 1024);
     }
   }
-  f32x4 bias[2][2], csum[LN ? 2 : 1][2];  // layer norm: row sums of the packed weight
+  // the bias of the lane's 8 channels in each store slot j (zero without a
+  // bias); held for the launch, except with the layer norm (below)
+  auto load_bias = [&](f32x4 (&bv)[2][2]) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    bias[j][0] = bias[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (s_active[j] && p.bias) {
-      bias[j][0] = *reinterpret_cast<const f32x4*>(p.bias + sch[j]);
-      bias[j][1] = *reinterpret_cast<const f32x4*>(p.bias + sch[j] + 4);
-    }
-    if constexpr (LN) {
-      csum[j][0] = csum[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (s_active[j]) {
-        csum[j][0] = *reinterpret_cast<const f32x4*>(p.colsum + sch[j]);
-        csum[j][1] = *reinterpret_cast<const f32x4*>(p.colsum + sch[j] + 4);
+    for (int j = 0; j < 2; ++j) {
+      bv[j][0] = bv[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s_active[j] && p.bias) {
+        bv[j][0] = *reinterpret_cast<const f32x4*>(p.bias + sch[j]);
+        bv[j][1] = *reinterpret_cast<const f32x4*>(p.bias + sch[j] + 4);
       }
     }
-  }
+  };
+  f32x4 bias[2][2];
+  if constexpr (!LN) load_bias(bias);
 
   // Layer norm, folded into the weights: with z the unit-normalised row,
   //   y_j = sum_c (z_c gamma_c + beta_c) W_jc + b_j
@@ -182,26 +180,28 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
     for (int t0 = wv * TPW_LN; t0 < kLinRows; t0 += kLinWaves * TPW_LN) {  // wave-uniform
       const int t = t0 + lane / LL;
       const char* tile = s_x + (t >> 4) * KS * 1024;
-      float v[CPL][8];
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
+      // the lane's chunks are read twice (mean, then the variance about it)
+      // rather than held: holding 8 CPL floats would cost the registers of a
+      // fourth wave per SIMD
+      auto chunk = [&](int k) {
         const int q = ql + LL * k;
-        const bf16x8 h =
-            *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * 1024 + uchunk(t & 15, q & 3));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[k][e] = (float)h[e];
-      }
+        return *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * 1024 + uchunk(t & 15, q & 3));
+      };
       float s1 = 0.f;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k)
+      for (int k = 0; k < CPL; ++k) {
+        const bf16x8 h = chunk(k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s1 += v[k][e];
+        for (int e = 0; e < 8; ++e) s1 += (float)h[e];
+      }
       const float mu = group_sum<LL>(s1) * (1.f / (KS * 32));
       float s2 = 0.f;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k)
+      for (int k = 0; k < CPL; ++k) {
+        const bf16x8 h = chunk(k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s2 += (v[k][e] - mu) * (v[k][e] - mu);
+        for (int e = 0; e < 8; ++e) s2 += ((float)h[e] - mu) * ((float)h[e] - mu);
+      }
       const float rs = rsqrtf(group_sum<LL>(s2) * (1.f / (KS * 32)) + p.eps);
       if (ql == 0) s_stat[t] = make_float2(mu, rs);
     }
@@ -277,6 +277,21 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
       }
     } else if constexpr (LN) {
       ln_stats();
+    }
+    // layer norm: the bias and the row sums of the packed weight for the
+    // lane's 8 channels, read from cache for every row block rather than
+    // held for the launch (32 registers fewer)
+    f32x4 csum[LN ? 2 : 1][2];
+    if constexpr (LN) {
+      load_bias(bias);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        csum[j][0] = csum[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s_active[j]) {
+          csum[j][0] = *reinterpret_cast<const f32x4*>(p.colsum + sch[j]);
+          csum[j][1] = *reinterpret_cast<const f32x4*>(p.colsum + sch[j] + 4);
+        }
+      }
     }
     __syncthreads();  // output tile complete
 #pragma unroll
