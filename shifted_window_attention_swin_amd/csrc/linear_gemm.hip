@@ -66,8 +66,9 @@ SWA_INLINE float group_sum(float v) {
 }
 
 // LDS of the layer norm, after the x and output tiles: (mean, 1/sigma) of
-// the row block's tokens
-constexpr size_t lin_ln_lds_bytes() { return kLinRows * 8; }
+// the row block's tokens, then the bias and the packed weight's row sums of
+// the workgroup's 32 * waves output channels
+constexpr size_t lin_ln_lds_bytes(int waves) { return kLinRows * 8 + 2 * 32 * waves * 4; }
 
 // WAVES waves per workgroup, one 32-column block each: the workgroup's
 // WAVES * 32 channels are WAVES / 2 whole 128-byte lines of every token.
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   char* s_x = s_lds;              // NB blocks of 1 KB: the row block of x
   char* s_o = s_lds + NB * 1024;  // kLinRows x kOutStride: the fp32 output tile
   float2* s_stat = reinterpret_cast<float2*>(s_o + kLinRows * kOutStride);  // layer norm
+  float* s_cst = reinterpret_cast<float*>(s_stat + kLinRows);  // [bias | row sums][kLinCols]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -161,6 +163,18 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   };
   f32x4 bias[2][2];
   if constexpr (!LN) load_bias(bias);
+  // layer norm: the bias and row sums of the workgroup's channels go to LDS
+  // once (made visible by the first barrier of the row-block loop): held
+  // in registers they would cost 32 VGPRs, and read from memory per row
+  // block their wait would also wait for the next row block's loads
+  if constexpr (LN) {
+    for (int e = tid; e < 2 * kLinCols; e += kLinWaves * 64) {
+      const int ch = cg * kLinCols + (e % kLinCols);
+      float v = 0.f;
+      if (ch < p.N) v = e < kLinCols ? (p.bias ? p.bias[ch] : 0.f) : p.colsum[ch];
+      s_cst[e] = v;
+    }
+  }
 
   // Layer norm, folded into the weights: with z the unit-normalised row,
   //   y_j = sum_c (z_c gamma_c + beta_c) W_jc + b_j
@@ -278,21 +292,6 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
     } else if constexpr (LN) {
       ln_stats();
     }
-    // layer norm: the bias and the row sums of the packed weight for the
-    // lane's 8 channels, read from cache for every row block rather than
-    // held for the launch (32 registers fewer)
-    f32x4 csum[LN ? 2 : 1][2];
-    if constexpr (LN) {
-      load_bias(bias);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        csum[j][0] = csum[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (s_active[j]) {
-          csum[j][0] = *reinterpret_cast<const f32x4*>(p.colsum + sch[j]);
-          csum[j][1] = *reinterpret_cast<const f32x4*>(p.colsum + sch[j] + 4);
-        }
-      }
-    }
     __syncthreads();  // output tile complete
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -301,14 +300,23 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
         const char* o = s_o + srow[j] * kOutStride + (sch[j] - cg * kLinCols) * 4;
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(o);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(o + 16);
+        // layer norm: bias and row sums of the lane's 8 channels, from LDS
+        f32x4 b0, b1, cs0, cs1;
+        if constexpr (LN) {
+          const float* cc = s_cst + (sch[j] - cg * kLinCols);
+          b0 = *reinterpret_cast<const f32x4*>(cc);
+          b1 = *reinterpret_cast<const f32x4*>(cc + 4);
+          cs0 = *reinterpret_cast<const f32x4*>(cc + kLinCols);
+          cs1 = *reinterpret_cast<const f32x4*>(cc + kLinCols + 4);
+        }
         bf16x8 out;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float y0, y1;
           if constexpr (LN) {
             const float2 st = s_stat[srow[j]];  // (mean, 1/sigma) of the token
-            y0 = (v0[q] - st.x * csum[j][0][q]) * st.y + bias[j][0][q];
-            y1 = (v1[q] - st.x * csum[j][1][q]) * st.y + bias[j][1][q];
+            y0 = (v0[q] - st.x * cs0[q]) * st.y + b0[q];
+            y1 = (v1[q] - st.x * cs1[q]) * st.y + b1[q];
           } else {
             y0 = v0[q] + bias[j][0][q];
             y1 = v1[q] + bias[j][1][q];
@@ -378,7 +386,7 @@ int linear_waves(int ncb) { return ncb % 6 == 0 ? 6 : ncb % 4 == 0 ? 4 : 2; }
 
 size_t linear_lds_waves(int K, int waves) {
   return (size_t)kLinTiles * (K / 32) * 1024 + (size_t)kLinRows * lin_out_stride(waves) +
-         lin_ln_lds_bytes();
+         lin_ln_lds_bytes(waves);
 }
 
 template <int KS, int MODE, int WAVES>
