@@ -46,6 +46,8 @@
 namespace swinattn {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kLinRows = 32;               // tokens per row block: 2 tiles of 16
 constexpr int kLinTiles = kLinRows / 16;
 // bytes per token of the fp32 output tile of a WAVES-wave workgroup (padded)
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   // epilogue, so they are computed from LDS while the products are in
   // flight: LL lanes per token, CPL 16-byte chunks of its row per lane
   // (chunk q = ql + LL k: k-step q / 4, part q % 4), DPP sums over the group
-  // (mean first, then the biased variance about it).
+  // of the row sum and the sum of squares.
   constexpr int LL = KS % 2 == 0 ? 8 : 4;                 // lanes per token
   constexpr int CPL = KS * 4 / LL;                        // chunks per lane
   constexpr int TPW_LN = 64 / LL;                         // tokens per wave and pass
@@ -194,29 +196,28 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
     for (int t0 = wv * TPW_LN; t0 < kLinRows; t0 += kLinWaves * TPW_LN) {  // wave-uniform
       const int t = t0 + lane / LL;
       const char* tile = s_x + (t >> 4) * KS * 1024;
-      // the lane's chunks are read twice (mean, then the variance about it)
-      // rather than held: holding 8 CPL floats would cost the registers of a
-      // fourth wave per SIMD
-      auto chunk = [&](int k) {
+      // one pass of bf16 dot products over the lane's chunks: the sum and
+      // the sum of squares (each product exact in fp32); K var is formed as
+      // S2 - S1^2 / K, which keeps the mean's rounding out of it
+      float s1 = 0.f, s2 = 0.f;
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
         const int q = ql + LL * k;
-        return *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * 1024 + uchunk(t & 15, q & 3));
-      };
-      float s1 = 0.f;
+        const bf16x8 h =
+            *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * 1024 + uchunk(t & 15, q & 3));
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const bf16x8 h = chunk(k);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s1 += (float)h[e];
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 pr = {h[2 * e], h[2 * e + 1]};
+          s1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, s1, false);
+          s2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, s2, false);
+        }
       }
-      const float mu = group_sum<LL>(s1) * (1.f / (KS * 32));
-      float s2 = 0.f;
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const bf16x8 h = chunk(k);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s2 += ((float)h[e] - mu) * ((float)h[e] - mu);
-      }
-      const float rs = rsqrtf(group_sum<LL>(s2) * (1.f / (KS * 32)) + p.eps);
+      const float S1 = group_sum<LL>(s1), S2 = group_sum<LL>(s2);
+      constexpr float kInvK = 1.f / (KS * 32);
+      const float mu = S1 * kInvK;
+      const float s2c = fmaxf(S2 - S1 * S1 * kInvK, 0.f);  // K times the biased variance
+      const float rs = rsqrtf(s2c * kInvK + p.eps);
       if (ql == 0) s_stat[t] = make_float2(mu, rs);
     }
   };
