@@ -564,6 +564,14 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
     }
   }
   if (grid < 0) grid = fwd_grid<M, HG>(p, dev, cus, lds, 0);
+  // launches of at most two units per workgroup walk one contiguous range
+  // per XCD (Swin-T stage 3: 10.6 -> 10.0 us); longer ones keep grid order,
+  // which keeps the units in flight one compact stretch of the batch
+  // (Swin-L stage 1: 58.4 against 61.6 us with XCD ranges).  A one-head-
+  // group grid is then a multiple of 8 nhg already, as XCD ranges need.
+  if (!p.xcd_ranges && p.nhg > 1 && grid % 8 == 0 && p.units <= 2 * grid &&
+      (!p.own_bias || (grid / 8) % p.nhg == 0))
+    p.xcd_ranges = 1;
   hipLaunchKernelGGL((wattn_fwd_bf16_persistent<M, HG>), dim3((unsigned)grid),
                      dim3(Unit<M, HG>::kWaves * 64), lds, st, p);
   return hipGetLastError();
