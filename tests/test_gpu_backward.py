@@ -163,3 +163,41 @@ def test_backward_full_size(name):
             print(f"    image {b} d{comp}: max_abs={e.max():.3e} mean_abs={e.mean():.3e}", flush=True)
             assert np.isfinite(dq[b]).all()
             assert e.max() <= 2.0**-6 * ref.max() + 1e-6 and e.mean() <= 2.0**-8 * ref.mean() + 1e-7
+
+
+def test_backward_batch_split_over_2gib():
+    """600 images of the Swin-L stage-1 shape are 2.17 GB of qkv: the host
+    splits the batch into launches of 594 and 6 images (32-bit in-kernel
+    offsets).  Eight distinct images (and their output gradients) are tiled
+    along the batch on the device, so the gradients of any image are those
+    of its source image, and the table gradient is 75 times that of the
+    eight (it sums over every image of both launches)."""
+    w = synth.WORKLOADS["swin-l-s1"]
+    H, W, nh, M, s = w["H"], w["W"], w["heads"], w["window"], w["shifts"][0]
+    qkv8, table = synth.workload_inputs("swin-l-s1", batch=8)
+    dout8 = _dout(8, H, W, nh * 32, seed=w["seed"])
+    B = 600
+    _say(f"bwd batch split B={B}")
+    q = _bf16_dev(qkv8).repeat(B // 8, 1, 1, 1, 1, 1)
+    g = _bf16_dev(dout8).repeat(B // 8, 1, 1, 1)
+    t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.float32)).to(_dev())
+    dq = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=_dev())
+    dt = torch.full(t.shape, float("nan"), dtype=torch.float32, device=_dev())
+    swa.check(swa.swin_wattn_bwd(q, t, g, dq, dt, B, H, W, nh, 32, M, s), "bwd")
+    torch.cuda.synchronize()
+    rq, rt = oracle.swin_wattn_bwd(qkv8, table, dout8, M, s)
+    got_t = dt.cpu().numpy().astype(np.float64)
+    ref_t = 75.0 * rt
+    et = np.abs(got_t - ref_t).max()
+    print(f"    dtable max_err={et:.3e} (|ref| max {np.abs(ref_t).max():.3e})", flush=True)
+    assert np.isfinite(got_t).all() and et <= 1e-3 * np.abs(ref_t).max() + 1e-6
+    for b in (0, 593, 594, 595, 599):
+        got = dq[b].float().cpu().numpy().astype(np.float64)
+        for i, comp in enumerate("qkv"):
+            e = np.abs(got[:, :, i] - rq[b % 8, :, :, i])
+            ref = np.abs(rq[b % 8, :, :, i])
+            print(f"    image {b} d{comp}: max_abs={e.max():.3e} mean_abs={e.mean():.3e}", flush=True)
+            assert np.isfinite(got).all()
+            assert e.max() <= 2.0**-6 * ref.max() + 1e-6 and e.mean() <= 2.0**-8 * ref.mean() + 1e-7
+    del q, g, dq
+    torch.cuda.empty_cache()
