@@ -166,6 +166,8 @@ def test_bf16_workloads_full_size_sampled(name):
     (1, 6, 6, 2, 6, 3),      # N = 36
     (2, 6, 4, 2, 2, 1),      # tiny windows
     (1, 3, 3, 1, 1, 0),      # window 1: each token attends to itself
+    (2, 14, 14, 7, 7, 3),    # 7 heads: one-head units, grid cut to 8 x 7 with XCD ranges
+    (4, 14, 14, 4, 7, 3),    # 4 heads: two-head units, a small launch in XCD ranges
     (1, 14, 14, 12, 7, 3),   # many heads per window
     (1, 14, 14, 16, 7, 0),
 ])
