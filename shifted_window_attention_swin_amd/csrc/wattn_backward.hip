@@ -8,13 +8,16 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P o (dP - D),
 //   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dtable[rel(i,j)] += dS_ij.
 //
-//   unit      (image, window, head): q, k, v and dO of the head, each 16-token
-//             tile a 1 KB LDS block (16 tokens x 64 B), staged like the
-//             forward's (register prefetch of the next unit).
-//   streams   a workgroup keeps one head and walks a contiguous run of
-//             windows; the nh workgroups of one run (its nh heads) sit on
-//             one XCD and walk it in step, so the 128-byte lines that hold
-//             two heads of a token are fetched into one L2.
+//   unit      (image, window, head or head pair): q, k, v and dO of the
+//             heads, each 16-token tile a 1 KB LDS block (16 tokens x 64 B,
+//             16-byte parts swizzled against bank conflicts), staged like
+//             the forward's (register prefetch of the next unit, issued at
+//             raised wave priority).
+//   streams   a workgroup keeps one head (or a pair of heads whose 64-byte
+//             rows share the 128-byte lines of a token) and walks a
+//             contiguous run of at least 8 windows; the head groups of one
+//             run sit on one XCD and walk it in step, so the lines that
+//             hold several heads of a token are fetched into one L2.
 //   waves     one per 16-token tile of the head: 4 per head for windows up
 //             to 8 (1 or 4 tiles), 9 for windows of 9 to 12 (whose P and dS
 //             blocks, 81 KB, leave room for one workgroup per CU)
@@ -23,18 +26,21 @@
 //             S^T and P (fp32, exact softmax), dP^T = V dO^T, D, dS^T, and
 //             dQ^T = K^T dS^T (K^T from transposing LDS reads, as the
 //             forward's V^T).  P and dS go to LDS in bf16 as 16 x 16 blocks
-//             [query][key], one per (query tile, key tile).
+//             [query][key], one per (query tile, key tile), their 8-byte key
+//             groups swizzled by query row.
 //   phase 2   one wave per key tile: dV^T += dO^T P and dK^T += Q^T dS on
 //             16x16x16 MFMAs, their B operands read out of the P and dS
 //             blocks with transposing LDS reads (4 queries of a key per
 //             lane), dO^T and Q^T from transposing reads of the unit.
 //   bias grad the (query, key) pair of a phase-1 accumulator slot of a lane
 //             is the same in every window, hence so is its table row: each
-//             lane sums the fp32 dS of its 4 x tiles slots in registers over all its
-//             workgroup's windows (one head), then adds them once into an
-//             LDS copy of the head's table gradient (LDS atomics), which goes
-//             to HBM with global atomics.
-//   output    dQ, dK, dV of a token leave as 16-byte stores of 8 channels.
+//             lane sums the fp32 dS of its 4 x tiles slots in registers over
+//             all its workgroup's windows, then adds them once into an LDS
+//             copy of the head's table gradient (LDS atomics), which goes to
+//             HBM with global atomics.
+//   output    head pairs: dQ, dK, dV go through a swizzled LDS tile and leave
+//             as whole 128-byte lines; one head: 16-byte stores of 8
+//             channels of the lane's token.
 
 #include <atomic>
 

@@ -14,16 +14,18 @@
 //   workgroup  4 waves (3 for 9-tile windows), persistent: the grid walks
 //              the units in order, so the units in flight are one compact
 //              stretch of the batch; when the units of a window share cache
-//              lines, each XCD instead walks its own contiguous range (one
-//              L2 per line).  A workgroup whose units all belong to one head
-//              group stages only that group's bias tables.
-//   pipeline   the next unit's 16-byte loads are issued into registers right
-//              after the current unit is written to LDS, and stay in flight
-//              while the current unit is computed out of LDS.
-//   loads      wave w loads tile w of every slice: a lane owns one token and
-//              one 16-byte part of it, so the shift/partition index map is
-//              one address per lane per unit.  A load instruction covers 16
-//              tokens x 64 contiguous bytes.
+//              lines, or a launch has at most two units per workgroup, each
+//              XCD instead walks its own contiguous range.  A workgroup
+//              whose units all belong to one head group stages only that
+//              group's bias tables.
+//   pipeline   the next unit's 16-byte loads are issued into registers, at
+//              raised wave priority, right after the current unit is
+//              written to LDS, and stay in flight while the current unit is
+//              computed out of LDS.
+//   loads      wave w of W loads tiles w, w + W, ... of every slice: a lane
+//              owns one token and one 16-byte part of it, so the
+//              shift/partition index map is one address per lane per tile.
+//              A load instruction covers 16 tokens x 64 contiguous bytes.
 //   compute    (head, query tile) items are spread over the waves, a
 //              wave's items being all heads of its query tiles; operands
 //              come from LDS with ds_read_b128 out of 1 KB blocks whose
@@ -32,8 +34,8 @@
 //              which keeps them at 5 workgroups per CU (at most 102 VGPRs);
 //              units of 3-4 heads of small windows keep them in registers.
 //   stores     the HG heads of a token leave one wave back to back as
-//              non-temporal 16-byte stores: whole output cache lines, which
-//              the output never re-reads.
+//              non-temporal 16-byte stores (whole output lines when HG is
+//              even), which the output never re-reads.
 //
 // The attention math per item is the one described in wattn_kernels.hip.
 
