@@ -172,9 +172,15 @@ int swin_ln_linear_fwd(const void* x, const void* packed_weight, const float* co
 
 /* Copies of the precomputed tensors into caller-owned device memory, queued
  * on `stream` (for verification).  SWIN_ERR_NOT_PREPARED without a prior
- * swin_wattn_precompute for the key.
+ * swin_wattn_precompute for the key.  `stream` may differ from the
+ * precompute's stream: the copy is queued behind the precompute's fill (an
+ * event recorded at setup), never ahead of it.
  *   index  [N][N] int32;  mask [nW][N][N] float32;
- *   region [nW][N] uint8 region labels (label = 3*band_y + band_x). */
+ *   region [nW][N] uint8 region labels (label = 3*band_y + band_x).
+ * The index depends on the window only, but the cache is keyed by
+ * (device, H, W, window, shift) like the mask and the labels, so the index
+ * copy names the same key; each copy takes the caller's stream so that it
+ * is ordered with the caller's other work. */
 int swin_wattn_copy_index(int H, int W, int window, int shift, int32_t* dst, void* stream);
 int swin_wattn_copy_mask(int H, int W, int window, int shift, float* dst, void* stream);
 int swin_wattn_copy_region(int H, int W, int window, int shift, uint8_t* dst, void* stream);
@@ -182,7 +188,9 @@ int swin_wattn_copy_region(int H, int W, int window, int shift, uint8_t* dst, vo
 /* Frees every precomputed buffer on every device (synchronises each device
  * first).  Afterwards the copy calls return SWIN_ERR_NOT_PREPARED until the
  * next precompute; the forward calls are unaffected.  Must not run
- * concurrently with other calls. */
+ * concurrently with other calls.  Returns SWIN_OK, or SWIN_ERR_HIP when a
+ * device could not be synchronised or a buffer not freed (the cache is
+ * emptied either way), so that a failure is not silent. */
 int swin_wattn_release(void);
 
 /* Static, human-readable name of a status code. */

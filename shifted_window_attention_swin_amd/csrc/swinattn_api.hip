@@ -30,6 +30,9 @@ struct Prepared {
   int32_t* rel_index;
   float* mask;
   uint8_t* region;
+  // recorded on the precompute's stream after its fill: a copy on any other
+  // stream waits for it, so it never reads the tensors before they are written
+  hipEvent_t ready;
 };
 
 std::mutex g_mu;
@@ -181,8 +184,9 @@ int copy_common(int H, int W, int M, int s, void* dst, int which, void* stream) 
                     : which == 1 ? (const void*)e->mask
                                  : (const void*)e->region;
   const size_t bytes = which == 0 ? N * N * 4 : which == 1 ? nW * N * N * 4 : nW * N;
-  const hipError_t err =
-      hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamWaitEvent(st, e->ready, 0) != hipSuccess) return SWIN_ERR_HIP;
+  const hipError_t err = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
   return err == hipSuccess ? SWIN_OK : SWIN_ERR_HIP;
 }
 
@@ -212,9 +216,15 @@ int swin_wattn_precompute(int H, int W, int window, int shift, void* stream) {
   e.rel_index = reinterpret_cast<int32_t*>(base);
   e.mask = reinterpret_cast<float*>(base + b_idx);
   e.region = reinterpret_cast<uint8_t*>(base + b_idx + b_mask);
-  const hipError_t err = launch_precompute(H, W, window, shift, e.rel_index, e.mask, e.region,
-                                           static_cast<hipStream_t>(stream));
-  if (err != hipSuccess) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipEventCreateWithFlags(&e.ready, hipEventDisableTiming) != hipSuccess) {
+    (void)hipFree(block);
+    return SWIN_ERR_HIP;
+  }
+  if (launch_precompute(H, W, window, shift, e.rel_index, e.mask, e.region, st) != hipSuccess ||
+      hipEventRecord(e.ready, st) != hipSuccess) {
+    (void)hipStreamSynchronize(st);
+    (void)hipEventDestroy(e.ready);
     (void)hipFree(block);
     return SWIN_ERR_HIP;
   }
@@ -416,7 +426,7 @@ int swin_wattn_release(void) {
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   for (auto& e : g_cache) {
     if (hipSetDevice(e.dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-        hipFree(e.block) != hipSuccess)
+        hipEventDestroy(e.ready) != hipSuccess || hipFree(e.block) != hipSuccess)
       status = SWIN_ERR_HIP;
   }
   g_cache.clear();

@@ -14,11 +14,6 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define SWA_INLINE __device__ __forceinline__
 
-#ifndef SWA_PREFETCH
-#define SWA_PREFETCH 0
-#endif
-constexpr bool kPrefetch = SWA_PREFETCH != 0;
-
 template <int M>
 struct Win {
   static constexpr int Q = (M + 3) / 4;        // 4-token quads per row and 4-row groups

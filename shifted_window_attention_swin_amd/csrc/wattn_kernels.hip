@@ -242,32 +242,16 @@ SWA_INLINE void head_bf16(const HeadCtx& hc, const LaneWindow<M>& lw, int h, boo
   }
 }
 
-// Heads h = wave, wave + nwaves, ...  With PREFETCH the loads of the next
-// head are issued before the math of the current one (two register buffers,
-// no copies); without it latency is hidden by the other resident waves.
-template <int M, bool PREFETCH>
+// Heads h = wave, wave + nwaves, ...: the first head's tiles are loaded by
+// the caller, the others here; latency is hidden by the other resident waves.
+template <int M>
 SWA_INLINE void run_heads_bf16(const HeadCtx& hc, const LaneWindow<M>& lw, const char* in,
                                unsigned Cb, int nh, int wave, int nwaves, bool masked,
                                bf16x8 (&qa)[Win<M>::NT], bf16x8 (&ka)[Win<M>::NT],
                                bf16x8 (&va)[Win<M>::NT]) {
-  constexpr int NT = Win<M>::NT;
-  if (!PREFETCH) {
-    for (int h = wave; h < nh; h += nwaves) {
-      if (h != wave) load_head_bf16<M>(in + h * kHeadDim * 2, lw, Cb, qa, ka, va);
-      head_bf16<M>(hc, lw, h, masked, qa, ka, va);
-    }
-    return;
-  }
-  bf16x8 qb[NT], kb[NT], vb[NT];
-  for (int h = wave; h < nh;) {
-    const int h1 = h + nwaves;
-    if (h1 < nh) load_head_bf16<M>(in + h1 * kHeadDim * 2, lw, Cb, qb, kb, vb);
+  for (int h = wave; h < nh; h += nwaves) {
+    if (h != wave) load_head_bf16<M>(in + h * kHeadDim * 2, lw, Cb, qa, ka, va);
     head_bf16<M>(hc, lw, h, masked, qa, ka, va);
-    if (h1 >= nh) break;
-    const int h2 = h1 + nwaves;
-    if (h2 < nh) load_head_bf16<M>(in + h2 * kHeadDim * 2, lw, Cb, qa, ka, va);
-    head_bf16<M>(hc, lw, h1, masked, qb, kb, vb);
-    h = h2;
   }
 }
 
@@ -307,7 +291,7 @@ __global__ __launch_bounds__(256) void wattn_fwd_bf16_kernel(FwdParams p) {
 
   const bool masked = window_masked(p.shift, w / p.nWx, w % p.nWx, p.nWy, p.nWx);
   if (masked) lw.template init_labels<S::MASK_MFMA>(p, w, g, c);
-  run_heads_bf16<M, kPrefetch>(hc, lw, in, Cb, nh, wave, nwaves, masked, q, k, v);
+  run_heads_bf16<M>(hc, lw, in, Cb, nh, wave, nwaves, masked, q, k, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -319,22 +303,31 @@ SWA_INLINE void head_f32(const FwdParams& p, const LaneWindow<M>& lw, const floa
                          const char* in, char* out, int h, int g, int c, bool g_ok, bool masked) {
   using S = Win<M>;
   constexpr int NT = S::NT;
+  // windows of up to 4 tiles hold every key tile and V^T for all query
+  // tiles; larger windows re-read them (from cache) per query tile, which
+  // keeps the kernel within its registers
+  constexpr bool HOLD = NT <= 4;
+  constexpr int NH = HOLD ? NT : 1;
   const unsigned Cb = (unsigned)p.nh * kHeadDim * 4;
   const char* in_h = in + h * kHeadDim * 4;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  f32x4 vt[NT][2], kk[NT][2];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    f32x4 v0 = z, v1 = z, k0 = z, k1 = z;
+  // key tile t (its two 4-channel halves) and V^T of tile t
+  auto load_k = [&](int t, f32x4 (&k)[2]) {
+    k[0] = z;
+    k[1] = z;
     if (lw.ok[t]) {
-      const char* src = in_h + lw.in_off[t];
-      k0 = *reinterpret_cast<const f32x4*>(src + Cb);
-      k1 = *reinterpret_cast<const f32x4*>(src + Cb + 16);
-      v0 = *reinterpret_cast<const f32x4*>(src + 2 * Cb);
-      v1 = *reinterpret_cast<const f32x4*>(src + 2 * Cb + 16);
+      const char* src = in_h + lw.in_off[t] + Cb;
+      k[0] = *reinterpret_cast<const f32x4*>(src);
+      k[1] = *reinterpret_cast<const f32x4*>(src + 16);
     }
-    kk[t][0] = k0;
-    kk[t][1] = k1;
+  };
+  auto load_vt = [&](int t, f32x4 (&vt)[2]) {
+    f32x4 v0 = z, v1 = z;
+    if (lw.ok[t]) {
+      const char* src = in_h + lw.in_off[t] + 2 * Cb;
+      v0 = *reinterpret_cast<const f32x4*>(src);
+      v1 = *reinterpret_cast<const f32x4*>(src + 16);
+    }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       f32x4 acc = z;
@@ -344,12 +337,23 @@ SWA_INLINE void head_f32(const FwdParams& p, const LaneWindow<M>& lw, const floa
         const float vv = st < 4 ? v0[st] : v1[st - 4];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sv, acc, 0, 0, 0);
       }
-      vt[t][hf] = acc;
+      vt[hf] = acc;
+    }
+  };
+  f32x4 kk[NH][2], vt[NH][2];
+  if constexpr (HOLD) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      load_k(t, kk[t]);
+      load_vt(t, vt[t]);
     }
   }
   const int hbase = h * S::T;
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
+    // re-read tiles: an address opaque to the compiler per query tile, so
+    // the loads of different query tiles are not merged (and held)
+    if constexpr (!HOLD) asm volatile("" : "+v"(in_h));
     f32x4 q0 = z, q1 = z;
     if (lw.ok[it]) {
       const char* src = in_h + lw.in_off[it];
@@ -360,9 +364,16 @@ SWA_INLINE void head_f32(const FwdParams& p, const LaneWindow<M>& lw, const floa
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
       f32x4 acc = lw.score_init(s_bias, hbase, it, jt, g_ok, masked, p.mask_value);
+      f32x4 kj[2];
+      if constexpr (HOLD) {
+        kj[0] = kk[jt][0];
+        kj[1] = kk[jt][1];
+      } else {
+        load_k(jt, kj);
+      }
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const float ka = st < 4 ? kk[jt][0][st] : kk[jt][1][st - 4];
+        const float ka = st < 4 ? kj[0][st] : kj[1][st - 4];
         const float qb = st < 4 ? q0[st] : q1[st - 4];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, qb, acc, 0, 0, 0);
       }
@@ -371,20 +382,30 @@ SWA_INLINE void head_f32(const FwdParams& p, const LaneWindow<M>& lw, const floa
     softmax_numerators<M>(s, p.score_scale);
     f32x4 o0 = z, o1 = z, l4 = z;
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt)
+    for (int jt = 0; jt < NT; ++jt) {
+      f32x4 vj[2];
+      if constexpr (HOLD) {
+        vj[0] = vt[jt][0];
+        vj[1] = vt[jt][1];
+      } else {
+        load_vt(jt, vj);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (!S::col_ok(jt, r)) continue;
-        o0 = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[jt][0][r], s[jt][r], o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[jt][1][r], s[jt][r], o1, 0, 0, 0);
+        o0 = __builtin_amdgcn_mfma_f32_16x16x4f32(vj[0][r], s[jt][r], o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(vj[1][r], s[jt][r], o1, 0, 0, 0);
         l4 = __builtin_amdgcn_mfma_f32_16x16x4f32(1.f, s[jt][r], l4, 0, 0, 0);
       }
+    }
     if (lw.ok[it]) {
       const float inv = fast_rcp(l4[0]);
       char* dst = out + h * kHeadDim * 4 + lw.out_off[it];
       *reinterpret_cast<f32x4*>(dst) = o0 * inv;
       *reinterpret_cast<f32x4*>(dst + 16) = o1 * inv;
     }
+    // keep query tiles apart: interleaving them only raises register pressure
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

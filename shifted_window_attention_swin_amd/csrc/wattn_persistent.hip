@@ -54,11 +54,6 @@ template <int M>
 constexpr int fwd_waves() {
   return Win<M>::NT > 4 ? 3 : 4;
 }
-#ifndef SWA_PF_DEPTH
-#define SWA_PF_DEPTH 1
-#endif
-constexpr int kDepth = SWA_PF_DEPTH;  // units whose loads are in flight during the math
-
 template <int M, int HG>
 struct Unit {
   using S = Win<M>;
@@ -74,9 +69,11 @@ struct Unit {
   static constexpr bool HEAD_INNER = HG > 1 && IPW % HG == 0;
   // every wave's items belong to one head: key / value tiles load once
   static constexpr bool ONE_HEAD = !HEAD_INNER && ITEMS % kWaves == 0 && NT % IPW == 0;
-  // items that do not divide evenly over the waves (9 query tiles of one
-  // head at windows 9 to 12) leave the last wave short; the short wave
-  // rotates from unit to unit so that no SIMD sits out all the math
+  // items that do not divide evenly over the waves leave the last wave
+  // short; the short wave rotates from unit to unit so that no SIMD sits out
+  // all the math.  With 4 waves this applies to units of 1-tile windows (HG
+  // items) when HG is not a multiple of 4; the 9 query tiles of a one-head
+  // unit of windows 9 to 12 divide evenly over their 3 waves
   static constexpr bool ROTATE = ITEMS % kWaves != 0;
   static constexpr int BLOCK = 1024;                       // 16 tokens x 64 bytes
   // LEAN: windows of up to 4 tiles with units of one or two heads re-read
@@ -442,64 +439,30 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
     }
   };
 
-  // software pipeline: the loads of the next kDepth units are in flight
-  // while a unit is written to LDS and computed
-  if (kDepth == 1) {
-    Regs R;
-    int rot = 0;
-    Pos nxt = decode(u);
-    if (u < u_end) issue_loads(R, nxt);
-    // the bias table (reversed, divided by the scale) is staged while the
-    // first unit's loads are in flight
-    stage_bias_heads<M>(s_bias, p.table, nh, hbase, p.own_bias ? HG : nh, p.inv_scale);
-    __syncthreads();  // bias table visible
-    for (; u < u_end; u += u_step) {
-      write_unit(R);
-      write_mask(nxt);
-      __syncthreads();  // unit visible to every wave
-      const Pos cur = nxt;
-      if (u + u_step < u_end) {
-        nxt = decode(u + u_step);
-        // the loads leave ahead of the other workgroups' math on the SIMD
-        __builtin_amdgcn_s_setprio(3);
-        issue_loads(R, nxt);
-        __builtin_amdgcn_s_setprio(0);
-      }
-      process(cur, rot++);
-      __syncthreads();  // every wave is done with the unit before it is overwritten
+  // software pipeline: the next unit's loads are in flight while a unit is
+  // written to LDS and computed
+  Regs R;
+  int rot = 0;
+  Pos nxt = decode(u);
+  if (u < u_end) issue_loads(R, nxt);
+  // the bias table (reversed, divided by the scale) is staged while the
+  // first unit's loads are in flight
+  stage_bias_heads<M>(s_bias, p.table, nh, hbase, p.own_bias ? HG : nh, p.inv_scale);
+  __syncthreads();  // bias table visible
+  for (; u < u_end; u += u_step) {
+    write_unit(R);
+    write_mask(nxt);
+    __syncthreads();  // unit visible to every wave
+    const Pos cur = nxt;
+    if (u + u_step < u_end) {
+      nxt = decode(u + u_step);
+      // the loads leave ahead of the other workgroups' math on the SIMD
+      __builtin_amdgcn_s_setprio(3);
+      issue_loads(R, nxt);
+      __builtin_amdgcn_s_setprio(0);
     }
-  } else {
-    Regs R0, R1;
-    Pos p0 = decode(u), p1 = decode(u + u_step);
-    if (u < u_end) issue_loads(R0, p0);
-    if (u + u_step < u_end) issue_loads(R1, p1);
-    stage_bias_heads<M>(s_bias, p.table, nh, hbase, p.own_bias ? HG : nh, p.inv_scale);
-    __syncthreads();  // bias table visible
-    while (u < u_end) {
-      write_unit(R0);
-      write_mask(p0);
-      __syncthreads();
-      Pos cur = p0;
-      if (u + 2 * u_step < u_end) {
-        p0 = decode(u + 2 * u_step);
-        issue_loads(R0, p0);
-      }
-      process(cur, 0);
-      __syncthreads();
-      u += u_step;
-      if (u >= u_end) break;
-      write_unit(R1);
-      write_mask(p1);
-      __syncthreads();
-      cur = p1;
-      if (u + 2 * u_step < u_end) {
-        p1 = decode(u + 2 * u_step);
-        issue_loads(R1, p1);
-      }
-      process(cur, 1);
-      __syncthreads();
-      u += u_step;
-    }
+    process(cur, rot++);
+    __syncthreads();  // every wave is done with the unit before it is overwritten
   }
 }
 

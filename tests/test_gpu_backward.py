@@ -141,8 +141,8 @@ def test_backward_zero_batch_zeroes_dtable():
 def test_backward_full_size(name):
     """Swin-L stage 1 (B=64, the benchmark's batch and launch configuration)
     and Swin-L at 384 px (B=16, window 12) at full size: the oracle computes
-    the whole backward; dq, dk, dv are compared on three sampled images, the
-    table gradient (a sum over every image) in full."""
+    the whole backward, and dq, dk, dv of every image and the table gradient
+    are compared in full."""
     w = synth.WORKLOADS[name]
     B, H, W, nh, M = w["B"], w["H"], w["W"], w["heads"], w["window"]
     s = w["shifts"][-1]
@@ -151,18 +151,22 @@ def test_backward_full_size(name):
     _say(f"bwd {name} full B={B} shift={s}")
     dq, dt = _run(qkv, table, dout, M, s)
     rq, rt = oracle.swin_wattn_bwd(qkv, table, dout, M, s)
+    assert np.isfinite(dq).all(), "some gradient was never written (NaN pre-fill) or is not finite"
     assert np.isfinite(dt).all()
     lim_t = 1e-3 * np.abs(rt).max() + 1e-6
     et = np.abs(dt - rt).max()
     print(f"    dtable max_err={et:.3e} bound {lim_t:.3e}", flush=True)
     assert et <= lim_t
-    for b in (0, B // 2 + 5, B - 1):
-        for i, comp in enumerate("qkv"):
-            e = np.abs(dq[b, :, :, i] - rq[b, :, :, i])
-            ref = np.abs(rq[b, :, :, i])
-            print(f"    image {b} d{comp}: max_abs={e.max():.3e} mean_abs={e.mean():.3e}", flush=True)
-            assert np.isfinite(dq[b]).all()
-            assert e.max() <= 2.0**-6 * ref.max() + 1e-6 and e.mean() <= 2.0**-8 * ref.mean() + 1e-7
+    for i, comp in enumerate("qkv"):
+        # the bound of each image, on every image
+        e = np.abs(dq[:, :, :, i] - rq[:, :, :, i]).reshape(B, -1)
+        ref = np.abs(rq[:, :, :, i]).reshape(B, -1)
+        emax, emean = e.max(axis=1), e.mean(axis=1)
+        lmax, lmean = 2.0**-6 * ref.max(axis=1) + 1e-6, 2.0**-8 * ref.mean(axis=1) + 1e-7
+        worst = int(np.argmax(np.maximum(emax / lmax, emean / lmean)))
+        print(f"    d{comp}: worst image {worst}: max_abs={emax[worst]:.3e} (bound {lmax[worst]:.3e}) "
+              f"mean_abs={emean[worst]:.3e} (bound {lmean[worst]:.3e})", flush=True)
+        assert (emax <= lmax).all() and (emean <= lmean).all(), f"d{comp}"
 
 
 def test_backward_batch_split_over_2gib():

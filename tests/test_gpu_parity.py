@@ -81,6 +81,28 @@ def test_precompute_bit_exact(H, W, M, s):
     assert np.array_equal(reg.cpu().numpy().astype(np.float64), lab.reshape(nW, N))
 
 
+def test_precompute_copy_on_another_stream():
+    """The fill is queued on one stream and the copies on another, with no
+    host synchronisation between them: the copy stream waits for the event
+    the precompute recorded, so the copies see the finished tensors."""
+    H, W, M, s = 96, 96, 12, 6
+    _say(f"precompute on stream A, copies on stream B, H={H} W={W} M={M} s={s}")
+    swa.check(swa.swin_wattn_release())
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    N, nW = M * M, (H // M) * (W // M)
+    mask = torch.full((nW, N, N), float("nan"), dtype=torch.float32, device=_dev())
+    idx = torch.full((N, N), -1, dtype=torch.int32, device=_dev())
+    torch.cuda.synchronize()
+    swa.check(swa.swin_wattn_precompute(H, W, M, s, a))
+    swa.check(swa.swin_wattn_copy_mask(H, W, M, s, mask, b))
+    swa.check(swa.swin_wattn_copy_index(H, W, M, s, idx, b))
+    b.synchronize()
+    assert np.array_equal(mask.cpu().numpy(), oracle.shift_mask(H, W, M, s).astype(np.float32))
+    assert np.array_equal(idx.cpu().numpy(), oracle.rel_index(M))
+    torch.cuda.synchronize()
+    swa.check(swa.swin_wattn_release())
+
+
 # ---------------------------------------------------------------- fp32
 
 def test_fp32_tiny_workload():
@@ -121,20 +143,11 @@ def test_bf16_workloads_small_batch_full(name, batch):
     _check(got, oracle.swin_wattn_fwd(qkv, table, w["window"], s), True, f"{name} B={batch}")
 
 
-def _sample_windows(B, nWy, nWx, rng, extra=48):
-    nW = nWy * nWx
-    sel = set(range(nW))  # every window of the first image (all mask classes)
-    last = (B - 1) * nW
-    sel.update(last + wy * nWx + (nWx - 1) for wy in range(nWy))  # right column of the last image
-    sel.update(last + (nWy - 1) * nWx + wx for wx in range(nWx))  # bottom row of the last image
-    sel.update(rng.integers(0, B * nW, size=extra).tolist())
-    return np.array(sorted(sel), dtype=np.int64)
-
-
 @pytest.mark.parametrize("name", ["swin-l-s1", "swin-l-384"])
-def test_bf16_workloads_full_size_sampled(name):
-    # the launch the benchmark times: full batch, every window computed on the
-    # GPU; the oracle recomputes a sample of windows one by one
+def test_bf16_workloads_full_size(name):
+    # the launch the benchmark times: full batch; the oracle computes the
+    # whole forward (a second or two on the host) and every output element
+    # is compared
     w = synth.WORKLOADS[name]
     B, H, W, nh, M = w["B"], w["H"], w["W"], w["heads"], w["window"]
     s = w["shifts"][0]
@@ -142,10 +155,9 @@ def test_bf16_workloads_full_size_sampled(name):
     _say(f"bf16 {name} full size B={B} shift={s}")
     out = _run(qkv, table, M, s)
     assert not torch.isnan(out).any().item(), "some output position was never written"
-    sel = _sample_windows(B, H // M, W // M, np.random.default_rng(5))
-    ref, pos = oracle.swin_wattn_windows(qkv, table, M, s, sel)
-    got = _f64(out.view(B * H * W, nh * 32)[torch.from_numpy(pos.ravel()).to(_dev())])
-    _check(got, ref.reshape(-1, nh * 32), True, f"{name} {len(sel)} sampled windows")
+    got = _f64(out)
+    del out
+    _check(got, oracle.swin_wattn_fwd(qkv, table, M, s), True, f"{name} every window")
 
 
 @pytest.mark.parametrize("B,H,W,nh,M,s", [
