@@ -18,7 +18,11 @@ struct BwdParams {
   int B, H, W, nh, shift;
   int nWy, nWx, nW;
   int windows;         // B * nW
-  int xcd_streams;     // grid is a multiple of 8 * nh: streams laid out per XCD
+  int xcd_streams;     // 1: grid a multiple of 8 * nh / HP, the head groups of a run on one
+                       // XCD; 2 (one head per workgroup, even nh): the two heads of each
+                       // 128-byte line of a run on one XCD
+  int runs;            // runs of windows (the grid holds runs * nh / HP workgroups, and in
+                       // mode 2 up to 7 idle pairs of workgroups)
   unsigned dqkv_bytes; // bytes of dqkv in this launch (at most 2^31)
   float scale;         // 1 / sqrt(head_dim)
   float score_scale;   // log2(e) / sqrt(head_dim)

@@ -43,6 +43,7 @@
 //             channels of the lane's token.
 
 #include <atomic>
+#include <type_traits>
 
 #include "bwd_internal.h"
 #include "wattn_common.h"
@@ -176,13 +177,23 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
   };
 
   // this workgroup's heads and run of windows: workgroup id -> (XCD x, slot
-  // k); the nh/HP head groups of run 8 (k / groups) + x are slots
-  // groups (k / groups) .. + groups-1 of XCD x (workgroups are dealt to the
-  // XCDs round-robin)
+  // k) (workgroups are dealt to the XCDs round-robin).  Mode 1: the nh/HP
+  // head groups of run 8 (k / groups) + x are slots groups (k / groups) ..
+  // + groups-1 of XCD x.  Mode 2 (one head per workgroup, even head count):
+  // slots 2j and 2j+1 of XCD x hold heads 2i and 2i+1 (whose 64-byte rows
+  // share the 128-byte lines of a token) of one run, pair unit 8j + x = run
+  // * nh/2 + i; only pairs of heads need to meet in one L2, so every run
+  // need not fit on one XCD and the grid fills the chip more evenly
   const int groups = nh / HP;
   int grp, run;
   const int id = blockIdx.x;
-  if (p.xcd_streams) {
+  if (p.xcd_streams == 2) {
+    const int k = id >> 3, npairs = nh >> 1;
+    const int pu = (k >> 1) * 8 + (id & 7);
+    if (pu >= p.runs * npairs) return;  // idle workgroups of the last slots
+    run = pu / npairs;
+    grp = 2 * (pu - run * npairs) + (k & 1);
+  } else if (p.xcd_streams) {
     const int k = id >> 3;
     grp = k % groups;
     run = (k / groups) * 8 + (id & 7);
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
   }
   const int h0 = grp * HP;       // first head of the workgroup
   const int head = h0 + hl;      // head of the wave
-  const int runs = gridDim.x / groups;
+  const int runs = p.runs;
   const int w_lo = (int)((long long)run * p.windows / runs);
   const int w_hi = (int)((long long)(run + 1) * p.windows / runs);
 
@@ -312,33 +323,72 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
     const bf16x8 q = tok16(0, it), go = tok16(3, it);
     bf16x8 mq = {};
     if (masked) mq = mask_query(local_label(pos.wy * M + ty, pos.wx * M + tx));
-    f32x4 sc[NT], dp[NT];
+    // 9-tile windows recompute each dP tile (one MFMA) where it is needed
+    // instead of holding all of them next to the scores (36 VGPRs)
+    constexpr bool HOLD_DP = NT <= 4;
+    f32x4 sc[NT], dp[HOLD_DP ? NT : 1];
+    // the window's mask flag is tested once, outside the tile loop: with
+    // no branch between tiles, the LDS reads of one tile are issued while
+    // the products of the previous ones run
+    // 9-tile windows: one base register for the bias reads, opaque to the
+    // compiler, so that it keeps the table constants in the base and the
+    // key offsets E(jt) + r (at most 195 words) in the immediate offsets of
+    // paired reads instead of an address add per read (for head pairs of
+    // 4-tile windows it cost registers: 130 instead of 118, one workgroup
+    // per CU fewer)
+    int qb = qbase;
+    if constexpr (NT > 4) asm("" : "+v"(qb));
+    auto score_tiles = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) {
-      f32x4 acc;
+      for (int jt = 0; jt < NT; ++jt) {
+        f32x4 acc;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (!S::col_ok(jt, r)) {
-          acc[r] = -__builtin_inff();
-          continue;
+        for (int r = 0; r < 4; ++r) {
+          if (!S::col_ok(jt, r)) {
+            acc[r] = -__builtin_inff();
+            continue;
+          }
+          float v = s_brev[qb + S::E(jt) + r];
+          if (!S::rows_all(jt)) v = g_ok ? v : -__builtin_inff();
+          acc[r] = v;
         }
-        float v = s_brev[qbase + S::E(jt) + r];
-        if (!S::rows_all(jt)) v = g_ok ? v : -__builtin_inff();
-        acc[r] = v;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(1, jt), q, acc, 0, 0, 0);
+        if constexpr (MASKED) {
+          // key-side operand of this lane: key row (jt, 4g + r) is owned by
+          // lane group g, the key token is the lane's own token c of tile jt
+          int ky, kx;
+          btile_token<M>(jt, c, ky, kx);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              mask_key(local_label(pos.wy * M + ky, pos.wx * M + kx)), mq, acc, 0, 0, 0);
+        }
+        sc[jt] = acc;
+        if constexpr (HOLD_DP)
+          dp[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(2, jt), go, z, 0, 0, 0);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(1, jt), q, acc, 0, 0, 0);
-      if (masked) {
-        // key-side operand of this lane: key row (jt, 4g + r) is owned by
-        // lane group g, the key token is the lane's own token c of tile jt
-        int ky, kx;
-        btile_token<M>(jt, c, ky, kx);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            mask_key(local_label(pos.wy * M + ky, pos.wx * M + kx)), mq, acc, 0, 0, 0);
+    };
+    if (masked) score_tiles(std::true_type{});
+    else score_tiles(std::false_type{});
+    // dP tile jt of the lane's query: V_jt dO^T.  The recomputing path's
+    // second pass reads the value tiles through a lane offset the compiler
+    // cannot see through (one opaque copy per window, so the reads of both
+    // passes still schedule freely), so that the two reads and their
+    // products are not merged back into nine held tiles.
+    const int voff0 = uchunk(c, g);
+    int voff1 = voff0;
+    if constexpr (!HOLD_DP) asm("" : "+v"(voff1));
+    auto dp_tile = [&](int jt, int pass) -> f32x4 {
+      if constexpr (HOLD_DP) {
+        return dp[jt];
+      } else {
+        const bf16x8 v =
+            *reinterpret_cast<const bf16x8*>(block(2, jt) + (pass == 0 ? voff0 : voff1));
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, go, z, 0, 0, 0);
       }
-      sc[jt] = acc;
-      dp[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tok16(2, jt), go, z, 0, 0, 0);
-    }
-    // exact softmax in fp32: max, then the sum of exp2 about it
+    };
+    // exact softmax in fp32: the max, then e = exp2 about it, its sum l and
+    // sum(e dP) in the same pass, so that D = sum(e dP) / l needs no pass of
+    // its own (the value tiles are read while the exponentials run)
     float m = -__builtin_inff();
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt)
@@ -346,61 +396,74 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
       for (int r = 0; r < 4; ++r)
         if (S::col_ok(jt, r)) m = fmaxf(m, sc[jt][r]);
     m = max_groups(m) * p.score_scale;
-    float sum = 0.f;
+    float sum = 0.f, dsum = 0.f;
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt)
+    for (int jt = 0; jt < NT; ++jt) {
+      const f32x4 d = dp_tile(jt, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float e = S::col_ok(jt, r) ? fast_exp2(fmaf(sc[jt][r], p.score_scale, -m)) : 0.f;
         sc[jt][r] = e;
         sum += e;
+        dsum += e * d[r];
       }
+    }
     sum = sum_groups(sum);
     // padded queries: P = 0, so their dS, P and dQ vanish
     const float inv = ok ? fast_rcp(sum) : 0.f;
-    float dsum = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < NT; ++jt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sc[jt][r] *= inv;
-        dsum += sc[jt][r] * dp[jt][r];
-      }
-    const float Dq = sum_groups(dsum);
+    const float Dq = sum_groups(dsum) * inv;
     // dS^T = P o (dP^T - D): fp32 into the table sums; bf16 as the B
-    // operand of the key contraction and, with P, into the LDS blocks
-    bf16x8 pb[NK];
+    // operand of the key contraction and, with P, into the LDS blocks.
+    // dQ^T = K^T dS^T is accumulated as soon as a pair of key tiles has its
+    // dS^T, so that only one B operand is live; K^T comes from transposing
+    // reads (odd tile counts: any finite data for the missing tile, its dS^T
+    // is zero)
+    f32x4 o0 = z, o1 = z;
+    bf16x8 pb = {};
+    // second-pass dP: the value tile of key tile jt + 1 is read before the
+    // products of tile jt
+    auto vtile = [&](int jt) {
+      return *reinterpret_cast<const bf16x8*>(block(2, jt) + voff1);
+    };
+    bf16x8 vnext = {};
+    if constexpr (!HOLD_DP) vnext = vtile(0);
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
+      f32x4 d;
+      if constexpr (HOLD_DP) {
+        d = dp[jt];
+      } else {
+        const bf16x8 vcur = vnext;
+        if (jt + 1 < NT) vnext = vtile(jt + 1);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, go, z, 0, 0, 0);
+      }
       bf16x4 pt, st;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float ds = sc[jt][r] * (dp[jt][r] - Dq);
+        const float pr = sc[jt][r] * inv;
+        const float ds = pr * (d[r] - Dq);
         dta[jt][r] += ds;
         st[r] = (__bf16)ds;
-        pt[r] = (__bf16)sc[jt][r];
-        pb[jt / 2][4 * (jt % 2) + r] = st[r];
+        pt[r] = (__bf16)pr;
+        pb[4 * (jt % 2) + r] = st[r];
       }
       // P[query c][keys 4g .. 4g+3] of block (it, jt)
       *reinterpret_cast<bf16x4*>(pblock(L::OFF_P, it, jt) + pchunk(c, g)) = pt;
       *reinterpret_cast<bf16x4*>(pblock(L::OFF_DS, it, jt) + pchunk(c, g)) = st;
-    }
-    if constexpr (NT % 2 == 1) {
+      if (jt % 2 == 1 || jt == NT - 1) {
+        const int kk = jt / 2;
+        if (jt % 2 == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pb[NK - 1][4 + r] = (__bf16)0.f;
-    }
-    // dQ^T = K^T dS^T, K^T from transposing reads (odd tile counts: any
-    // finite data for the missing tile, its dS^T is zero)
-    f32x4 o0 = z, o1 = z;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const int t1 = 2 * kk + 1 < NT ? 2 * kk + 1 : 2 * kk;
-      const bf16x8 k0 = __builtin_shufflevector(tile_t(1, 2 * kk, 0), tile_t(1, t1, 0), 0, 1, 2, 3,
-                                                4, 5, 6, 7);
-      const bf16x8 k1 = __builtin_shufflevector(tile_t(1, 2 * kk, 1), tile_t(1, t1, 1), 0, 1, 2, 3,
-                                                4, 5, 6, 7);
-      o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, pb[kk], o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, pb[kk], o1, 0, 0, 0);
+          for (int r = 0; r < 4; ++r) pb[4 + r] = (__bf16)0.f;
+        }
+        const int t1 = 2 * kk + 1 < NT ? 2 * kk + 1 : 2 * kk;
+        const bf16x8 k0 = __builtin_shufflevector(tile_t(1, 2 * kk, 0), tile_t(1, t1, 0), 0, 1, 2,
+                                                  3, 4, 5, 6, 7);
+        const bf16x8 k1 = __builtin_shufflevector(tile_t(1, 2 * kk, 1), tile_t(1, t1, 1), 0, 1, 2,
+                                                  3, 4, 5, 6, 7);
+        o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, pb, o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, pb, o1, 0, 0, 0);
+      }
     }
     return pack8(o0, o1, scale);
   };
@@ -409,15 +472,54 @@ __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kerne
   auto phase2 = [&](bf16x8& dk, bf16x8& dv) {
     const int jk = tw;
     f32x4 dk0 = z, dk1 = z, dv0 = z, dv1 = z;
+    if constexpr (HP == 2) {
+      // head pairs (two workgroups of 8 waves per CU): reads and products
+      // in source order; the pipelined form below was slower here (Swin-L
+      // stage 1: 125.3 against 123.5 us)
 #pragma unroll
-    for (int iq = 0; iq < NT; ++iq) {
-      // element k of lane (g, c): P (dS) of query 4g + k of tile iq, key c
-      const bf16x4 pb = lds_read_tr(pblock(L::OFF_P, iq, jk) + pchunk(lane >> 2, lane & 3));
-      const bf16x4 sb = lds_read_tr(pblock(L::OFF_DS, iq, jk) + pchunk(lane >> 2, lane & 3));
-      dv0 = mfma16(tile_t(3, iq, 0), pb, dv0);
-      dv1 = mfma16(tile_t(3, iq, 1), pb, dv1);
-      dk0 = mfma16(tile_t(0, iq, 0), sb, dk0);
-      dk1 = mfma16(tile_t(0, iq, 1), sb, dk1);
+      for (int iq = 0; iq < NT; ++iq) {
+        const bf16x4 pb = lds_read_tr(pblock(L::OFF_P, iq, jk) + pchunk(lane >> 2, lane & 3));
+        const bf16x4 sb = lds_read_tr(pblock(L::OFF_DS, iq, jk) + pchunk(lane >> 2, lane & 3));
+        dv0 = mfma16(tile_t(3, iq, 0), pb, dv0);
+        dv1 = mfma16(tile_t(3, iq, 1), pb, dv1);
+        dk0 = mfma16(tile_t(0, iq, 0), sb, dk0);
+        dk1 = mfma16(tile_t(0, iq, 1), sb, dk1);
+      }
+    } else {
+      // the six operands of query tile iq: P and dS (element k of lane (g, c):
+      // query 4g + k of tile iq, key c), dO^T and Q^T halves
+      struct Ops {
+        bf16x4 pb, sb, o0, o1, q0, q1;
+      };
+      auto fetch = [&](int iq) {
+        Ops o;
+        o.pb = lds_read_tr(pblock(L::OFF_P, iq, jk) + pchunk(lane >> 2, lane & 3));
+        o.sb = lds_read_tr(pblock(L::OFF_DS, iq, jk) + pchunk(lane >> 2, lane & 3));
+        o.o0 = tile_t(3, iq, 0);
+        o.o1 = tile_t(3, iq, 1);
+        o.q0 = tile_t(0, iq, 0);
+        o.q1 = tile_t(0, iq, 1);
+        return o;
+      };
+      // software pipeline: the reads of tile iq + 1 are issued before the
+      // products of tile iq, so each product waits for reads issued one step
+      // earlier (the scheduling groups keep that order)
+      Ops cur = fetch(0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int iq = 0; iq < NT; ++iq) {
+        Ops nxt = cur;
+        if (iq + 1 < NT) {
+          nxt = fetch(iq + 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        }
+        dv0 = mfma16(cur.o0, cur.pb, dv0);
+        dv1 = mfma16(cur.o1, cur.pb, dv1);
+        dk0 = mfma16(cur.q0, cur.sb, dk0);
+        dk1 = mfma16(cur.q1, cur.sb, dk1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        cur = nxt;
+      }
     }
     dk = pack8(dk0, dk1, scale);
     dv = pack8(dv0, dv1, 1.f);
@@ -535,8 +637,22 @@ hipError_t launch_bwd_mh(const BwdParams& p_in, int dev, int cus, hipStream_t st
   if (runs < 1) runs = 1;
   p.xcd_streams = runs >= 8 ? 1 : 0;
   if (p.xcd_streams) runs -= runs % 8;
-  const long long grid = runs * groups;
+  long long grid = runs * groups;
+  // one head per workgroup and an even head count: place pairs of heads,
+  // not whole runs, on one XCD (window 12, 6 heads: 42 runs on 252 of 256
+  // CUs instead of 40 runs on 240)
+  if (HP == 1 && p.nh % 2 == 0 && slots % 16 == 0) {
+    const long long npairs = p.nh / 2;
+    long long r2 = (slots / 2) / npairs;
+    if (r2 > p.windows / kMinRunWindows) r2 = p.windows / kMinRunWindows;
+    if (r2 >= 8 && r2 > runs) {
+      runs = r2;
+      p.xcd_streams = 2;
+      grid = 16 * ((runs * npairs - 1) / 8 + 1);
+    }
+  }
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  p.runs = (int)runs;
   hipLaunchKernelGGL((wattn_bwd_bf16_kernel<M, HP>), dim3((unsigned)grid),
                      dim3(bwd_waves<M>() * 64 * HP), lds, st, p);
   return hipGetLastError();
