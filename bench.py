@@ -75,23 +75,13 @@ def bwd_algorithmic(B, H, W, heads, head_dim, window, elem=2):
 def fwd_kernel_name(window: int, heads: int) -> str:
     """Name of the bf16 forward kernel the library launches.  Mirrors its
     dispatch: head groups of 2, else 3, else 1 for windows of up to 4 tiles
-    of 16 tokens (window <= 8), 1 beyond; the persistent kernel when the bias
-    table and one unit fit in 64 KiB of LDS, else the per-window kernel."""
+    of 16 tokens (window <= 8), 1 beyond."""
     q = (window + 3) // 4
-    nt = q * q
-    if nt > 4:
+    if q * q > 4:
         hg = 1
     else:
         hg = 2 if heads % 2 == 0 else 3 if heads % 3 == 0 else 1
-    t = (2 * window - 1) ** 2
-    tail = 2 * window * (4 * q - window)
-    bias = ((heads * t + tail) * 4 + 15) // 16 * 16
-    # key-side mask operands are staged for 9-tile windows and for units of
-    # one or two heads (which re-read their operands from LDS)
-    unit = 3 * hg * nt * 1024 + (nt * 1024 if nt > 4 or hg <= 2 else 0)
-    if bias + unit <= 64 * 1024:
-        return f"wattn_fwd_bf16_persistent<{window}, {hg}>"
-    return f"wattn_fwd_bf16_kernel<{window}>"
+    return f"wattn_fwd_bf16_persistent<{window}, {hg}>"
 
 
 def measured_traffic(workload: str, family: str = "wattn_fwd_bf16"):

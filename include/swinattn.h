@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   SWIN_OK = 0,
   SWIN_ERR_INVALID_ARG = -1,  /* null or misaligned pointer, bad size, shift, divisibility */
-  SWIN_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim != 32, window > 12, too many heads */
+  SWIN_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim != 32, window > 12, too many heads (fp32) */
   SWIN_ERR_NOT_PREPARED = -3, /* copy calls: no swin_wattn_precompute for the key */
   SWIN_ERR_HIP = -4           /* the HIP runtime reported an error (allocation, launch) */
 } swin_status_t;
@@ -81,15 +81,16 @@ int swin_wattn_precompute(int H, int W, int window, int shift, void* stream);
  * Scores and softmax in float32, products on bf16 inputs with float32
  * accumulation, attention weights rounded to bf16 before the value product,
  * output rounded to nearest-even bf16.  B == 0 queues nothing and returns
- * SWIN_OK.  head_dim must be 32; heads * (2*window-1)^2 * 4 bytes must fit
- * in 64 KiB (the bias table is staged in LDS).  No setup call needed, no
- * allocation, no host synchronisation; safe to call concurrently from
- * several threads. */
+ * SWIN_OK.  head_dim must be 32; any number of heads.  No setup call
+ * needed, no allocation, no host synchronisation; safe to call concurrently
+ * from several threads. */
 int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int B, int H, int W,
                    int heads, int head_dim, int window, int shift, void* stream);
 
 /* Same operation with float32 qkv and out (products and accumulation in
- * float32).  Same layouts, alignment and error behaviour. */
+ * float32).  Same layouts, alignment and error behaviour, except that the
+ * bias tables of all heads, heads * (2*window-1)^2 * 4 bytes, must fit in
+ * 160 KiB (they are staged in LDS together; else SWIN_ERR_UNSUPPORTED). */
 int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out, int B, int H,
                        int W, int heads, int head_dim, int window, int shift, void* stream);
 

@@ -90,7 +90,9 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
   if (B < 0 || H <= 0 || W <= 0 || heads <= 0 || head_dim <= 0 || M <= 0) return SWIN_ERR_INVALID_ARG;
   if (H % M != 0 || W % M != 0 || s < 0 || s >= M) return SWIN_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || M > kMaxWindow) return SWIN_ERR_UNSUPPORTED;
-  if (fwd_lds_bytes(M, heads) > (size_t)kMaxTableLds) return SWIN_ERR_UNSUPPORTED;
+  // the fp32 kernel stages every head's bias table in LDS; the bf16 kernel
+  // stages one head group's when every head's would not fit
+  if (!bf16 && fwd_lds_bytes(M, heads) > (size_t)kMaxLds) return SWIN_ERR_UNSUPPORTED;
   const long long nW = (long long)(H / M) * (W / M);
   const long long C = (long long)heads * head_dim;
   const long long image_bytes = (long long)H * W * 3 * C * (long long)elem;
@@ -131,19 +133,17 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
       rest -= piece;
     }
   }
-  // bf16 windows whose bias table and unit fit in LDS go to the persistent
-  // LDS-staged kernel, the rest to the per-window kernels
+  // bf16: the persistent LDS-staged kernel; fp32: the per-window kernel
   const int hg = head_group(heads, M);
-  const bool persistent = bf16 && M <= kMaxPersistentWindow &&
-                          persistent_lds_bytes(M, hg, heads) <= (size_t)kMaxTableLds;
+  const bool persistent = bf16;
   const int cus = persistent ? compute_units(dev) : 0;
   p.nhg = heads / hg;
   // a unit's per-token slice is hg * 64 bytes: with odd hg and several head
   // groups, neighbouring units of a window share 128-byte lines
   p.xcd_ranges = (hg % 2 == 1 && p.nhg > 1) ? 1 : 0;
   p.own_bias = 0;  // chosen per launch by the persistent kernel's launcher
-  // per-window kernels: heads are dealt round-robin to the waves of a
-  // workgroup, preferably 2-3 heads per wave
+  // fp32 kernel: heads are dealt round-robin to the waves of a workgroup,
+  // preferably 2-3 heads per wave
   int waves = 1;
   for (int cand = 4; cand >= 1; --cand)
     if (heads % cand == 0 && heads / cand >= 2) {
@@ -165,7 +165,6 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
     p.total_windows = (int)(nb * nW);
     p.units = (int)(nb * nW * p.nhg);
     const hipError_t err = persistent ? launch_fwd_bf16_persistent(M, hg, p, dev, cus, st)
-                           : bf16     ? launch_fwd_bf16(M, p, waves, st)
                                       : launch_fwd_f32(M, p, waves, st);
     if (err != hipSuccess) return SWIN_ERR_HIP;
   }

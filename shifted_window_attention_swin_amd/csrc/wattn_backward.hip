@@ -116,7 +116,7 @@ template <int M, int HP>
 __global__ __launch_bounds__(bwd_waves<M>() * 64 * HP) void wattn_bwd_bf16_kernel(BwdParams p) {
   using S = Win<M>;
   using L = BwdLds<M, HP>;
-  constexpr int NT = S::NT, NK = S::NK, T = S::T;
+  constexpr int NT = S::NT, T = S::T;
   constexpr int WV = bwd_waves<M>();  // waves per head
   static_assert(NT <= WV, "one wave per tile");
   static_assert(HP == 1 || (HP == 2 && NT == 4), "head pairs for 4-tile windows");

@@ -31,9 +31,6 @@ struct Win {
   static constexpr bool rows_all(int t) { return 4 * (t / Q) + 3 < M; }
   // code (2M-1)*row + col of in-tile token 0 of tile t
   static constexpr int E(int t) { return 4 * D * (t / Q) + 4 * (t % Q); }
-  // shift mask through one extra MFMA per score tile (small windows) or
-  // through per-element selects (large windows: fewer registers)
-  static constexpr bool MASK_MFMA = NT <= 4;
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that each

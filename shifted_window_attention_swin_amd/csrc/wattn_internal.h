@@ -10,7 +10,10 @@ namespace swinattn {
 
 constexpr int kHeadDim = 32;    // one MFMA K-step (16x16x32 bf16) per score tile
 constexpr int kMaxWindow = 12;  // N = 144 = 9 tiles of 16 tokens
+// bias tables of every head staged by one persistent forward workgroup, at
+// most (beyond it the workgroup stages one head group's tables)
 constexpr int kMaxTableLds = 64 * 1024;
+constexpr int kMaxLds = 160 * 1024;  // LDS of one workgroup on gfx950
 // In-kernel token offsets are 32-bit: one launch covers at most this many
 // bytes of qkv; larger batches are split into several launches.
 constexpr long long kMaxChunkBytes = 1LL << 31;
@@ -26,7 +29,8 @@ struct FwdParams {
   int units;                // B * nW * nhg (work units of the persistent kernel)
   int nhg;                  // head groups per window (persistent kernel)
   int xcd_ranges;           // persistent kernel: one contiguous unit range per XCD
-  int own_bias;             // persistent kernel: stage only the workgroup's head group's tables
+  int own_bias;             // persistent kernel: 0 every head's tables, 1 the workgroup's head
+                            // group's, 2 the current unit's head group's (restaged)
   float score_scale;        // log2(e) / sqrt(head_dim)
   float inv_scale;          // sqrt(head_dim): bias and mask are pre-divided by the scale
   float mask_value;         // -100 * sqrt(head_dim)
@@ -38,20 +42,19 @@ struct FwdParams {
 hipError_t launch_precompute(int H, int W, int M, int s, int32_t* rel_index, float* mask,
                              uint8_t* region, hipStream_t stream);
 
-// Queue the forward kernels; M in [1, kMaxWindow].  `waves` = waves per
+// Queue the fp32 forward kernel; M in [1, kMaxWindow].  `waves` = waves per
 // workgroup (heads are dealt round-robin to waves).
-hipError_t launch_fwd_bf16(int M, const FwdParams& p, int waves, hipStream_t stream);
-// Dynamic LDS of one forward workgroup (staged bias table plus slack).
-size_t fwd_lds_bytes(int M, int nh);
 hipError_t launch_fwd_f32(int M, const FwdParams& p, int waves, hipStream_t stream);
+// Dynamic LDS of one fp32 forward workgroup (every head's bias table plus
+// slack); at most kMaxLds.
+size_t fwd_lds_bytes(int M, int nh);
 
-// Persistent LDS-staged bf16 forward (every window up to kMaxWindow): heads
-// are processed in groups of HG (1..4, HG divides nh; 1 for windows of more
-// than 4 tiles); `dev` = current device, `cus` = its compute units (the grid
-// fills them at the kernel's occupancy, cached per device).
-constexpr int kMaxPersistentWindow = 12;
+// Persistent LDS-staged bf16 forward (every window up to kMaxWindow, any
+// number of heads): heads are processed in groups of HG (1..4, HG divides nh;
+// 1 for windows of more than 4 tiles); `dev` = current device, `cus` = its
+// compute units (the grid fills them at the kernel's occupancy, cached per
+// device).
 hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
                                       hipStream_t stream);
-size_t persistent_lds_bytes(int M, int HG, int nh);
 
 }  // namespace swinattn

@@ -37,7 +37,34 @@
 //              non-temporal 16-byte stores (whole output lines when HG is
 //              even), which the output never re-reads.
 //
-// The attention math per item is the one described in wattn_kernels.hip.
+// The attention math of one item (head h, query tile it):
+//
+//   S^T = K Q^T + C   v_mfma_f32_16x16x32_bf16 per key tile, K = head_dim =
+//             32 exactly.  The accumulator C starts as relative position
+//             bias divided by the score scale (and, in masked windows, one
+//             more MFMA adds the shift mask, see write_mask), so one fma
+//             later turns D into a base-2 logit.  Transposing S puts one
+//             query per lane column: the softmax over keys is in-lane plus
+//             two permlane swaps.
+//   P^T       exp2 of the logits, rounded to bf16: the C/D layout of S^T is
+//             directly the B-operand layout of the next MFMA.
+//   O^T = V^T P^T   V^T read from LDS with transposing reads; the row sums
+//             of P come from one more MFMA against a tile of ones, so the
+//             normaliser sums exactly the weights applied.
+//   store     each lane writes 8 consecutive channels of one query token:
+//             the window reverse and the roll back are the store addresses.
+//
+// Token layout inside a window ("quad tiles"): with Q = ceil(M/4) the window
+// is padded to (4Q) x (4Q) tokens and cut into Q*Q tiles of 4 rows x 4
+// columns; in-tile token u sits at row 4*(t/Q) + u/4, column 4*(t%Q) + u%4.
+// In the C/D layout row 4g+r of a key tile (g = lane/16) is then window row
+// 4*(t/Q)+g, column 4*(t%Q)+r, so the relative position index
+// (dy+M-1)(2M-1) + (dx+M-1) of (query, key) splits into a per-lane part and
+// a compile-time part: with the bias table stored reversed in LDS, every bias
+// gather is one ds_read with an immediate offset.  Padded keys get -inf in
+// the accumulator (weight exactly 0); padded tokens load the window's first
+// token as finite stand-in data (weight 0 times finite = 0 in the value
+// product); padded queries are not stored.
 
 #include <atomic>
 #include <type_traits>
@@ -139,8 +166,12 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
   extern __shared__ float s_lds[];
   float* s_bias = s_lds;
   constexpr int kWaves = U::kWaves;
-  // bias tables staged: every head, or (own_bias) only the HG heads of the
-  // workgroup's head group, which is the same in all its units
+  // bias tables staged: every head (own_bias 0); only the HG heads of the
+  // workgroup's head group, which is the same in all its units (1); or
+  // only the HG heads of the current unit's head group, staged again
+  // between units when it changes (2: head counts whose tables together
+  // exceed the LDS budget, on grids that cannot keep one head group per
+  // workgroup)
   const int bias_floats = (p.own_bias ? HG : p.nh) * S::T + S::TAIL;
   char* s_unit = reinterpret_cast<char*>(s_lds) + ((bias_floats * 4 + 15) & ~15);
 
@@ -181,7 +212,7 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
   // first head of the workgroup's head group when its bias tables alone are
   // staged (the host sets own_bias only for grids that keep u_step a
   // multiple of the head-group count)
-  const int hbase = p.own_bias ? (u % p.nhg) * HG : 0;
+  int hbase = p.own_bias ? (u % p.nhg) * HG : 0;
 
 
   // unit u -> (head group, image, window); decoded once, used for the loads
@@ -458,7 +489,13 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
   for (; u < u_end; u += u_step) {
     write_unit(R);
     write_mask(nxt);
-    __syncthreads();  // unit visible to every wave
+    if (p.own_bias == 2 && nxt.hg * HG != hbase) {
+      // the previous unit's math is done (barrier at the end of the
+      // iteration): its tables may be replaced
+      hbase = nxt.hg * HG;
+      stage_bias_heads<M>(s_bias, p.table, nh, hbase, HG, p.inv_scale);
+    }
+    __syncthreads();  // unit (and its bias tables) visible to every wave
     const Pos cur = nxt;
     if (u + u_step < u_end) {
       nxt = decode(u + u_step);
@@ -513,8 +550,12 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
   FwdParams p = p_in;
   p.own_bias = 0;
   size_t lds = lds_bytes_mh<M, HG>(p.nh);
+  const size_t small = lds_bytes_mh<M, HG>(HG);
+  // the tables of every head would take more than the LDS budget (e.g. 48
+  // heads at window 12, 101.6 KB): one head group's tables only
+  const bool must_own = lds > (size_t)kMaxTableLds;
   long long grid = -1;
-  if constexpr (Win<M>::NT > 4 || Unit<M, HG>::LEAN) {
+  if (Win<M>::NT > 4 || Unit<M, HG>::LEAN || must_own) {
     // 9-tile windows: when a workgroup's units all share one head group it
     // stages only that group's bias tables (one head's table instead of
     // nh), which leaves LDS for one more workgroup per CU.  A workgroup
@@ -522,7 +563,6 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
     // ranges), so the grid is cut to a multiple of nhg (8 nhg): at most
     // 8 nhg - 8 workgroups fewer, e.g. 1008 instead of 1024 at 6 heads.
     if (p.nhg > 1) {
-      const size_t small = lds_bytes_mh<M, HG>(HG);
       long long g = fwd_grid<M, HG>(p, dev, cus, small, 1);
       const bool xcd = p.xcd_ranges && g % 8 == 0;
       const long long q = xcd || Unit<M, HG>::LEAN ? 8LL * p.nhg : p.nhg;
@@ -531,6 +571,10 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
         grid = g;
         lds = small;
         p.own_bias = 1;
+      } else if (must_own) {
+        grid = fwd_grid<M, HG>(p, dev, cus, small, 1);
+        lds = small;
+        p.own_bias = 2;
       }
     }
   }
@@ -541,7 +585,7 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
   // (Swin-L stage 1: 58.4 against 61.6 us with XCD ranges).  A one-head-
   // group grid is then a multiple of 8 nhg already, as XCD ranges need.
   if (!p.xcd_ranges && p.nhg > 1 && grid % 8 == 0 && p.units <= 2 * grid &&
-      (!p.own_bias || (grid / 8) % p.nhg == 0))
+      (p.own_bias != 1 || (grid / 8) % p.nhg == 0))
     p.xcd_ranges = 1;
   hipLaunchKernelGGL((wattn_fwd_bf16_persistent<M, HG>), dim3((unsigned)grid),
                      dim3(Unit<M, HG>::kWaves * 64), lds, st, p);
@@ -559,21 +603,6 @@ hipError_t launch_m(int HG, const FwdParams& p, int dev, int cus, hipStream_t st
       case 3: return launch_mh<M, 3>(p, dev, cus, st);
       case 4: return launch_mh<M, 4>(p, dev, cus, st);
       default: return hipErrorInvalidValue;
-    }
-  }
-}
-
-template <int M>
-size_t lds_m(int HG, int nh) {
-  if constexpr (Win<M>::NT > 4) {
-    return HG == 1 ? lds_bytes_mh<M, 1>(nh) : 0;
-  } else {
-    switch (HG) {
-      case 1: return lds_bytes_mh<M, 1>(nh);
-      case 2: return lds_bytes_mh<M, 2>(nh);
-      case 3: return lds_bytes_mh<M, 3>(nh);
-      case 4: return lds_bytes_mh<M, 4>(nh);
-      default: return 0;
     }
   }
 }
@@ -596,13 +625,6 @@ size_t lds_m(int HG, int nh) {
     case 12: return CALL(12);                                                    \
     default: break;                                                              \
   }
-
-size_t persistent_lds_bytes(int M, int HG, int nh) {
-#define SWA_LDS(m) lds_m<m>(HG, nh)
-  SWA_PERSISTENT_M(SWA_LDS)
-#undef SWA_LDS
-  return 0;
-}
 
 hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
                                       hipStream_t stream) {

@@ -80,7 +80,16 @@ def test_fwd_reports_unsupported_configurations(fn):
     assert _fwd(fn, head_dim=64) == U
     assert _fwd(fn, head_dim=16) == U
     assert _fwd(fn, window=14, shift=0) == U
-    assert _fwd(fn, window=12, H=24, W=24, shift=0, heads=40) == U  # bias table beyond 64 KiB of LDS
+
+
+def test_fp32_fwd_reports_bias_tables_beyond_lds():
+    # the fp32 kernel stages every head's table: 78 heads at window 12 are
+    # 165,048 bytes, beyond the 160 KiB of LDS a workgroup may use (the bf16
+    # forward takes any number of heads; a call with valid arguments cannot
+    # be made here, since these placeholder pointers must never reach a
+    # kernel)
+    U = swa.SWIN_ERR_UNSUPPORTED
+    assert _fwd(swa.swin_wattn_fwd_f32, window=12, H=24, W=24, shift=0, heads=78) == U
 
 
 @pytest.mark.parametrize("fn", [swa.swin_wattn_fwd, swa.swin_wattn_fwd_f32])

@@ -49,7 +49,8 @@ def _twice(run):
     (2, 96, 96, 6, 12, 6, "bf16"),   # persistent, window 12, one head's bias, XCD ranges
     (8, 14, 14, 12, 7, 3, "bf16"),   # small launch in XCD ranges
     (2, 14, 14, 3, 7, 3, "bf16"),    # three-head units (operands held)
-    (1, 14, 14, 64, 7, 3, "bf16"),   # per-window kernel (bias of every head in LDS)
+    (1, 14, 14, 64, 7, 3, "bf16"),   # 64 heads: one head group's tables, staged per unit
+    (1, 12, 12, 48, 12, 0, "bf16"),  # window 12, 48 heads: tables staged per unit
     (2, 28, 14, 3, 7, 3, "f32"),     # fp32 kernel
 ])
 def test_forward_independent_of_stale_lds(B, H, W, nh, M, s, dtype):

@@ -258,10 +258,17 @@ def test_forward_needs_no_setup_and_release(dtype):
 
 
 @pytest.mark.parametrize("B,H,W,nh,M,s", [
-    (1, 14, 14, 64, 7, 3),   # bias table + unit beyond 64 KiB of LDS: per-window kernel
+    # every head's bias tables beyond the 64 KiB staged per workgroup: each
+    # workgroup stages one head group's tables, fixed for its units when the
+    # grid allows it, else staged again whenever the unit's group changes
+    (16, 12, 12, 32, 12, 0),  # Swin-B at 384 px, stage 4 (window = image): fixed group
+    (16, 12, 12, 48, 12, 0),  # Swin-L at 384 px, stage 4: fixed group
+    (1, 12, 12, 48, 12, 0),   # 48 units on 48 workgroups: restaged
+    (2, 24, 24, 48, 12, 6),   # shifted, 4 windows, restaged
+    (1, 14, 14, 64, 7, 3),    # two-head units of 64 heads: restaged
     (1, 24, 24, 20, 12, 6),
 ])
-def test_bf16_many_heads_fallback_kernel(B, H, W, nh, M, s):
+def test_bf16_many_heads(B, H, W, nh, M, s):
     _say(f"bf16 many heads B={B} H={H} W={W} nh={nh} M={M} s={s}")
     qkv, table = synth.make_inputs(B, H, W, nh, 32, M, seed=300 + nh, dtype="bf16")
     got = _f64(_run(qkv, table, M, s))
