@@ -186,8 +186,14 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   // block; the mean and 1/sigma of every token are only needed by the
   // epilogue, so they are computed from LDS while the products are in
   // flight: LL lanes per token, CPL 16-byte chunks of its row per lane
-  // (chunk q = ql + LL k: k-step q / 4, part q % 4), DPP sums over the group
-  // of the row sum and the sum of squares.
+  // (chunk q = ql + LL k: k-step q / 4, part q % 4) held in registers, DPP
+  // sums over the group.  One pass of bf16 dot products (each product exact
+  // in fp32) gives the sum S1 and the sum of squares S2, and K var = S2 -
+  // S1 mean.  That difference loses about log2(S2 / (K var)) bits to
+  // cancellation; where more than 8 are at stake (a row whose mean is
+  // large against its spread, e.g. mean 40 and spread 1) the wave forms the
+  // variance as the definition has it instead, the mean of the squared
+  // deviations from the mean, in a second pass over the held chunks.
   constexpr int LL = KS % 2 == 0 ? 8 : 4;                 // lanes per token
   constexpr int CPL = KS * 4 / LL;                        // chunks per lane
   constexpr int TPW_LN = 64 / LL;                         // tokens per wave and pass
@@ -196,28 +202,39 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
     for (int t0 = wv * TPW_LN; t0 < kLinRows; t0 += kLinWaves * TPW_LN) {  // wave-uniform
       const int t = t0 + lane / LL;
       const char* tile = s_x + (t >> 4) * KS * 1024;
-      // one pass of bf16 dot products over the lane's chunks: the sum and
-      // the sum of squares (each product exact in fp32); K var is formed as
-      // S2 - S1^2 / K, which keeps the mean's rounding out of it
-      float s1 = 0.f, s2 = 0.f;
-      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+      bf16x8 h[CPL];
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
         const int q = ql + LL * k;
-        const bf16x8 h =
-            *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * 1024 + uchunk(t & 15, q & 3));
+        h[k] = *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * 1024 +
+                                                uchunk(t & 15, q & 3));
+      }
+      float s1 = 0.f, s2 = 0.f;
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bf16x2 pr = {h[2 * e], h[2 * e + 1]};
+          const bf16x2 pr = {h[k][2 * e], h[k][2 * e + 1]};
           s1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, s1, false);
           s2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, s2, false);
         }
-      }
-      const float S1 = group_sum<LL>(s1), S2 = group_sum<LL>(s2);
       constexpr float kInvK = 1.f / (KS * 32);
+      const float S1 = group_sum<LL>(s1), S2 = group_sum<LL>(s2);
       const float mu = S1 * kInvK;
-      const float s2c = fmaxf(S2 - S1 * S1 * kInvK, 0.f);  // K times the biased variance
-      const float rs = rsqrtf(s2c * kInvK + p.eps);
+      float kvar = fmaxf(S2 - S1 * mu, 0.f);
+      if (__builtin_amdgcn_ballot_w64(kvar < S2 * (1.f / 256.f)) != 0) {  // wave-uniform
+        float d2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float d = (float)h[k][e] - mu;
+            d2 = fmaf(d, d, d2);
+          }
+        kvar = group_sum<LL>(d2);
+      }
+      const float rs = rsqrtf(kvar * kInvK + p.eps);
       if (ql == 0) s_stat[t] = make_float2(mu, rs);
     }
   };

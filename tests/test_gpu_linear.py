@@ -279,6 +279,21 @@ def test_layernorm_qkv_feeds_the_attention():
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
 
 
+def test_ln_linear_huge_mean_rows():
+    """Rows of mean 1000 and spread 4 (bf16 steps of 4 there): the variance
+    is the mean of squared deviations from the mean, as defined; a form
+    S2 - S1^2 / K in fp32 would lose about 2 % of it to cancellation (S2 is
+    about 1.9e8, K var about 3e3), beyond the bound."""
+    _say("ln_linear rows with mean 1000 and spread 4")
+    T, K, N = 96, 192, 576
+    _, g, be, w, b = synth.make_ln_linear_inputs(T, K, N, seed=22)
+    rng = np.random.default_rng(22)
+    x = synth.bf16_bits((4.0 * rng.standard_normal((T, K)) + 1000.0).astype(np.float32))
+    got = _run_ln(x, g, be, w, b)
+    ref, extra = _ln_ref_and_bound(x, g, be, w, b)
+    _check(got, ref, extra, "mean 1000")
+
+
 def test_ln_linear_large_mean_rows():
     """Rows whose mean is large beside their spread: the folded form
     subtracts mean * sum_c W' from the product of the raw row, with the same
