@@ -11,8 +11,10 @@ the working set of the timed region exceeds twice the 256 MB Infinity Cache
 With --backward a step is one swin_wattn_bwd over the workload instead (the
 bias-gradient zero fill and the backward kernel).  With --workload naming a
 linear-layer workload (qkv-l-s1, proj-l-s1, ...) a
-step is one swin_linear_fwd over its tokens instead, and with a layer norm +
-QKV workload (lnqkv-l-s1, ...) one swin_ln_linear_fwd.
+step is one swin_linear_fwd over its tokens instead, with a layer norm +
+QKV workload (lnqkv-l-s1, ...) one swin_ln_linear_fwd, and with a layer norm
++ attention workload (lnattn-l-s1, lnattn-t-s1) one swin_ln_qkv_wattn_fwd
+(the two-kernel chain is timed beside it).
 """
 from __future__ import annotations
 
@@ -37,6 +39,7 @@ CSRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc")
 # the sources that define each kernel family's device code
 KERNEL_SOURCES = {
     "wattn_fwd_bf16": ("wattn_internal.h", "wattn_common.h", "wattn_persistent.hip"),
+    "ln_qkv_wattn": ("wattn_internal.h", "wattn_common.h", "ln_attn_internal.h", "ln_qkv_wattn.hip"),
     "linear_fwd": ("wattn_internal.h", "wattn_common.h", "linear_internal.h", "linear_gemm.hip"),
     "wattn_bwd_bf16": ("wattn_internal.h", "wattn_common.h", "bwd_internal.h", "wattn_backward.hip"),
 }
@@ -311,6 +314,133 @@ def linear_bench(args, torch, np) -> int:
     return 0
 
 
+def ln_attn_algorithmic(B, H, W, heads, head_dim, window):
+    """Bytes: x read once + out written once.  FLOPs: the QKV projection
+    (2 C 3C per token) and the attention's two contractions over the
+    unpadded window (4 N C per token)."""
+    T = B * H * W
+    C = heads * head_dim
+    return 4 * C * T, 2 * T * C * 3 * C + 4 * window * window * C * T
+
+
+def ln_attn_cpu_baseline(name: str, min_seconds: float = 10.0, max_reps: int = 50):
+    """The fp64 oracle chain (layer norm, linear, attention) on the first
+    images of the workload, repeated for about `min_seconds`."""
+    import oracle
+    import synth
+    spec = synth.LN_ATTN_WORKLOADS[name]
+    a = synth.WORKLOADS[spec["attn"]]
+    M, s = a["window"], a["shifts"][0]
+    nb = 2
+    x, g, be, w, b, t = synth.ln_attn_inputs(name, batch=nb)
+    B, H, W, C = x.shape
+    reps, cores = 0, 0
+    t0 = time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        xn = oracle.layernorm(x, g, be)
+        qkv, cores = oracle.linear(xn, w, b, return_threads=True)
+        oracle.swin_wattn_fwd(qkv.reshape(B, H, W, 3, C // 32, 32), t, M, s)
+        reps += 1
+    dt = time.perf_counter() - t0
+    nbytes, _ = ln_attn_algorithmic(nb, H, W, C // 32, 32, M)
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{name}, first {nb} of {a['B']} images, layer norm + linear + attention "
+                      f"x{reps} ({dt:.1f} s wall, fp64, {cores} threads)"}
+
+
+def ln_attn_bench(args, torch, np) -> int:
+    """One swin_ln_qkv_wattn_fwd per step over the whole workload; the
+    two-kernel chain (swin_ln_linear_fwd, then swin_wattn_fwd) is timed
+    beside it on the same buffers."""
+    import shifted_window_attention_swin_amd as swa
+    import synth
+    spec = synth.LN_ATTN_WORKLOADS[args.workload]
+    a = synth.WORKLOADS[spec["attn"]]
+    B, H, W, nh, d, M = a["B"], a["H"], a["W"], a["heads"], a["head_dim"], a["window"]
+    s = a["shifts"][0]
+    C = nh * d
+    T = B * H * W
+    dev = torch.device("cuda:0")
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+    x_np, g_np, be_np, w_np, b_np, t_np = synth.ln_attn_inputs(args.workload)
+    x0, wd = bf(x_np), bf(w_np)
+    del x_np
+    packed = torch.empty_like(wd)
+    consts = torch.empty(2, 3 * C, dtype=torch.float32, device=dev)
+    swa.check(swa.swin_ln_linear_pack_weight(wd, torch.from_numpy(g_np).to(dev),
+                                             torch.from_numpy(be_np).to(dev),
+                                             torch.from_numpy(b_np).to(dev), packed, consts,
+                                             3 * C, C), "pack")
+    table = torch.from_numpy(t_np).to(dev)
+    nbytes, nflops = ln_attn_algorithmic(B, H, W, nh, d, M)
+    sets = 1 if args.hot else 2 * MALL_BYTES // nbytes + 1
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    outs = [torch.empty(B, H, W, C, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        k = i % sets
+        swa.check(swa.swin_ln_qkv_wattn_fwd(xs[k], packed, consts, 1e-5, table, outs[k], B, H, W,
+                                            nh, d, M, s, stream), "ln_qkv_wattn")
+
+    K = args.steps
+    total_ms, avg_launch_s, isolated_s = time_steps(torch, step, K, args.warmup, stream, 1)
+    # the two-kernel chain on the same inputs: the layer norm + QKV
+    # projection writes qkv, the attention reads it
+    qkv = torch.empty(T, 3 * C, dtype=torch.bfloat16, device=dev)
+
+    def chain(i):
+        k = i % sets
+        swa.check(swa.swin_ln_linear_fwd(xs[k], packed, consts, 1e-5, qkv, T, C, 3 * C, stream),
+                  "ln_linear")
+        swa.check(swa.swin_wattn_fwd(qkv, table, outs[k], B, H, W, nh, d, M, s, stream), "fwd")
+
+    chain_ms, _, _ = time_steps(torch, chain, K, args.warmup, stream, 1)
+    value = nbytes * K / (total_ms / 1e3) / 1e9
+    tflops = nflops / avg_launch_s / 1e12
+    mfma_bound = nflops / nbytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    else:
+        ach = nbytes / avg_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": measured_traffic(args.workload, "ln_qkv_wattn"),
+                 "kernel": f"ln_qkv_wattn_kernel<{M}, {C // 32}>",
+                 "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                 "isolated_launch_us": round(isolated_s * 1e6, 3),
+                 "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
+                 "hbm_gbs": round(nbytes / avg_launch_s / 1e9, 2),
+                 "flop_per_byte": round(nflops / nbytes, 1)})
+    result = {
+        "metric": f"layer norm + QKV + window attention GB/s & TFLOP/s ({spec['desc']}, bf16)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, x ~ N(0.5,2), gamma ~ N(1,0.1), "
+                "beta ~ N(0,0.1), W and bias ~ N(0,0.02), bias table ~ N(0,0.02))",
+        "config": {"workload": args.workload, "desc": spec["desc"], "B": B, "H": H, "W": W,
+                   "heads": nh, "head_dim": d, "window": M, "shift": s, "buffer_sets": sets,
+                   "cache": "hot" if args.hot else "cold"},
+        "tflops": round(nflops * K / (total_ms / 1e3) / 1e12, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "two_kernel_chain_us": round(chain_ms / K * 1e3, 3),
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else ln_attn_cpu_baseline(args.workload),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def bwd_bench(args, torch, np) -> int:
     """One swin_wattn_bwd per step over the whole workload (first shift)."""
     import shifted_window_attention_swin_amd as swa
@@ -418,6 +548,8 @@ def main() -> int:
 
     if args.workload in synth.LINEAR_WORKLOADS or args.workload in synth.LN_LINEAR_WORKLOADS:
         return linear_bench(args, torch, np)
+    if args.workload in synth.LN_ATTN_WORKLOADS:
+        return ln_attn_bench(args, torch, np)
     if args.backward:
         return bwd_bench(args, torch, np)
     w = synth.WORKLOADS[args.workload]

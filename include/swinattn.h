@@ -171,6 +171,30 @@ int swin_ln_linear_pack_weight(const void* weight, const float* gamma, const flo
 int swin_ln_linear_fwd(const void* x, const void* packed_weight, const float* consts, float eps,
                        void* y, long long T, int K, int N, void* stream);
 
+/* Layer norm + QKV projection + shifted-window attention in one pass: the
+ * attention half of a Swin block before its output projection,
+ *   out = swin_wattn_fwd( layer_norm(x) W_qkv^T + b_qkv )
+ * with q, k and v formed per window on the chip instead of being written to
+ * memory and read back.  The NVIDIA talk, section 3, fuses the layer norm
+ * with the window shift and partition, fuses the QKV GEMM with its bias and
+ * prepares its weight to suit the fused attention.
+ *   x        [B][H][W][C] bf16 raw token rows (C = heads * head_dim), image
+ *            order, 16-byte aligned
+ *   packed_qkv, consts  from swin_ln_linear_pack_weight of the QKV weight
+ *            [3C][C] (rows ordered [3][heads][head_dim]), gamma, beta and
+ *            bias, with N = 3C and K = C
+ *   eps      layer-norm epsilon, >= 0
+ *   rel_bias_table, out, B, H, W, heads, head_dim, window, shift: as
+ *            swin_wattn_fwd, with out [B][H][W][C]; out must overlap none of
+ *            the inputs
+ * Arithmetic: the layer norm and the projection as swin_ln_linear_fwd, q, k
+ * and v rounded to bf16, then the attention as swin_wattn_fwd.  head_dim
+ * must be 32, 5 <= window <= 8 and C <= 192 (else SWIN_ERR_UNSUPPORTED).
+ * B == 0 queues nothing.  No allocation, no host synchronisation. */
+int swin_ln_qkv_wattn_fwd(const void* x, const void* packed_qkv, const float* consts, float eps,
+                          const float* rel_bias_table, void* out, int B, int H, int W, int heads,
+                          int head_dim, int window, int shift, void* stream);
+
 /* Copies of the precomputed tensors into caller-owned device memory, queued
  * on `stream` (for verification).  SWIN_ERR_NOT_PREPARED without a prior
  * swin_wattn_precompute for the key.  `stream` may differ from the

@@ -31,7 +31,7 @@ SWIN_ERR_HIP = -4
 EXPORTS = ("swin_wattn_precompute", "swin_wattn_fwd", "swin_wattn_fwd_f32", "swin_wattn_bwd",
            "swin_wattn_copy_index", "swin_wattn_copy_mask", "swin_wattn_copy_region",
            "swin_linear_pack_weight", "swin_linear_fwd", "swin_ln_linear_pack_weight",
-           "swin_ln_linear_fwd",
+           "swin_ln_linear_fwd", "swin_ln_qkv_wattn_fwd",
            "swin_wattn_release", "swin_wattn_status_string")
 
 
@@ -58,6 +58,8 @@ _lib.swin_linear_pack_weight.argtypes = [_P, _P, _I, _I, _P]
 _lib.swin_linear_fwd.argtypes = [_P, _P, _P, _P, _P, ctypes.c_longlong, _I, _I, _P]
 _lib.swin_ln_linear_pack_weight.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _P]
 _lib.swin_ln_linear_fwd.argtypes = [_P, _P, _P, ctypes.c_float, _P, ctypes.c_longlong, _I, _I, _P]
+_lib.swin_ln_qkv_wattn_fwd.argtypes = [_P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       _I, _P]
 _lib.swin_wattn_release.argtypes = []
 _lib.swin_wattn_status_string.argtypes = [_I]
 _lib.swin_wattn_status_string.restype = ctypes.c_char_p
@@ -138,6 +140,14 @@ def swin_ln_linear_fwd(x, packed_weight, consts, eps: float, y, T: int, K: int, 
                        stream=None) -> int:
     return _lib.swin_ln_linear_fwd(_addr(x), _addr(packed_weight), _addr(consts), eps, _addr(y),
                                    T, K, N, _stream(stream))
+
+
+def swin_ln_qkv_wattn_fwd(x, packed_qkv, consts, eps: float, rel_bias_table, out, B: int, H: int,
+                          W: int, heads: int, head_dim: int, window: int, shift: int,
+                          stream=None) -> int:
+    return _lib.swin_ln_qkv_wattn_fwd(_addr(x), _addr(packed_qkv), _addr(consts), eps,
+                                      _addr(rel_bias_table), _addr(out), B, H, W, heads, head_dim,
+                                      window, shift, _stream(stream))
 
 
 def swin_wattn_release() -> int:

@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libswinattn.so")
 SOURCES = ["swinattn_api.hip", "wattn_kernels.hip", "wattn_persistent.hip", "linear_gemm.hip",
-           "wattn_backward.hip"]
+           "wattn_backward.hip", "ln_qkv_wattn.hip"]
 ARCH = "gfx950"
 
 

@@ -17,6 +17,7 @@
 
 #include "../../include/swinattn.h"
 #include "bwd_internal.h"
+#include "ln_attn_internal.h"
 #include "linear_internal.h"
 #include "wattn_internal.h"
 
@@ -83,6 +84,21 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// 100*sqrt(d) as three bf16 pieces (each the top 8 significant bits of the
+// remainder); their sum is the fp32 value exactly, in any order
+void mask_pieces(int head_dim, float (&pieces)[3]) {
+  float rest = (float)(100.0 * sqrt((double)head_dim));
+  for (int k = 0; k < 3; ++k) {
+    uint32_t u;
+    memcpy(&u, &rest, 4);
+    u &= 0xFFFF0000u;
+    float piece;
+    memcpy(&piece, &u, 4);
+    pieces[k] = piece;
+    rest -= piece;
+  }
+}
+
 int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int W, int heads,
                int head_dim, int M, int s, void* stream, size_t elem, bool bf16) {
   if (!qkv || !table || !out) return SWIN_ERR_INVALID_ARG;
@@ -119,20 +135,7 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
   p.score_scale = (float)(1.4426950408889634 / sd);
   p.inv_scale = (float)sd;
   p.mask_value = (float)(-100.0 * sd);
-  // 100*sqrt(d) as three bf16 pieces (each the top 8 significant bits of the
-  // remainder); their sum is the fp32 value exactly, in any order
-  {
-    float rest = (float)(100.0 * sd);
-    for (int k = 0; k < 3; ++k) {
-      uint32_t u;
-      memcpy(&u, &rest, 4);
-      u &= 0xFFFF0000u;
-      float piece;
-      memcpy(&piece, &u, 4);
-      p.mask_pieces[k] = piece;
-      rest -= piece;
-    }
-  }
+  mask_pieces(head_dim, p.mask_pieces);
   // bf16: the persistent LDS-staged kernel; fp32: the per-window kernel
   const int hg = head_group(heads, M);
   const bool persistent = bf16;
@@ -318,18 +321,7 @@ int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dou
   p.scale = (float)(1.0 / sd);
   p.score_scale = (float)(1.4426950408889634 / sd);
   p.inv_scale = (float)sd;
-  {
-    float rest = (float)(100.0 * sd);
-    for (int k = 0; k < 3; ++k) {
-      uint32_t u;
-      memcpy(&u, &rest, 4);
-      u &= 0xFFFF0000u;
-      float piece;
-      memcpy(&piece, &u, 4);
-      p.mask_pieces[k] = piece;
-      rest -= piece;
-    }
-  }
+  mask_pieces(head_dim, p.mask_pieces);
   const int cus = compute_units(dev);
   // images per launch: in-kernel byte offsets stay below 2^31
   const long long per = kMaxChunkBytes / image_bytes;
@@ -404,6 +396,65 @@ int swin_ln_linear_fwd(const void* x, const void* packed_weight, const float* co
                        void* y, long long T, int K, int N, void* stream) {
   if (!consts || !aligned(consts, 16)) return SWIN_ERR_INVALID_ARG;
   return linear_common(x, consts, eps, packed_weight, consts + N, nullptr, y, T, K, N, stream);
+}
+
+int swin_ln_qkv_wattn_fwd(const void* x, const void* packed_qkv, const float* consts, float eps,
+                          const float* rel_bias_table, void* out, int B, int H, int W, int heads,
+                          int head_dim, int window, int shift, void* stream) {
+  if (!x || !packed_qkv || !consts || !rel_bias_table || !out) return SWIN_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(packed_qkv, 16) || !aligned(consts, 16) || !aligned(out, 16) ||
+      !aligned(rel_bias_table, 4))
+    return SWIN_ERR_INVALID_ARG;
+  const int M = window, s = shift;
+  if (B < 0 || H <= 0 || W <= 0 || heads <= 0 || head_dim <= 0 || M <= 0 || !(eps >= 0.f))
+    return SWIN_ERR_INVALID_ARG;
+  if (H % M != 0 || W % M != 0 || s < 0 || s >= M) return SWIN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || M < kMinLnAttnWindow || M > kMaxLnAttnWindow ||
+      (long long)heads * head_dim > kMaxLnAttnC)
+    return SWIN_ERR_UNSUPPORTED;
+  const int C = heads * head_dim, N = 3 * C;
+  const long long image_bytes = (long long)H * W * C * 2;
+  const long long tokens = (long long)B * H * W;
+  const size_t xb = (size_t)(tokens * C * 2), wb = (size_t)N * C * 2, cb = (size_t)N * 8;
+  const size_t tb = (size_t)(2 * M - 1) * (2 * M - 1) * heads * 4;
+  if (overlap(out, xb, x, xb) || overlap(out, xb, packed_qkv, wb) || overlap(out, xb, consts, cb) ||
+      overlap(out, xb, rel_bias_table, tb))
+    return SWIN_ERR_INVALID_ARG;
+  if (B == 0) return SWIN_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SWIN_ERR_HIP;
+  LnAttnParams p;
+  p.wp = packed_qkv;
+  p.consts = consts;
+  p.table = rel_bias_table;
+  p.eps = eps;
+  p.H = H;
+  p.W = W;
+  p.nh = heads;
+  p.C = C;
+  p.N = N;
+  p.shift = s;
+  p.nWy = H / M;
+  p.nWx = W / M;
+  p.nW = p.nWy * p.nWx;
+  const double sd = sqrt((double)head_dim);
+  p.score_scale = (float)(1.4426950408889634 / sd);
+  p.inv_scale = (float)sd;
+  mask_pieces(head_dim, p.mask_pieces);
+  const int cus = compute_units(dev);
+  // images per launch: in-kernel byte offsets of x and out stay below 2^31
+  const long long per = kMaxChunkBytes / image_bytes;
+  if (per < 1) return SWIN_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (long long b0 = 0; b0 < B; b0 += per) {
+    const long long nb = B - b0 < per ? B - b0 : per;
+    p.x = static_cast<const char*>(x) + b0 * image_bytes;
+    p.out = static_cast<char*>(out) + b0 * image_bytes;
+    p.B = (int)nb;
+    p.windows = (int)(nb * p.nW);
+    if (launch_ln_qkv_wattn(M, p, dev, cus, st) != hipSuccess) return SWIN_ERR_HIP;
+  }
+  return SWIN_OK;
 }
 
 int swin_wattn_copy_index(int H, int W, int window, int shift, int32_t* dst, void* stream) {

@@ -190,3 +190,48 @@ def ln_linear_inputs(name: str, tokens: int | None = None):
     w = LN_LINEAR_WORKLOADS[name]
     T = w["tokens"] if tokens is None else tokens
     return make_ln_linear_inputs(T, w["K"], w["N"], w["seed"])
+
+
+# ---------------------------------------------------------------------------
+# Layer norm + QKV projection + window attention workloads (the attention
+# half of a Swin block, before its output projection): x, gamma, beta, the
+# QKV weight and bias of a layer norm + QKV workload (x as [B, H, W, C]),
+# and the bias table of an attention workload of the same stage.
+
+LN_ATTN_WORKLOADS = {
+    "lnattn-l-s1": dict(ln="lnqkv-l-s1", attn="swin-l-s1",
+                        desc="Swin-L stage 1 layer norm + QKV + window attention, B=64, 56x56, C=192"),
+    "lnattn-t-s1": dict(ln="lnqkv-t-s1", attn="swin-t-s1",
+                        desc="Swin-T stage 1 layer norm + QKV + window attention, B=32, 56x56, C=96"),
+}
+
+
+def attention_table(seed: int, heads: int, window: int, table_std: float = 0.02) -> np.ndarray:
+    """The bias table ``make_inputs`` draws for ``seed`` (sub-stream 1),
+    without drawing qkv."""
+    T = (2 * window - 1) ** 2
+    return normal(stream_key(seed, 1), T * heads, table_std).reshape(T, heads)
+
+
+def make_ln_attn_inputs(B: int, H: int, W: int, heads: int, window: int, seed: int):
+    """Returns ``(x [B,H,W,C], gamma, beta, w [3C, C], bias [3C], table)`` with
+    C = 32 heads: the layer norm + QKV recipe for B*H*W tokens and the
+    attention table of the same seed."""
+    C = 32 * heads
+    x, gamma, beta, w, bias = make_ln_linear_inputs(B * H * W, C, 3 * C, seed)
+    return x.reshape(B, H, W, C), gamma, beta, w, bias, attention_table(seed, heads, window)
+
+
+def ln_attn_inputs(name: str, batch: int | None = None):
+    """Inputs of a named layer norm + attention workload (optionally its
+    first images): those of its layer norm + QKV workload and the table of
+    its attention workload."""
+    spec = LN_ATTN_WORKLOADS[name]
+    a = WORKLOADS[spec["attn"]]
+    B = a["B"] if batch is None else batch
+    T = B * a["H"] * a["W"]
+    x, gamma, beta, w, bias = ln_linear_inputs(spec["ln"], tokens=T)
+    C = a["heads"] * a["head_dim"]
+    table = attention_table(a["seed"], a["heads"], a["window"])
+    return x.reshape(B, a["H"], a["W"], C), gamma, beta, w, bias, table
+

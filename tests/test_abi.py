@@ -187,3 +187,31 @@ def test_bwd_reports_unsupported_configurations():
     U = swa.SWIN_ERR_UNSUPPORTED
     assert _bwd(head_dim=64) == U
     assert _bwd(window=13, H=26, W=26, shift=6) == U        # windows beyond 12
+
+
+def test_ln_qkv_wattn_rejects_invalid_arguments():
+    E, U = swa.SWIN_ERR_INVALID_ARG, swa.SWIN_ERR_UNSUPPORTED
+    a, b, c, d, o = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20  # aligned, never dereferenced
+
+    def call(x=a, wp=b, cs=c, eps=1e-5, tab=d, out=o, B=2, H=14, W=14, heads=6, hd=32, M=7, s=3):
+        return swa.swin_ln_qkv_wattn_fwd(x, wp, cs, eps, tab, out, B, H, W, heads, hd, M, s)
+
+    assert call(x=0) == E
+    assert call(wp=0) == E
+    assert call(cs=0) == E
+    assert call(tab=0) == E
+    assert call(out=0) == E
+    assert call(x=a + 8) == E          # misaligned
+    assert call(cs=c + 4) == E
+    assert call(tab=d + 2) == E
+    assert call(eps=-1.0) == E
+    assert call(B=-1) == E
+    assert call(H=15) == E             # H % window
+    assert call(s=7) == E              # shift >= window
+    assert call(out=a) == E            # out overlaps x
+    assert call(hd=64) == U
+    assert call(M=4, H=16, W=16, s=0) == U    # windows of one token tile
+    assert call(M=12, H=24, W=24, s=0) == U
+    assert call(heads=8) == U          # C = 256 > 192
+    assert call(B=0) == swa.SWIN_OK
+

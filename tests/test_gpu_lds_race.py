@@ -156,3 +156,34 @@ def test_linear_independent_of_stale_lds(layernorm):
     lim = 2.0**-7 * np.abs(ref) + 2.0**-7 * mag
     print(f"    worst err/bound={float((err / lim).max()):.3f}", flush=True)
     assert np.isfinite(got).all() and (err <= lim).all()
+
+
+def test_ln_attn_independent_of_stale_lds():
+    B, H, W, nh, M, s = 2, 28, 28, 6, 7, 3
+    _say(f"lds race ln_qkv_wattn B={B} H={H} W={W} nh={nh} M={M} s={s}")
+    x, g, be, w, b, t = synth.make_ln_attn_inputs(B, H, W, nh, M, seed=977)
+    C = 32 * nh
+    wd = _bf16_dev(w)
+    packed = torch.empty_like(wd)
+    consts = torch.empty(2, 3 * C, dtype=torch.float32, device=_dev())
+    swa.check(swa.swin_ln_linear_pack_weight(wd, torch.from_numpy(g).to(_dev()),
+                                             torch.from_numpy(be).to(_dev()),
+                                             torch.from_numpy(b).to(_dev()), packed, consts,
+                                             3 * C, C), "pack")
+    xd, td = _bf16_dev(x), torch.from_numpy(t).to(_dev())
+    out = torch.empty(B, H, W, C, dtype=torch.bfloat16, device=_dev())
+
+    def run():
+        out.fill_(float("nan"))
+        swa.check(swa.swin_ln_qkv_wattn_fwd(xd, packed, consts, 1e-5, td, out, B, H, W, nh, 32, M,
+                                            s), "ln_qkv_wattn")
+        return [out]
+
+    (a,), (c,) = _twice(run)
+    assert torch.equal(a, c), "fused output depends on the LDS contents before the launch"
+    xn = oracle.layernorm(x, g, be)
+    ref = oracle.swin_wattn_fwd(oracle.linear(xn, w, b).reshape(B, H, W, 3, nh, 32), t, M, s)
+    err = np.abs(a.float().cpu().numpy().astype(np.float64) - ref)
+    print(f"    max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
