@@ -12,7 +12,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libswinoracle.so")
+# a sanitizer build of the oracle may be substituted (tests/test_sanitizers.py)
+LIB_PATH = os.environ.get("SWIN_ORACLE_LIB") or os.path.join(_HERE, "libswinoracle.so")
 _SRC = os.path.join(_HERE, "swin_oracle.c")
 
 F64, F32, BF16 = 0, 1, 2
