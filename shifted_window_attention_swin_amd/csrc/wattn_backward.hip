@@ -620,24 +620,28 @@ int bwd_blocks_per_cu(int dev, size_t lds) {
 // Grid: nh / HP workgroups (one per head group) per run of windows, as many
 // runs as the chip holds at the kernel's occupancy (at most one per
 // window); with 8 runs or more, a multiple of 8 runs, laid out per XCD.
+struct BwdPlan {
+  long long grid;
+  int runs, xcd_streams;
+};
+
 template <int M, int HP>
-hipError_t launch_bwd_mh(const BwdParams& p_in, int dev, int cus, hipStream_t st) {
-  BwdParams p = p_in;
-  const size_t lds = BwdLds<M, HP>::BYTES;
+BwdPlan plan_bwd(const BwdParams& p, int dev, int cus) {
   const int groups = p.nh / HP;
-  const long long slots = (long long)cus * bwd_blocks_per_cu<M, HP>(dev, lds);
+  const long long slots = (long long)cus * bwd_blocks_per_cu<M, HP>(dev, BwdLds<M, HP>::BYTES);
   long long runs = slots / groups;
   if (runs > p.windows) runs = p.windows;
   // at least kMinRunWindows windows per run: each workgroup adds its table
   // gradient to HBM once with global atomics, and short runs make those adds
   // (and the per-workgroup setup) a large share of a small launch (Swin-T
   // stage 3: 45.2 -> 40.7 us, stage 1: 50.4 -> 46.0 us; 16 windows per run
-  // was slower, 55.0 us on stage 3)
+  // was slower, 55.0 us on stage 3, and 4 windows too, 43.9 us)
   if (runs > p.windows / kMinRunWindows) runs = p.windows / kMinRunWindows;
   if (runs < 1) runs = 1;
-  p.xcd_streams = runs >= 8 ? 1 : 0;
-  if (p.xcd_streams) runs -= runs % 8;
-  long long grid = runs * groups;
+  BwdPlan pl;
+  pl.xcd_streams = runs >= 8 ? 1 : 0;
+  if (pl.xcd_streams) runs -= runs % 8;
+  pl.grid = runs * groups;
   // one head per workgroup and an even head count: place pairs of heads,
   // not whole runs, on one XCD (window 12, 6 heads: 42 runs on 252 of 256
   // CUs instead of 40 runs on 240)
@@ -647,24 +651,38 @@ hipError_t launch_bwd_mh(const BwdParams& p_in, int dev, int cus, hipStream_t st
     if (r2 > p.windows / kMinRunWindows) r2 = p.windows / kMinRunWindows;
     if (r2 >= 8 && r2 > runs) {
       runs = r2;
-      p.xcd_streams = 2;
-      grid = 16 * ((runs * npairs - 1) / 8 + 1);
+      pl.xcd_streams = 2;
+      pl.grid = 16 * ((runs * npairs - 1) / 8 + 1);
     }
   }
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  p.runs = (int)runs;
-  hipLaunchKernelGGL((wattn_bwd_bf16_kernel<M, HP>), dim3((unsigned)grid),
-                     dim3(bwd_waves<M>() * 64 * HP), lds, st, p);
+  pl.runs = (int)runs;  // at most the window count
+  return pl;
+}
+
+template <int M, int HP>
+hipError_t launch_bwd_mh(const BwdParams& p_in, const BwdPlan& pl, hipStream_t st) {
+  if (pl.grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  BwdParams p = p_in;
+  p.runs = pl.runs;
+  p.xcd_streams = pl.xcd_streams;
+  hipLaunchKernelGGL((wattn_bwd_bf16_kernel<M, HP>), dim3((unsigned)pl.grid),
+                     dim3(bwd_waves<M>() * 64 * HP), (BwdLds<M, HP>::BYTES), st, p);
   return hipGetLastError();
 }
 
-// head pairs for 4-tile windows (5..8) when the head count is even
+// head pairs for 4-tile windows (5..8) when the head count is even and the
+// pairs' grid covers every CU; a smaller grid takes one head per workgroup,
+// twice the workgroups (Swin-T stage 3, 12 heads, 256 windows: 192 head-pair
+// workgroups took 40.3 us, 384 one-head workgroups 32.1 us)
 template <int M>
 hipError_t launch_bwd_m(const BwdParams& p, int dev, int cus, hipStream_t st) {
   if constexpr (Win<M>::NT == 4) {
-    if (p.nh % 2 == 0) return launch_bwd_mh<M, 2>(p, dev, cus, st);
+    if (p.nh % 2 == 0) {
+      const BwdPlan pl = plan_bwd<M, 2>(p, dev, cus);
+      if (pl.grid >= cus) return launch_bwd_mh<M, 2>(p, pl, st);
+    }
   }
-  return launch_bwd_mh<M, 1>(p, dev, cus, st);
+  return launch_bwd_mh<M, 1>(p, plan_bwd<M, 1>(p, dev, cus), st);
 }
 
 template <int M>
