@@ -17,9 +17,14 @@
 // y_j = (sum_c x_c W'_jc - mean s_j) / sigma + b'_j, so the products run on
 // the raw rows and each token needs only its mean and 1/sigma.
 //
-//   workgroup  4 waves, persistent, fixed on one head for the launch: waves
-//              0-2 hold the head's q, k and v weight blocks (32 channels x C
-//              each, MFMA A operands) in registers for the whole launch.
+//   workgroup  persistent, fixed on one head for the launch, its q, k and v
+//              weight blocks (32 channels x C each, MFMA A operands) held in
+//              registers for the whole launch.  C <= 96: 4 waves, waves 0-2
+//              holding one 32-channel block each and wave 3 taking the
+//              token statistics.  C >= 128: 8 waves, waves 0-5 holding one
+//              16-channel tile each (half the weight registers, so that two
+//              workgroups of 8 waves fit per CU instead of two of 4) and
+//              waves 6-7 taking the statistics, two lanes per token.
 //              The nh head workgroups of a stream of windows sit on one XCD
 //              and walk the same windows in the same order, so a window's x
 //              rows come from HBM once and from that XCD's L2 for the other
@@ -27,8 +32,8 @@
 //   window     the x rows of its 64 padded quad-tile tokens (49 at window 7)
 //              are staged in LDS as 1 KB blocks (16 tokens x 32 channels),
 //              the next window's rows waiting in registers; waves 0-2 form
-//              D = W' x^T for q, k and v (the head's 96 channels), wave 3 the
-//              mean and 1/sigma of every token; then the folded epilogue
+//              D = W' x^T for q, k and v (the head's 96 channels), the other
+//              waves the mean and 1/sigma of every token; then the folded epilogue
 //              writes q, k, v in bf16 into LDS in the attention's tile layout
 //              and each wave runs the attention of one query tile (the math
 //              of wattn_persistent.hip: bias and mask in the accumulator,
@@ -49,8 +54,13 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kLaWaves = 4;
 constexpr int kLaBlock = 1024;  // 16 tokens x 64 bytes
+
+// waves per workgroup: 8 from 4 k-steps (C >= 128) on, see above
+template <int KS>
+constexpr int la_waves() {
+  return KS >= 4 ? 8 : 4;
+}
 
 template <int M, int KS>
 struct LaLds {
@@ -84,20 +94,25 @@ SWA_INLINE unsigned la_pixel(const LnAttnParams& p, int M, int b, int wy, int wx
   return ((unsigned)b * p.H + y) * p.W + x;
 }
 
-// workgroups per CU the registers must leave room for: 3 while the weight
-// blocks (8 KS VGPRs) and the next window's rows (4 KS) leave the attention
-// enough registers, else 2
+// waves per SIMD the registers must leave room for (the second launch
+// bound): 4-wave workgroups, 3 (three per CU) while the weight blocks (8 KS
+// VGPRs) and the next window's rows (4 KS) leave the attention enough
+// registers; 8-wave workgroups, 4 (two per CU, at most 128 VGPRs)
 template <int KS>
-constexpr int la_min_blocks() {
-  return KS <= 3 ? 3 : 2;
+constexpr int la_min_waves() {
+  return la_waves<KS>() == 8 ? 4 : 3;
 }
 
 template <int M, int KS>
-__global__ __launch_bounds__(kLaWaves * 64, la_min_blocks<KS>()) void ln_qkv_wattn_kernel(LnAttnParams p) {
+__global__ __launch_bounds__(la_waves<KS>() * 64, la_min_waves<KS>()) void ln_qkv_wattn_kernel(LnAttnParams p) {
   using S = Win<M>;
   using L = LaLds<M, KS>;
   constexpr int NT = S::NT, NK = S::NK, T = S::T;
   static_assert(NT == 4, "windows of 5 to 8 tokens a side: 4 token tiles");
+  constexpr int kLaWaves = la_waves<KS>();
+  constexpr bool W8 = kLaWaves == 8;
+  // waves computing the products (0 .. kGemm-1) and the statistics (the rest)
+  constexpr int kGemm = W8 ? 6 : 3;
   constexpr int XB = NT * KS;                                  // x blocks of a window
   constexpr int XPW = (XB + kLaWaves - 1) / kLaWaves;          // x blocks loaded per wave
   constexpr int C = KS * 32;
@@ -146,16 +161,19 @@ __global__ __launch_bounds__(kLaWaves * 64, la_min_blocks<KS>()) void ln_qkv_wat
     const int ch = (r / 32) * C + h * 32 + (r % 32);      // output channel of the QKV row
     s_cst[e] = p.consts[half * p.N + ch];
   }
-  // the wave's weight block: slice wv (q, k, v) of head h, column block
-  // wv * nh + h of the packed weight; wave 3 holds none
-  bf16x8 a[KS][2];
-  if (wv < 3) {
-    const char* wcb = static_cast<const char*>(p.wp) + (size_t)(wv * nh + h) * KS * 2048 + lane * 16;
+  // the wave's weights: slice sl (q, k, v) of head h, column block
+  // sl * nh + h of the packed weight, both of its 16-row tiles (4 waves) or
+  // tile ti (8 waves: tile ti of a block carries channels 8 j + 4 ti + r,
+  // j = 0..3, r = 0..3); the statistics waves hold none
+  constexpr int NTI = W8 ? 1 : 2;  // weight tiles per wave
+  const int sl = W8 ? wv >> 1 : wv, ti = W8 ? wv & 1 : 0;
+  bf16x8 a[KS][NTI];
+  if (wv < kGemm) {
+    const char* wcb = static_cast<const char*>(p.wp) + (size_t)(sl * nh + h) * KS * 2048 + lane * 16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      a[ks][0] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2) * 1024);
-      a[ks][1] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2 + 1) * 1024);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < NTI; ++i) a[ks][i] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2 + ti + i) * 1024);
   }
 
   struct Pos {
@@ -194,9 +212,10 @@ __global__ __launch_bounds__(kLaWaves * 64, la_min_blocks<KS>()) void ln_qkv_wat
     }
   };
   // key-side shift-mask operands of a masked window (see wattn_persistent.hip)
-  auto write_mask = [&](const Pos& q) {
+  auto write_mask = [&](const Pos& q, int t0, int t1) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      if (t < t0 || t >= t1) continue;
       int ty, tx;
       la_token<M>(t, c, ty, tx);
       const int loc = 2 * (q.wy * M + ty >= p.H - p.shift) + (q.wx * M + tx >= p.W - p.shift);
@@ -213,48 +232,57 @@ __global__ __launch_bounds__(kLaWaves * 64, la_min_blocks<KS>()) void ln_qkv_wat
   // 8 bits to cancellation (rows whose mean is large against their spread)
   // the wave takes the mean of the squared deviations from the mean in a
   // second pass, as the definition reads
+  // 4 waves: wave 3, one lane per token.  8 waves: waves 6 and 7, tokens
+  // 32 (wv - 6) .. + 31, two lanes per token (lane and lane + 32), each
+  // summing half of the row's 16-byte chunks; the halves are added with a
+  // swap of the wave's two 32-lane halves
   auto ln_stats = [&]() {
     constexpr float kInvK = 1.f / C;
+    constexpr int QH = W8 ? 2 * KS : 4 * KS;  // chunks a lane sums
     const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-    const int t = lane;  // 16 NT = 64 tokens
+    const int t = W8 ? (wv - kGemm) * 32 + (lane & 31) : lane;  // 16 NT = 64 tokens
+    const int q0 = W8 ? (lane >> 5) * QH : 0;
     const char* tile = s_x + (t >> 4) * KS * kLaBlock;
     auto chunk = [&](int q) {  // chunk q of the row: k-step q / 4, part q % 4
       return *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * kLaBlock + uchunk(t & 15, q & 3));
     };
-    // one k-step (4 chunks) at a time: the row's 4 KS chunks are not held
+    auto both_halves = [&](float x) {
+      if constexpr (W8) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      return x;
+    };
+    // a few chunks at a time: the row's chunks are not held
     float s1 = 0.f, s2 = 0.f;
-#pragma unroll 1
-    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll 4
+    for (int q = 0; q < QH; ++q) {
+      const bf16x8 hv = chunk(q0 + q);
 #pragma unroll
-      for (int part = 0; part < 4; ++part) {
-        const bf16x8 hv = chunk(4 * ks + part);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 pr = {hv[2 * e], hv[2 * e + 1]};
-          s1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, s1, false);
-          s2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, s2, false);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {hv[2 * e], hv[2 * e + 1]};
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, s1, false);
+        s2 = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, s2, false);
       }
     }
+    s1 = both_halves(s1);
+    s2 = both_halves(s2);
     const float mu = s1 * kInvK;
     float kvar = fmaxf(s2 - s1 * mu, 0.f);
     if (__builtin_amdgcn_ballot_w64(kvar < s2 * (1.f / 256.f)) != 0) {  // wave-uniform
       float d2 = 0.f;
-#pragma unroll 1
-      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll 4
+      for (int q = 0; q < QH; ++q) {
+        const bf16x8 hv = chunk(q0 + q);
 #pragma unroll
-        for (int part = 0; part < 4; ++part) {
-          const bf16x8 hv = chunk(4 * ks + part);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float d = (float)hv[e] - mu;
-            d2 = fmaf(d, d, d2);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const float d = (float)hv[e] - mu;
+          d2 = fmaf(d, d, d2);
         }
       }
-      kvar = d2;
+      kvar = both_halves(d2);
     }
-    s_stat[t] = make_float2(mu, rsqrtf(kvar * kInvK + p.eps));
+    if (!W8 || lane < 32) s_stat[t] = make_float2(mu, rsqrtf(kvar * kInvK + p.eps));
   };
 
   const bool g_ok = g < S::LG;  // lane group is a window row in the last row group
@@ -359,11 +387,13 @@ __global__ __launch_bounds__(kLaWaves * 64, la_min_blocks<KS>()) void ln_qkv_wat
       issue(R, decode(w + streams));
       __builtin_amdgcn_s_setprio(0);
     }
-    f32x4 acc[NT][2];
-    if (wv < 3) {
+    f32x4 acc[NT][NTI];
+    if (wv < kGemm) {
       // D = W'_block x^T: rows output channels, columns the window's tokens
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = z;
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < NTI; ++i) acc[t][i] = z;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
@@ -371,33 +401,48 @@ __global__ __launch_bounds__(kLaWaves * 64, la_min_blocks<KS>()) void ln_qkv_wat
         for (int t = 0; t < NT; ++t) {
           const bf16x8 xv =
               *reinterpret_cast<const bf16x8*>(s_x + (t * KS + ks) * kLaBlock + uchunk(c, g));
-          acc[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][0], xv, acc[t][0], 0, 0, 0);
-          acc[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][1], xv, acc[t][1], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < NTI; ++i)
+            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], xv, acc[t][i], 0, 0, 0);
         }
       }
     } else {
       ln_stats();
-      if (window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx)) write_mask(cur);
+      if (window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx)) {
+        if constexpr (W8) write_mask(cur, 2 * (wv - kGemm), 2 * (wv - kGemm) + 2);
+        else write_mask(cur, 0, NT);
+      }
     }
     __syncthreads();  // token statistics and mask operands visible
-    if (wv < 3) {
-      // folded layer norm and bias: lane (g, c) holds channels 8g .. 8g+7 of
-      // slice wv for token c of every tile; bf16 q, k or v into the tile
-      const float* cs = s_cst + wv * 32 + 8 * g;
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + 4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(cs + 96);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(cs + 100);
+    if (wv < kGemm) {
+      // folded layer norm and bias: lane (g, c) holds channels 8g + 4 i + r
+      // (weight tile i, r = 0..3) of slice sl for token c of every tile;
+      // bf16 q, k or v into the tile, 8 bytes per weight tile
+      const float* cs = s_cst + sl * 32 + 8 * g + 4 * ti;
+      f32x4 sv[NTI], bv[NTI];
+#pragma unroll
+      for (int i = 0; i < NTI; ++i) {
+        sv[i] = *reinterpret_cast<const f32x4*>(cs + 4 * i);
+        bv[i] = *reinterpret_cast<const f32x4*>(cs + 4 * i + 96);
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const float2 st = s_stat[t * 16 + c];
-        bf16x8 o;
+        char* dst = s_unit + (sl * NT + t) * kLaBlock + uchunk(c, g) + 8 * ti;
+        if constexpr (W8) {
+          bf16x4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          o[r] = (__bf16)fmaf(fmaf(-st.x, s0[r], acc[t][0][r]), st.y, b0[r]);
-          o[4 + r] = (__bf16)fmaf(fmaf(-st.x, s1[r], acc[t][1][r]), st.y, b1[r]);
+          for (int r = 0; r < 4; ++r) o[r] = (__bf16)fmaf(fmaf(-st.x, sv[0][r], acc[t][0][r]), st.y, bv[0][r]);
+          *reinterpret_cast<bf16x4*>(dst) = o;
+        } else {
+          bf16x8 o;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              o[4 * i + r] = (__bf16)fmaf(fmaf(-st.x, sv[i][r], acc[t][i][r]), st.y, bv[i][r]);
+          *reinterpret_cast<bf16x8*>(dst) = o;
         }
-        *reinterpret_cast<bf16x8*>(s_unit + (wv * NT + t) * kLaBlock + uchunk(c, g)) = o;
       }
     }
     __syncthreads();  // q, k, v of the window visible
@@ -419,7 +464,7 @@ int la_blocks_per_cu(int dev) {
   }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_qkv_wattn_kernel<M, KS>,
-                                                   kLaWaves * 64, LaLds<M, KS>::BYTES) !=
+                                                   la_waves<KS>() * 64, LaLds<M, KS>::BYTES) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -441,7 +486,7 @@ hipError_t launch_la(const LnAttnParams& p_in, int dev, int cus, hipStream_t st)
   p.streams = (int)streams;
   const long long grid = streams * p.nh;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ln_qkv_wattn_kernel<M, KS>), dim3((unsigned)grid), dim3(kLaWaves * 64),
+  hipLaunchKernelGGL((ln_qkv_wattn_kernel<M, KS>), dim3((unsigned)grid), dim3(la_waves<KS>() * 64),
                      (LaLds<M, KS>::BYTES), st, p);
   return hipGetLastError();
 }
