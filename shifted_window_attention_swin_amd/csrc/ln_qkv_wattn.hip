@@ -71,8 +71,10 @@ struct LaLds {
   static constexpr int STAT = 16 * NT * 8;                  // (mean, 1/sigma) per token
   static constexpr int OFF_CST = BIAS;
   static constexpr int OFF_STAT = OFF_CST + CST;
-  static constexpr int OFF_X = OFF_STAT + STAT;             // NT * KS blocks of x
-  static constexpr int OFF_UNIT = OFF_X + NT * KS * kLaBlock;  // q, k, v tiles
+  static constexpr int OFF_X = OFF_STAT + STAT;             // NT * KS blocks of x, two
+                                                            // windows' with 8 waves
+  static constexpr int XBUF = la_waves<KS>() == 8 ? 2 : 1;
+  static constexpr int OFF_UNIT = OFF_X + XBUF * NT * KS * kLaBlock;  // q, k, v tiles
   static constexpr int OFF_MASK = OFF_UNIT + 3 * NT * kLaBlock;
   static constexpr int BYTES = OFF_MASK + NT * kLaBlock;
 };
@@ -204,11 +206,11 @@ __global__ __launch_bounds__(la_waves<KS>() * 64, la_min_waves<KS>()) void ln_qk
       }
     }
   };
-  auto write = [&](const Regs& R) {
+  auto write = [&](const Regs& R, char* sx) {
 #pragma unroll
     for (int k = 0; k < XPW; ++k) {
       const int xi = wv + kLaWaves * k;
-      if (xi < XB) *reinterpret_cast<u32x4*>(s_x + xi * kLaBlock + uchunk(cq, gq)) = R[k];
+      if (xi < XB) *reinterpret_cast<u32x4*>(sx + xi * kLaBlock + uchunk(cq, gq)) = R[k];
     }
   };
   // key-side shift-mask operands of a masked window (see wattn_persistent.hip)
@@ -236,13 +238,13 @@ __global__ __launch_bounds__(la_waves<KS>() * 64, la_min_waves<KS>()) void ln_qk
   // 32 (wv - 6) .. + 31, two lanes per token (lane and lane + 32), each
   // summing half of the row's 16-byte chunks; the halves are added with a
   // swap of the wave's two 32-lane halves
-  auto ln_stats = [&]() {
+  auto ln_stats = [&](const char* sx) {
     constexpr float kInvK = 1.f / C;
     constexpr int QH = W8 ? 2 * KS : 4 * KS;  // chunks a lane sums
     const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
     const int t = W8 ? (wv - kGemm) * 32 + (lane & 31) : lane;  // 16 NT = 64 tokens
     const int q0 = W8 ? (lane >> 5) * QH : 0;
-    const char* tile = s_x + (t >> 4) * KS * kLaBlock;
+    const char* tile = sx + (t >> 4) * KS * kLaBlock;
     auto chunk = [&](int q) {  // chunk q of the row: k-step q / 4, part q % 4
       return *reinterpret_cast<const bf16x8*>(tile + (q >> 2) * kLaBlock + uchunk(t & 15, q & 3));
     };
@@ -373,84 +375,136 @@ __global__ __launch_bounds__(la_waves<KS>() * 64, la_min_waves<KS>()) void ln_qk
     }
   };
 
+  // D = W'_tiles x^T of the window in sx: rows output channels, columns
+  // the window's tokens
+  auto gemm = [&](const char* sx, f32x4 (&acc)[NT][NTI]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < NTI; ++i) acc[t][i] = z;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(sx + (t * KS + ks) * kLaBlock + uchunk(c, g));
+#pragma unroll
+        for (int i = 0; i < NTI; ++i)
+          acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], xv, acc[t][i], 0, 0, 0);
+      }
+    }
+  };
+  // folded layer norm and bias: lane (g, c) holds channels 8g + 4 i + r
+  // (weight tile i, r = 0..3) of slice sl for token c of every tile; bf16
+  // q, k or v into the tile, 8 bytes per weight tile
+  auto epilogue = [&](const f32x4 (&acc)[NT][NTI]) {
+    const float* cs = s_cst + sl * 32 + 8 * g + 4 * ti;
+    f32x4 sv[NTI], bv[NTI];
+#pragma unroll
+    for (int i = 0; i < NTI; ++i) {
+      sv[i] = *reinterpret_cast<const f32x4*>(cs + 4 * i);
+      bv[i] = *reinterpret_cast<const f32x4*>(cs + 4 * i + 96);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float2 st = s_stat[t * 16 + c];
+      char* dst = s_unit + (sl * NT + t) * kLaBlock + uchunk(c, g) + 8 * ti;
+      if constexpr (W8) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (__bf16)fmaf(fmaf(-st.x, sv[0][r], acc[t][0][r]), st.y, bv[0][r]);
+        *reinterpret_cast<bf16x4*>(dst) = o;
+      } else {
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            o[4 * i + r] = (__bf16)fmaf(fmaf(-st.x, sv[i][r], acc[t][i][r]), st.y, bv[i][r]);
+        *reinterpret_cast<bf16x8*>(dst) = o;
+      }
+    }
+  };
+
   Regs R;
   int w = stream;
   if (w < p.windows) issue(R, decode(w));
   __syncthreads();  // tables and constants staged
-  for (; w < p.windows; w += streams) {
-    const Pos cur = decode(w);
-    write(R);
-    __syncthreads();  // x rows of the window visible
-    if (w + streams < p.windows) {
-      // the loads leave ahead of the other workgroups' math on the SIMD
-      __builtin_amdgcn_s_setprio(3);
-      issue(R, decode(w + streams));
-      __builtin_amdgcn_s_setprio(0);
+  if constexpr (!W8) {
+    // one window at a time: products and statistics, epilogue, attention
+    for (; w < p.windows; w += streams) {
+      const Pos cur = decode(w);
+      write(R, s_x);
+      __syncthreads();  // x rows of the window visible
+      if (w + streams < p.windows) {
+        // the loads leave ahead of the other workgroups' math on the SIMD
+        __builtin_amdgcn_s_setprio(3);
+        issue(R, decode(w + streams));
+        __builtin_amdgcn_s_setprio(0);
+      }
+      f32x4 acc[NT][NTI];
+      if (wv < kGemm) {
+        gemm(s_x, acc);
+      } else {
+        ln_stats(s_x);
+        if (window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx)) write_mask(cur, 0, NT);
+      }
+      __syncthreads();  // token statistics and mask operands visible
+      if (wv < kGemm) epilogue(acc);
+      __syncthreads();  // q, k, v of the window visible
+      if (wv < NT) attend(cur, wv);
+      // the x tile is rewritten only after every wave has passed the second
+      // barrier above; the q, k, v tiles, statistics and mask operands only
+      // after the next window's first barrier, which every wave reaches
+      // after its attention
     }
-    f32x4 acc[NT][NTI];
-    if (wv < kGemm) {
-      // D = W'_block x^T: rows output channels, columns the window's tokens
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < NTI; ++i) acc[t][i] = z;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const bf16x8 xv =
-              *reinterpret_cast<const bf16x8*>(s_x + (t * KS + ks) * kLaBlock + uchunk(c, g));
-#pragma unroll
-          for (int i = 0; i < NTI; ++i)
-            acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], xv, acc[t][i], 0, 0, 0);
-        }
+  } else {
+    // two windows in flight: while waves 0-3 run the attention of window
+    // i - 1, waves 4-5 form v of window i and waves 6-7 its statistics;
+    // then waves 0-3 form q and k of window i (and waves 4-7 finish v and
+    // the mask operands).  The x rows of consecutive windows alternate
+    // between two buffers, so the rows of window i + 1 are written while
+    // waves 0-3 still read those of window i.
+    Pos prev = decode(w);
+    bool have_prev = false;
+    for (int it = 0; w < p.windows; w += streams, ++it) {
+      const Pos cur = decode(w);
+      char* sx = s_x + (it & 1) * XB * kLaBlock;
+      write(R, sx);
+      // x rows of window i visible; q, k, v and mask operands of window
+      // i - 1 visible
+      __syncthreads();
+      if (w + streams < p.windows) {
+        __builtin_amdgcn_s_setprio(3);
+        issue(R, decode(w + streams));
+        __builtin_amdgcn_s_setprio(0);
       }
-    } else {
-      ln_stats();
-      if (window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx)) {
-        if constexpr (W8) write_mask(cur, 2 * (wv - kGemm), 2 * (wv - kGemm) + 2);
-        else write_mask(cur, 0, NT);
+      f32x4 acc[NT][NTI];
+      if (wv < NT) {
+        if (have_prev) attend(prev, wv);
+      } else if (wv < kGemm) {
+        gemm(sx, acc);
+      } else {
+        ln_stats(sx);
       }
+      // statistics of window i visible; the attention of window i - 1 is
+      // done with the q, k, v tiles and the mask operands
+      __syncthreads();
+      if (wv < NT) {
+        gemm(sx, acc);
+        epilogue(acc);
+      } else if (wv < kGemm) {
+        epilogue(acc);
+      } else if (window_masked(p.shift, cur.wy, cur.wx, p.nWy, p.nWx)) {
+        write_mask(cur, 2 * (wv - kGemm), 2 * (wv - kGemm) + 2);
+      }
+      prev = cur;
+      have_prev = true;
     }
-    __syncthreads();  // token statistics and mask operands visible
-    if (wv < kGemm) {
-      // folded layer norm and bias: lane (g, c) holds channels 8g + 4 i + r
-      // (weight tile i, r = 0..3) of slice sl for token c of every tile;
-      // bf16 q, k or v into the tile, 8 bytes per weight tile
-      const float* cs = s_cst + sl * 32 + 8 * g + 4 * ti;
-      f32x4 sv[NTI], bv[NTI];
-#pragma unroll
-      for (int i = 0; i < NTI; ++i) {
-        sv[i] = *reinterpret_cast<const f32x4*>(cs + 4 * i);
-        bv[i] = *reinterpret_cast<const f32x4*>(cs + 4 * i + 96);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float2 st = s_stat[t * 16 + c];
-        char* dst = s_unit + (sl * NT + t) * kLaBlock + uchunk(c, g) + 8 * ti;
-        if constexpr (W8) {
-          bf16x4 o;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (__bf16)fmaf(fmaf(-st.x, sv[0][r], acc[t][0][r]), st.y, bv[0][r]);
-          *reinterpret_cast<bf16x4*>(dst) = o;
-        } else {
-          bf16x8 o;
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              o[4 * i + r] = (__bf16)fmaf(fmaf(-st.x, sv[i][r], acc[t][i][r]), st.y, bv[i][r]);
-          *reinterpret_cast<bf16x8*>(dst) = o;
-        }
-      }
+    if (have_prev) {
+      __syncthreads();  // q, k, v and mask operands of the last window visible
+      if (wv < NT) attend(prev, wv);
     }
-    __syncthreads();  // q, k, v of the window visible
-    if (wv < NT) attend(cur, wv);
-    // the x tile is rewritten only after every wave has passed the second
-    // barrier above; the q, k, v tiles, statistics and mask operands only
-    // after the next window's first barrier, which every wave reaches after
-    // its attention
   }
 }
 

@@ -87,6 +87,21 @@ def test_ln_attn_matches_oracle_chain(B, H, W, nh, M, s):
     _check(_run(x, g, be, w, b, t, M, s), _reference(x, g, be, w, b, t, M, s), "chain")
 
 
+@pytest.mark.parametrize("nh", [3, 6])
+def test_ln_attn_huge_mean_rows(nh):
+    """Token rows of mean 1000 and spread 4 (bf16 steps of 4 there): the
+    statistics lanes must take the variance as the mean of squared
+    deviations (the sums S2 and S1 mean nearly cancel).  Three heads run
+    4-wave workgroups (one lane per token), six heads 8-wave workgroups
+    (two lanes per token, the halves added across the wave)."""
+    _say(f"ln_qkv_wattn rows with mean 1000 and spread 4, nh={nh}")
+    B, H, W, M, s = 1, 14, 14, 7, 3
+    _, g, be, w, b, t = synth.make_ln_attn_inputs(B, H, W, nh, M, seed=70 + nh)
+    rng = np.random.default_rng(70 + nh)
+    x = synth.bf16_bits((4.0 * rng.standard_normal((B, H, W, 32 * nh)) + 1000.0).astype(np.float32))
+    _check(_run(x, g, be, w, b, t, M, s), _reference(x, g, be, w, b, t, M, s), "mean 1000")
+
+
 @pytest.mark.parametrize("name", ["lnattn-t-s1", "lnattn-l-s1"])
 def test_ln_attn_workloads_full_size(name):
     """The launches the benchmark times, every output element against the
