@@ -24,7 +24,6 @@ struct LinearParams {
   int ncg;     // column groups, one per workgroup (set by launch_linear)
   int blocks;  // row blocks (set by launch_linear)
 };
-size_t linear_lds_bytes(int K, int N);
 // gamma null: plain packing; else the packed weight is gamma o W.
 hipError_t launch_linear_pack(const void* w, const float* gamma, void* wp, int N, int K,
                               hipStream_t stream);
