@@ -67,10 +67,9 @@ SWA_INLINE float group_sum(float v) {
   return v;
 }
 
-// LDS of the layer norm, after the x and output tiles: a second x buffer
-// (the next row block, staged a row block ahead) and two slots of
-// (mean, 1/sigma) of a row block's tokens
-constexpr size_t lin_ln_lds_bytes(int KS) { return (size_t)kLinTiles * KS * 1024 + 2 * kLinRows * 8; }
+// LDS of the layer norm, after the x and output tiles: (mean, 1/sigma) of
+// the row block's tokens
+constexpr size_t lin_ln_lds_bytes() { return kLinRows * 8; }
 
 // WAVES waves per workgroup, one 32-column block each: the workgroup's
 // WAVES * 32 channels are WAVES / 2 whole 128-byte lines of every token.
@@ -88,9 +87,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   extern __shared__ char s_lds[];
   char* s_x = s_lds;              // NB blocks of 1 KB: the row block of x
   char* s_o = s_lds + NB * 1024;  // kLinRows x kOutStride: the fp32 output tile
-  // layer norm: the second x buffer, then two slots of token statistics
-  char* s_x2 = s_o + kLinRows * kOutStride;
-  float2* s_stat = reinterpret_cast<float2*>(s_x2 + NB * 1024);
+  float2* s_stat = reinterpret_cast<float2*>(s_o + kLinRows * kOutStride);  // layer norm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -168,11 +165,11 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   if constexpr (!LN) load_bias(bias);
   // layer norm: the folded bias b'_j and row sum s_j of the 8 channels
   // 8g + 4i + r (i = 0, 1, r = 0..3) of the wave's column block that lane
-  // (g, c) holds in the product layout, for the launch: the epilogue is
+  // (g, c) holds in the product layout, for the launch.  The epilogue is
   // applied there, before the output tile, so that the store phase reads
-  // only the tile.  (Applied in the store layout, every row block re-read
-  // 64 bytes of these constants per lane and slot from LDS: three times the
-  // tile's bytes, about 10 us of LDS traffic at Swin-L stage 1.)
+  // only the tile: applied in the store layout, every row block re-read
+  // 64 bytes of these constants per lane and slot from LDS, three times
+  // the tile's bytes (Swin-L stage 1: 76.8 against about 80 us)
   f32x4 ln_b[LN ? 2 : 1], ln_s[LN ? 2 : 1];
   if constexpr (LN) {
 #pragma unroll
@@ -206,10 +203,10 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   constexpr int CPL = KS * 4 / LL;                        // chunks per lane
   constexpr int TPW_LN = 64 / LL;                         // tokens per wave and pass
   const int ql = lane % LL;
-  auto ln_stats = [&](const char* sx, float2* st) {
+  auto ln_stats = [&]() {
     for (int t0 = wv * TPW_LN; t0 < kLinRows; t0 += kLinWaves * TPW_LN) {  // wave-uniform
       const int t = t0 + lane / LL;
-      const char* tile = sx + (t >> 4) * KS * 1024;
+      const char* tile = s_x + (t >> 4) * KS * 1024;
       bf16x8 h[CPL];
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
@@ -243,7 +240,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
         kvar = group_sum<LL>(d2);
       }
       const float rs = rsqrtf(kvar * kInvK + p.eps);
-      if (ql == 0) st[t] = make_float2(mu, rs);
+      if (ql == 0) s_stat[t] = make_float2(mu, rs);
     }
   };
 
@@ -262,42 +259,19 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
       }
     }
   };
-  auto write = [&](const Regs& R, char* sx) {
+  auto write = [&](const Regs& R) {
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
       const int bi = wv + kLinWaves * k;
-      if (bi < NB) *reinterpret_cast<u32x4*>(sx + bi * 1024 + uchunk(cq, gq)) = R[k];
+      if (bi < NB) *reinterpret_cast<u32x4*>(s_x + bi * 1024 + uchunk(cq, gq)) = R[k];
     }
   };
 
-  // Layer norm: the row blocks alternate between the two x buffers and the
-  // statistics between the two slots.  Each iteration stages the next row
-  // block and, while its products run, computes that row block's
-  // statistics, which the next iteration's first barrier makes visible: the
-  // statistics cost no barrier of their own.
   Regs R;
   if (r < r_end) issue(R, r);
-  if constexpr (LN) {
-    if (r < r_end) write(R, s_x);
-    __syncthreads();  // first row block visible
-    if (r < r_end) {
-      if (r + step < r_end) issue(R, r + step);
-      ln_stats(s_x, s_stat);
-    }
-  }
-  for (int n = 0; r < r_end; r += step, ++n) {
-    const char* xc = LN && (n & 1) ? s_x2 : s_x;   // this row block
-    char* xn = LN && (n & 1) ? s_x : s_x2;         // the next one (layer norm)
-    const float2* st_c = s_stat + (n & 1) * kLinRows;
-    float2* st_n = s_stat + ((n + 1) & 1) * kLinRows;
-    if constexpr (LN) {
-      if (r + step < r_end) write(R, xn);
-    } else {
-      write(R, s_x);
-    }
-    // row block visible to every wave (layer norm: the next row block and
-    // this row block's statistics too)
-    __syncthreads();
+  for (; r < r_end; r += step) {
+    write(R);
+    __syncthreads();  // row block visible to every wave
     const int tok0 = r * kLinRows;
     // the residual goes out before the next row block's loads, so waiting
     // for it never waits for them (vector memory returns count in order)
@@ -311,11 +285,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
           res[j] = *reinterpret_cast<const bf16x8*>(rb + (size_t)tok * yrow + sch[j] * 2);
         }
     }
-    if constexpr (LN) {
-      if (r + 2 * step < r_end) issue(R, r + 2 * step);
-    } else {
-      if (r + step < r_end) issue(R, r + step);
-    }
+    if (r + step < r_end) issue(R, r + step);
     if (active) {
       f32x4 acc[kLinTiles][2];
 #pragma unroll
@@ -328,18 +298,18 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
 #pragma unroll
         for (int tt = 0; tt < kLinTiles; ++tt) {
           const bf16x8 b =
-              *reinterpret_cast<const bf16x8*>(xc + (tt * KS + ks) * 1024 + uchunk(c, g));
+              *reinterpret_cast<const bf16x8*>(s_x + (tt * KS + ks) * 1024 + uchunk(c, g));
           acc[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][0], b, acc[tt][0], 0, 0, 0);
           acc[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][1], b, acc[tt][1], 0, 0, 0);
         }
       }
       if constexpr (LN) {
-        // the next row block's statistics overlap the products in flight
-        if (r + step < r_end) ln_stats(xn, st_n);
+        ln_stats();       // overlaps the products in flight
+        __syncthreads();  // every token's (mean, 1/sigma) visible
         // y = (acc - mean s_j) / sigma + b'_j, in the product layout
 #pragma unroll
         for (int tt = 0; tt < kLinTiles; ++tt) {
-          const float2 st = st_c[tt * 16 + c];
+          const float2 st = s_stat[tt * 16 + c];
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -356,7 +326,8 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
         *reinterpret_cast<f32x4*>(o + 16) = acc[tt][1];
       }
     } else if constexpr (LN) {
-      if (r + step < r_end) ln_stats(xn, st_n);
+      ln_stats();
+      __syncthreads();  // (the barrier of the product waves above)
     }
     __syncthreads();  // output tile complete
 #pragma unroll
@@ -440,9 +411,9 @@ __global__ void linear_ln_consts_kernel(const uint16_t* w, const float* gamma, c
 // group that divides them (fewer re-reads of x), else 2
 int linear_waves(int ncb) { return ncb % 6 == 0 ? 6 : ncb % 4 == 0 ? 4 : 2; }
 
-size_t linear_lds_waves(int K, int waves, int mode) {
+size_t linear_lds_waves(int K, int waves) {
   return (size_t)kLinTiles * (K / 32) * 1024 + (size_t)kLinRows * lin_out_stride(waves) +
-         (mode == kLinLayerNorm ? lin_ln_lds_bytes(K / 32) : 0);
+         lin_ln_lds_bytes();
 }
 
 template <int KS, int MODE, int WAVES>
@@ -455,7 +426,7 @@ int linear_blocks_per_cu(int dev) {
   }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, linear_fwd_kernel<KS, MODE, WAVES>,
-                                                   WAVES * 64, linear_lds_waves(KS * 32, WAVES, MODE)) !=
+                                                   WAVES * 64, linear_lds_waves(KS * 32, WAVES)) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -474,7 +445,7 @@ hipError_t launch_linear_krw(LinearParams p, int dev, int cus, hipStream_t st) {
   if (grid >= 8LL * p.ncg) grid -= grid % (8LL * p.ncg);
   else grid -= grid % p.ncg;
   hipLaunchKernelGGL((linear_fwd_kernel<KS, MODE, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64),
-                     linear_lds_waves(KS * 32, WAVES, MODE), st, p);
+                     linear_lds_waves(KS * 32, WAVES), st, p);
   return hipGetLastError();
 }
 
