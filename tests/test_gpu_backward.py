@@ -85,6 +85,8 @@ def _check(qkv, table, dout, M, s, what):
     (1, 20, 20, 2, 10, 0),    # window 10: padded tiles, no shift
     (1, 18, 27, 1, 9, 4),     # window 9: one padded token row and column per tile row
     (1, 22, 11, 2, 11, 7),    # window 11
+    (150, 14, 14, 2, 7, 3),   # window 7, one head per workgroup (head pairs would leave CUs
+                              # idle), 600 windows in 75 runs, head pairs placed per XCD
 ])
 def test_backward_matches_oracle(B, H, W, nh, M, s):
     _say(f"bwd B={B} H={H} W={W} nh={nh} M={M} s={s}")
