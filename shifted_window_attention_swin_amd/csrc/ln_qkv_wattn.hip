@@ -31,14 +31,18 @@
 //              heads.
 //   window     the x rows of its 64 padded quad-tile tokens (49 at window 7)
 //              are staged in LDS as 1 KB blocks (16 tokens x 32 channels),
-//              the next window's rows waiting in registers; waves 0-2 form
-//              D = W' x^T for q, k and v (the head's 96 channels), the other
-//              waves the mean and 1/sigma of every token; then the folded epilogue
-//              writes q, k, v in bf16 into LDS in the attention's tile layout
-//              and each wave runs the attention of one query tile (the math
-//              of wattn_persistent.hip: bias and mask in the accumulator,
-//              exp2 softmax across lanes, V^T from transposing reads, the
-//              normaliser from an MFMA against ones).
+//              the next window's rows waiting in registers; the weight
+//              waves form D = W' x^T for q, k and v (the head's 96
+//              channels), the statistics waves the mean and 1/sigma of
+//              every token; then the folded epilogue writes q, k, v in bf16
+//              into LDS in the attention's tile layout and waves 0-3 run
+//              the attention of one query tile each (the math of
+//              wattn_persistent.hip: bias and mask in the accumulator, exp2
+//              softmax across lanes, V^T from transposing reads, the
+//              normaliser from an MFMA against ones).  4 waves: one window
+//              at a time.  8 waves: two windows in flight, the attention of
+//              window i - 1 beside the v products and statistics of window
+//              i (see the main loop).
 //   output     each lane stores 8 channels (16 bytes) of its query token;
 //              the two 64-byte halves of a token's line come from the
 //              workgroups of two heads on the same XCD and meet in its L2.
