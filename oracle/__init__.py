@@ -56,6 +56,9 @@ def lib():
         L.oracle_layernorm.restype = I
         L.oracle_swin_wattn_bwd.argtypes = [P, I, P, P, I, I, I, I, I, I, I, I, I, P, P]
         L.oracle_swin_wattn_bwd.restype = I
+        L.oracle_dequant_qkv_i8.argtypes = [P, L64, I, P, P]
+        L.oracle_linear_i8.argtypes = [P, L64, I, ctypes.c_float, P, I, P, P, P, I, P, I, P, P, P]
+        L.oracle_linear_i8.restype = I
         _lib = L
     return _lib
 
@@ -235,3 +238,67 @@ def swin_wattn_bwd(qkv, table, dout, window: int, shift: int, nthreads: int = 0,
     if used < 0:
         raise ValueError("oracle rejected the arguments")
     return (dq, dt, used) if return_threads else (dq, dt)
+
+
+def dequant_qkv_i8(codes, scales) -> np.ndarray:
+    """INT8 q, k, v codes ``[..., 3, heads, head_dim]`` (int8) times one
+    scale per part (query, key, value); returns float64 of the same shape."""
+    c = np.ascontiguousarray(codes, dtype=np.int8)
+    assert c.ndim >= 3 and c.shape[-3] == 3
+    C = c.shape[-2] * c.shape[-1]
+    tokens = c.size // (3 * C)
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    assert sc.shape == (3,)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib().oracle_dequant_qkv_i8(_ptr(c), tokens, C, _ptr(sc), _ptr(out))
+    return out
+
+
+def swin_wattn_fwd_i8(codes, scales, table, window: int, shift: int, nthreads: int = 0,
+                      return_threads: bool = False):
+    """The forward of INT8 q, k, v: the fp64 forward of the dequantized
+    codes.  ``codes [B,H,W,3,heads,head_dim]`` int8, ``scales`` (query, key,
+    value) float32."""
+    return swin_wattn_fwd(dequant_qkv_i8(codes, scales), table, window, shift,
+                          nthreads=nthreads, return_threads=return_threads)
+
+
+def linear_i8(xq, sx: float, wq, sw, bias=None, residual=None, so=None, nthreads: int = 0,
+              return_threads: bool = False):
+    """INT8 linear layer.  ``xq [..., K]`` int8 codes with scale ``sx``;
+    ``wq [N, K]`` int8 codes with per-output-channel scales ``sw [N]``;
+    ``bias [N]`` float32; ``residual [..., N]`` (uint16 = bfloat16
+    patterns, float32 or float64); ``so [N]`` output scales for INT8 output
+    (no residual then).  Returns ``(acc int64, y float64, yq int8 or None)``:
+    the exact integer sums, the dequantized value and the output codes."""
+    x = np.ascontiguousarray(xq, dtype=np.int8)
+    w = np.ascontiguousarray(wq, dtype=np.int8)
+    N, K = w.shape
+    assert x.shape[-1] == K
+    lead = x.shape[:-1]
+    T = int(np.prod(lead)) if lead else 1
+    swa = np.ascontiguousarray(sw, dtype=np.float32)
+    assert swa.shape == (N,)
+    bp = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.shape == (N,)
+        bp = _ptr(bias)
+    rp, rc = None, F64
+    if residual is not None:
+        rq, rc = _qkv_arg(residual)
+        assert rq.shape == lead + (N,)
+        rp = _ptr(rq)
+    sop, yq = None, None
+    if so is not None:
+        so = np.ascontiguousarray(so, dtype=np.float32)
+        assert so.shape == (N,)
+        sop = so.ctypes.data_as(ctypes.c_void_p)
+        yq = np.empty(lead + (N,), dtype=np.int8)
+    acc = np.empty(lead + (N,), dtype=np.int64)
+    y = np.empty(lead + (N,), dtype=np.float64)
+    used = lib().oracle_linear_i8(_ptr(x), T, K, float(sx), _ptr(w), N, _ptr(swa), bp, rp, rc, sop,
+                                  nthreads, _ptr(acc), _ptr(y), None if yq is None else _ptr(yq))
+    if used < 0:
+        raise ValueError("oracle rejected the arguments")
+    return ((acc, y, yq), used) if return_threads else (acc, y, yq)

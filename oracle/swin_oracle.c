@@ -379,6 +379,82 @@ int oracle_linear(const void* x, int xdtype, long T, int K, const void* w, int w
 }
 
 /* ---------------------------------------------------------------------- */
+/* INT8 quantized tensors                                                   */
+
+void oracle_dequant_qkv_i8(const int8_t* codes, long tokens, int C, const float* scales,
+                           double* out) {
+  for (long t = 0; t < tokens; ++t)
+    for (int part = 0; part < 3; ++part)
+      for (int c = 0; c < C; ++c) {
+        const long i = (t * 3 + part) * C + c;
+        out[i] = (double)codes[i] * (double)scales[part];
+      }
+}
+
+typedef struct {
+  const int8_t* x;
+  const int8_t* w;
+  const void* r;
+  const float *sw, *bias, *so;
+  float sx;
+  int rdtype, K, N;
+  long t0, t1;
+  int64_t* acc;
+  double* y;
+  int8_t* yq;
+} linear_i8_job;
+
+static void* linear_i8_worker(void* arg) {
+  const linear_i8_job* J = (const linear_i8_job*)arg;
+  for (long t = J->t0; t < J->t1; ++t)
+    for (int j = 0; j < J->N; ++j) {
+      /* the integer sum, exact */
+      int64_t a = 0;
+      for (int c = 0; c < J->K; ++c)
+        a += (int64_t)J->x[t * J->K + c] * (int64_t)J->w[(long)j * J->K + c];
+      const double b = J->bias ? (double)J->bias[j] : 0.0;
+      const long o = t * J->N + j;
+      if (J->acc) J->acc[o] = a;
+      /* dequantized value, fp64 */
+      if (J->y) {
+        double v = (double)a * (double)J->sx * (double)J->sw[j] + b;
+        if (J->r) v += load_elem(J->r, J->rdtype, o);
+        J->y[o] = v;
+      }
+      /* the output code, decided in fp32 as one fused multiply-add */
+      if (J->yq) {
+        const float scale = (J->sx * J->sw[j]) / J->so[j];
+        const float shift = (J->bias ? J->bias[j] : 0.0f) / J->so[j];
+        float q = nearbyintf(fmaf((float)a, scale, shift));
+        q = q > 127.0f ? 127.0f : q < -127.0f ? -127.0f : q;
+        J->yq[o] = (int8_t)q;
+      }
+    }
+  return NULL;
+}
+
+int oracle_linear_i8(const int8_t* xq, long T, int K, float sx, const int8_t* wq, int N,
+                     const float* sw, const float* bias, const void* residual, int rdtype,
+                     const float* so, int nthreads, int64_t* acc, double* y, int8_t* yq) {
+  if (T < 0 || K <= 0 || N <= 0 || !xq || !wq || !sw || rdtype < ORACLE_F64 ||
+      rdtype > ORACLE_BF16 || (yq && !so) || (so && residual))
+    return -1;
+  nthreads = resolve_threads(nthreads, T > 0 ? T : 1);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  linear_i8_job* jobs = (linear_i8_job*)malloc(sizeof(linear_i8_job) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    linear_i8_job J = {xq, wq, residual, sw, bias, so, sx, rdtype, K, N,
+                       T * i / nthreads, T * (i + 1) / nthreads, acc, y, yq};
+    jobs[i] = J;
+    pthread_create(&th[i], NULL, linear_i8_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  return nthreads;
+}
+
+/* ---------------------------------------------------------------------- */
 /* layer normalisation: two passes over each row, mean then variance */
 
 int oracle_layernorm(const void* x, int xdtype, long T, int C, const float* gamma,

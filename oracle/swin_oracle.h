@@ -109,6 +109,32 @@ int oracle_swin_wattn_windows(const void* qkv, int dtype, const float* table, in
 int oracle_linear(const void* x, int xdtype, long T, int K, const void* w, int wdtype, int N,
                   const float* bias, const void* residual, int rdtype, int nthreads, double* y);
 
+/* INT8 quantized q, k and v (NVIDIA talk, section 3, INT8 quantization:
+ * tensors quantized to INT8 carry a scale, and dequantizing multiplies the
+ * code by it).  codes [tokens][3][C] int8, one scale per part (query, key,
+ * value): out[t][p][c] = codes[t][p][c] * scales[p], fp64.  The INT8
+ * attention is the forward of these dequantized values. */
+void oracle_dequant_qkv_i8(const int8_t* codes, long tokens, int C, const float* scales,
+                           double* out);
+
+/* INT8 linear layer (NVIDIA talk, section 3, INT8 quantization: input and
+ * weight quantized to INT8, products accumulated in INT32, the sum
+ * dequantized; bias and residual stay in floating point).  xq [T][K] int8
+ * codes with one scale sx; wq [N][K] int8 codes with one scale per output
+ * channel sw[N]; bias [N] fp32 or NULL:
+ *   acc[t][j] = sum_c xq[t][c] * wq[j][c]                        exact, 64-bit
+ *   y[t][j]   = acc[t][j] * sx * sw[j] + bias[j] (+ residual[t][j])      fp64
+ * INT8 output (so != NULL, the form the talk takes for Swin): y is quantized
+ * again with the scale so[j] of its column, a decision taken in fp32 as one
+ * fused multiply-add per output (fl = round to nearest fp32):
+ *   yq[t][j] = clamp(round_half_even(fma(fl(acc), fl(fl(sx*sw[j]) / so[j]),
+ *                                        fl(bias[j] / so[j]))), -127, 127)
+ * No residual with INT8 output.  acc, y and yq may each be NULL (not
+ * computed).  Returns the thread count used, or -1 on bad arguments. */
+int oracle_linear_i8(const int8_t* xq, long T, int K, float sx, const int8_t* wq, int N,
+                     const float* sw, const float* bias, const void* residual, int rdtype,
+                     const float* so, int nthreads, int64_t* acc, double* y, int8_t* yq);
+
 /* Layer normalisation over the last dimension, fp64:
  *   mu[t] = mean_c x[t][c],  var[t] = mean_c (x[t][c] - mu[t])^2
  *   y[t][c] = (x[t][c] - mu[t]) / sqrt(var[t] + eps) * gamma[c] + beta[c]

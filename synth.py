@@ -235,3 +235,42 @@ def ln_attn_inputs(name: str, batch: int | None = None):
     table = attention_table(a["seed"], a["heads"], a["window"])
     return x.reshape(B, a["H"], a["W"], C), gamma, beta, w, bias, table
 
+
+
+# ---------------------------------------------------------------------------
+# INT8 workloads: integer codes drawn from a normal of std 32, rounded to the
+# nearest integer and clipped to [-127, 127] (about 1 draw in 10^4 sits at
+# an end), and one float32 scale per tensor or channel.  The codes and the
+# scales are the inputs; nothing here quantizes a floating-point tensor.
+
+def int8_codes(key: int, n: int, std: float = 32.0) -> np.ndarray:
+    """``n`` int8 codes: rounded normal draws of ``std``, clipped to +-127."""
+    return np.clip(np.rint(normal(key, n, std)), -127, 127).astype(np.int8)
+
+
+# INT8 attention: q, k, v codes with one scale each (dequantized std about 1),
+# at the shapes of the bf16 attention workloads (same seeds, same bias table)
+I8_ATTN_SCALES = (0.031, 0.029, 0.033)
+I8_WORKLOADS = {
+    "swin-l-s1-i8": dict(attn="swin-l-s1", desc="Swin-L stage 1, B=64, 56x56, C=192, INT8 q/k/v"),
+    "swin-t-s1-i8": dict(attn="swin-t-s1", desc="Swin-T stage 1, B=32, 56x56, C=96, INT8 q/k/v"),
+    "swin-t-s3-i8": dict(attn="swin-t-s3", desc="Swin-T stage 3, B=64, 14x14, C=384, INT8 q/k/v"),
+    "swin-l-384-i8": dict(attn="swin-l-384", desc="Swin-L at 384px, B=16, 96x96, C=192, window 12, "
+                                                   "INT8 q/k/v"),
+}
+
+
+def make_i8_inputs(B: int, H: int, W: int, heads: int, head_dim: int, window: int, seed: int,
+                   scales=I8_ATTN_SCALES):
+    """Returns ``(codes [B,H,W,3,heads,head_dim] int8, scales [3] float32,
+    table [(2*window-1)**2, heads] float32)``."""
+    n = B * H * W * 3 * heads * head_dim
+    codes = int8_codes(stream_key(seed, 10), n).reshape(B, H, W, 3, heads, head_dim)
+    return codes, np.array(scales, dtype=np.float32), attention_table(seed, heads, window)
+
+
+def i8_inputs(name: str, batch: int | None = None):
+    """Inputs of a named INT8 attention workload (optionally its first images)."""
+    a = WORKLOADS[I8_WORKLOADS[name]["attn"]]
+    B = a["B"] if batch is None else batch
+    return make_i8_inputs(B, a["H"], a["W"], a["heads"], a["head_dim"], a["window"], a["seed"])

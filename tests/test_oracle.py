@@ -525,3 +525,97 @@ def test_backward_invariants(oracle_lib):
     dq0, dt0 = oracle.swin_wattn_bwd(q0, table, g, M, s)
     assert np.all(dq0[:, :, :, :2] == 0.0) and np.all(dt0 == 0.0)
     assert np.any(dq0[:, :, :, 2] != 0.0)
+
+
+# ------------------------------------------------------------------- INT8
+
+def test_dequant_qkv_i8_golden(oracle_lib):
+    # hand-worked: catches a scale applied to the wrong part
+    codes = np.array([[-127, 3], [0, 127], [-1, 64]], dtype=np.int8).reshape(1, 3, 1, 2)
+    got = oracle.dequant_qkv_i8(codes, [0.5, 0.25, 2.0])
+    assert np.array_equal(got.reshape(3, 2), _golden("dequant_qkv_i8_c2.txt"))
+
+
+@pytest.mark.parametrize("B,H,W,nh,M,s", [(2, 14, 14, 2, 7, 3), (1, 24, 24, 3, 12, 6), (1, 8, 12, 1, 4, 0)])
+def test_forward_i8_matches_torch_sdpa_float64(oracle_lib, B, H, W, nh, M, s):
+    # the codes dequantized by torch broadcasting, then the library
+    # composition: catches a scale taken from the wrong part or a code read
+    # as unsigned
+    codes, scales, table = synth.make_i8_inputs(B, H, W, nh, 32, M, seed=91 + M,
+                                                scales=(0.05, 0.02, 0.07))
+    codes[0, 0, 0, :, 0, :3] = np.array([-128, 127, -1], dtype=np.int8)  # the extreme codes
+    sc = torch.tensor(scales.astype(np.float64)).view(3, 1, 1)
+    x = torch.from_numpy(codes.astype(np.int64)).double() * sc
+    ref = _torch_reference(x.numpy(), table, M, s)
+    got = oracle.swin_wattn_fwd_i8(codes, scales, table, M, s)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_forward_i8_scale_invariances(oracle_lib):
+    # exact invariances of the definition: the scores see only the product of
+    # the query and key scales, and the output is linear in the value scale.
+    # Catches the value scale applied to the query or key (then the output
+    # would not scale linearly) and a query or key scale that is dropped.
+    codes, _, table = synth.make_i8_inputs(1, 14, 14, 2, 32, 7, seed=95)
+    base = oracle.swin_wattn_fwd_i8(codes, [0.04, 0.03, 0.02], table, 7, 3)
+    swapped = oracle.swin_wattn_fwd_i8(codes, [0.16, 0.0075, 0.02], table, 7, 3)
+    assert np.max(np.abs(swapped - base)) < 1e-12
+    tripled = oracle.swin_wattn_fwd_i8(codes, [0.04, 0.03, 0.06], table, 7, 3)
+    assert np.max(np.abs(tripled - 3 * base)) < 1e-12
+    sharper = oracle.swin_wattn_fwd_i8(codes, [0.08, 0.03, 0.02], table, 7, 3)
+    assert np.max(np.abs(sharper - base)) > 1e-3
+
+
+def test_linear_i8_golden(oracle_lib):
+    # hand-worked: ties to even and saturation at +-127 (never -128)
+    x = np.array([[3, -2], [5, 7]], dtype=np.int8)
+    w = np.array([[10, 20], [-7, 1], [1, 0], [-127, 127]], dtype=np.int8)
+    acc, y, yq = oracle.linear_i8(x, 0.5, w, [0.25, 2, 1, 1], bias=[0.5, -1, 0, 0],
+                                  so=[1, 4, 1, 0.25])
+    g = _golden("linear_i8_t2_k2_n4.txt")
+    assert np.array_equal(acc, np.array([[-10, -23, 3, -635], [190, -28, 5, 254]]))
+    assert np.array_equal(y, g[:2]) and np.array_equal(yq.astype(np.float64), g[2:])
+
+
+@pytest.mark.parametrize("T,K,N,with_res", [(37, 96, 288, False), (64, 192, 576, True), (5, 1536, 64, False)])
+def test_linear_i8_matches_numpy(oracle_lib, T, K, N, with_res):
+    # exact integer sums against numpy's int64 product; the dequantized value
+    # against numpy float64; catches a transposed weight, a per-channel scale
+    # taken by input channel, or a dropped bias or residual
+    x = synth.int8_codes(synth.stream_key(7, 0), T * K).reshape(T, K)
+    w = synth.int8_codes(synth.stream_key(7, 1), N * K).reshape(N, K)
+    sw = np.abs(synth.normal(synth.stream_key(7, 2), N, 1e-3)) + np.float32(1e-4)
+    b = synth.normal(synth.stream_key(7, 3), N, 0.1)
+    r = synth.normal(synth.stream_key(7, 4), T * N, 1.0).reshape(T, N) if with_res else None
+    acc, y, _ = oracle.linear_i8(x, 0.02, w, sw, bias=b, residual=r)
+    ref_acc = x.astype(np.int64) @ w.astype(np.int64).T
+    assert np.array_equal(acc, ref_acc)
+    ref = ref_acc.astype(np.float64) * 0.019999999552965164 * sw.astype(np.float64) + b
+    if with_res:
+        ref = ref + r
+    assert np.max(np.abs(y - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_linear_i8_codes_round_the_value(oracle_lib):
+    # the fp32 decision may differ from rounding the fp64 value only at a
+    # near-tie: every code is within 1/2 (plus fp32 rounding) of y / so and
+    # equals the rounded fp64 value away from ties; codes saturate at +-127
+    T, K, N = 256, 192, 96
+    x = synth.int8_codes(synth.stream_key(8, 0), T * K).reshape(T, K)
+    w = synth.int8_codes(synth.stream_key(8, 1), N * K).reshape(N, K)
+    sw = np.abs(synth.normal(synth.stream_key(8, 2), N, 1e-3)) + np.float32(1e-4)
+    b = synth.normal(synth.stream_key(8, 3), N, 0.5)
+    so = np.abs(synth.normal(synth.stream_key(8, 4), N, 0.02)) + np.float32(0.005)
+    so[:8] = 1e-4  # columns that saturate
+    acc, y, yq = oracle.linear_i8(x, 0.015, w, sw, bias=b, so=so)
+    v = y / so.astype(np.float64)
+    exact = np.clip(np.rint(v), -127, 127)
+    got = yq.astype(np.float64)
+    assert np.all(np.abs(got - exact) <= 1)
+    inside = np.abs(v) < 126
+    assert np.all(np.abs(got[inside] - v[inside]) <= 0.5 + 1e-5 * np.abs(v[inside]) + 1e-6)
+    far = np.abs(np.abs(v - np.floor(v)) - 0.5) > 1e-3
+    assert np.array_equal(got[far], exact[far])
+    sat = np.abs(v) >= 127.5
+    assert sat[:, :8].mean() > 0.9 and np.array_equal(got[sat], 127 * np.sign(v[sat]))
+    assert got.min() >= -127

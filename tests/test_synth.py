@@ -58,3 +58,14 @@ def test_ln_linear_inputs_prefix_and_shapes():
         assert x.shape == (4, w["K"]) and g.shape == (w["K"],) and wt.shape == (w["N"], w["K"])
         assert g.dtype == np.float32 and bias.shape == (w["N"],)
         assert np.array_equal(x, x2[:4]) and np.array_equal(g, g2) and np.array_equal(wt, wt2)
+
+
+def test_int8_codes_range_and_prefix():
+    key = synth.stream_key(5, 10)
+    c = synth.int8_codes(key, 100000)
+    assert c.dtype == np.int8 and c.min() >= -127 and c.max() <= 127
+    assert 31.0 < c.astype(np.float64).std() < 33.0
+    assert np.array_equal(synth.int8_codes(key, 1000), c[:1000])
+    codes, scales, table = synth.i8_inputs("swin-t-s3-i8", batch=2)
+    assert codes.shape == (2, 14, 14, 3, 12, 32) and scales.dtype == np.float32
+    assert np.array_equal(table, synth.workload_inputs("swin-t-s3", batch=1)[1])
