@@ -14,7 +14,8 @@ linear-layer workload (qkv-l-s1, proj-l-s1, ...) a
 step is one swin_linear_fwd over its tokens instead, with a layer norm +
 QKV workload (lnqkv-l-s1, ...) one swin_ln_linear_fwd, and with a layer norm
 + attention workload (lnattn-l-s1, lnattn-t-s1) one swin_ln_qkv_wattn_fwd
-(the two-kernel chain is timed beside it).
+(the two-kernel chain is timed beside it).  With an INT8 attention workload
+(swin-l-s1-i8, ...) a step is one swin_wattn_fwd_i8 over the workload.
 """
 from __future__ import annotations
 
@@ -39,6 +40,7 @@ CSRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc")
 # the sources that define each kernel family's device code
 KERNEL_SOURCES = {
     "wattn_fwd_bf16": ("wattn_internal.h", "wattn_common.h", "wattn_persistent.hip"),
+    "wattn_fwd_i8": ("wattn_internal.h", "wattn_common.h", "wattn_persistent.hip"),
     "ln_qkv_wattn": ("wattn_internal.h", "wattn_common.h", "ln_attn_internal.h", "ln_qkv_wattn.hip"),
     "linear_fwd": ("wattn_internal.h", "wattn_common.h", "linear_internal.h", "linear_gemm.hip"),
     "wattn_bwd_bf16": ("wattn_internal.h", "wattn_common.h", "bwd_internal.h", "wattn_backward.hip"),
@@ -56,13 +58,15 @@ def kernel_source_hash(family: str = "wattn_fwd_bf16") -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(B, H, W, heads, head_dim, window, elem=2):
-    """Bytes: qkv read once + out written once.  FLOPs: two contractions of
-    N x N x head_dim per window and head over the unpadded N."""
+def algorithmic(B, H, W, heads, head_dim, window, elem=2, out_elem=None):
+    """Bytes: qkv read once (`elem` bytes per element) + out written once
+    (`out_elem`, default `elem`).  FLOPs: two contractions of N x N x
+    head_dim per window and head over the unpadded N."""
     T = B * H * W
     C = heads * head_dim
     N = window * window
-    return 4 * C * T * elem, 4 * N * C * T
+    out_elem = elem if out_elem is None else out_elem
+    return 3 * C * T * elem + C * T * out_elem, 4 * N * C * T
 
 
 def bwd_algorithmic(B, H, W, heads, head_dim, window, elem=2):
@@ -75,16 +79,16 @@ def bwd_algorithmic(B, H, W, heads, head_dim, window, elem=2):
     return 7 * C * T * elem, 10 * N * C * T
 
 
-def fwd_kernel_name(window: int, heads: int) -> str:
-    """Name of the bf16 forward kernel the library launches.  Mirrors its
-    dispatch: head groups of 2, else 3, else 1 for windows of up to 4 tiles
-    of 16 tokens (window <= 8), 1 beyond."""
+def fwd_kernel_name(window: int, heads: int, i8: bool = False) -> str:
+    """Name of the bf16 (int8) forward kernel the library launches.  Mirrors
+    its dispatch: head groups of 2, else 3, else 1 for windows of up to 4
+    tiles of 16 tokens (window <= 8), 1 beyond."""
     q = (window + 3) // 4
     if q * q > 4:
         hg = 1
     else:
         hg = 2 if heads % 2 == 0 else 3 if heads % 3 == 0 else 1
-    return f"wattn_fwd_bf16_persistent<{window}, {hg}>"
+    return f"wattn_fwd_persistent<{window}, {hg}, {'true' if i8 else 'false'}>"
 
 
 def measured_traffic(workload: str, family: str = "wattn_fwd_bf16"):
@@ -118,6 +122,28 @@ def cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_re
     return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
             "kind": "oracle",
             "sample": f"{name}, first {sample_batch} of {w['B']} images, whole forward x{reps} "
+                      f"({dt:.1f} s wall, fp64, {used} threads)"}
+
+
+def i8_cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50):
+    """The fp64 oracle (dequantize, then the forward) on the first
+    `sample_batch` images of an INT8 workload, as cpu_baseline does."""
+    import oracle
+    import synth
+    a = synth.WORKLOADS[synth.I8_WORKLOADS[name]["attn"]]
+    codes, scales, table = synth.i8_inputs(name, batch=sample_batch)
+    reps, used = 0, 0
+    t0 = time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        _, used = oracle.swin_wattn_fwd_i8(codes, scales, table, a["window"], a["shifts"][0],
+                                           return_threads=True)
+        reps += 1
+    dt = time.perf_counter() - t0
+    nbytes, _ = algorithmic(sample_batch, a["H"], a["W"], a["heads"], a["head_dim"], a["window"],
+                            elem=1, out_elem=2)
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{name}, first {sample_batch} of {a['B']} images, whole forward x{reps} "
                       f"({dt:.1f} s wall, fp64, {used} threads)"}
 
 
@@ -508,6 +534,73 @@ def bwd_bench(args, torch, np) -> int:
     return 0
 
 
+def i8_bench(args, torch, np) -> int:
+    """One swin_wattn_fwd_i8 per step over the whole INT8 workload (first
+    shift)."""
+    import shifted_window_attention_swin_amd as swa
+    import synth
+    spec = synth.I8_WORKLOADS[args.workload]
+    a = synth.WORKLOADS[spec["attn"]]
+    B, H, W, nh, d, M = a["B"], a["H"], a["W"], a["heads"], a["head_dim"], a["window"]
+    s = a["shifts"][0]
+    dev = torch.device("cuda:0")
+    codes, scales, table_np = synth.i8_inputs(args.workload)
+    q0 = torch.from_numpy(codes).to(dev)
+    table = torch.from_numpy(table_np).to(dev)
+    del codes
+    sq, sk, sv = (float(x) for x in scales)
+    nbytes, nflops = algorithmic(B, H, W, nh, d, M, elem=1, out_elem=2)
+    sets = 1 if args.hot else 2 * MALL_BYTES // nbytes + 1
+    qs = [q0] + [q0.clone() for _ in range(sets - 1)]
+    outs = [torch.empty(B, H, W, nh * d, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        k = i % sets
+        swa.check(swa.swin_wattn_fwd_i8(qs[k], sq, sk, sv, table, outs[k], B, H, W, nh, d, M, s,
+                                        stream), "fwd_i8")
+
+    K = args.steps
+    total_ms, avg_launch_s, isolated_s = time_steps(torch, step, K, args.warmup, stream, 1)
+    value = nbytes * K / (total_ms / 1e3) / 1e9
+    achieved = nbytes / avg_launch_s / 1e9
+    result = {
+        "metric": f"shifted-window attn fwd GB/s & TFLOP/s ({spec['desc']}); % HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        # int8 codes in; exact products and sums on the bf16 MFMA path, bf16 out
+        "dtype": "i8",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, int8 codes = rint(N(0, 32)) clipped to "
+                "+-127, scales (q, k, v) = " + ", ".join(f"{x:g}" for x in scales)
+                + ", bias table ~ N(0,0.02))",
+        "config": {"workload": args.workload, "desc": spec["desc"], "B": B, "H": H, "W": W,
+                   "heads": nh, "head_dim": d, "window": M, "shift": s, "buffer_sets": sets,
+                   "cache": "hot" if args.hot else "cold", "out_dtype": "bf16"},
+        "tflops": round(nflops * K / (total_ms / 1e3) / 1e12, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, "wattn_fwd_i8"),
+                     "kernel": fwd_kernel_name(M, nh, i8=True),
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "isolated_launch_us": round(isolated_s * 1e6, 3),
+                     "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
+                     "mfma_tflops": round(nflops / avg_launch_s / 1e12, 3),
+                     "mfma_peak_tflops": BF16_PEAK_TFLOPS},
+        "cpu_baseline": None if args.no_cpu_baseline else
+        i8_cpu_baseline(args.workload, min(args.cpu_sample_batch, B)),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,6 +643,8 @@ def main() -> int:
         return linear_bench(args, torch, np)
     if args.workload in synth.LN_ATTN_WORKLOADS:
         return ln_attn_bench(args, torch, np)
+    if args.workload in synth.I8_WORKLOADS:
+        return i8_bench(args, torch, np)
     if args.backward:
         return bwd_bench(args, torch, np)
     w = synth.WORKLOADS[args.workload]

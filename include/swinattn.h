@@ -94,6 +94,28 @@ int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int 
 int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out, int B, int H,
                        int W, int heads, int head_dim, int window, int shift, void* stream);
 
+/* INT8 variant of swin_wattn_fwd (NVIDIA talk, section 3, INT8
+ * quantization: a tensor quantized to INT8 carries a scale, products of
+ * INT8 values are summed as integers and the sums are dequantized; the
+ * other operations stay in floating point, with INT8 input and output).
+ *   qkv       [B][H][W][3][heads][head_dim] int8 codes, contiguous, image
+ *             order; 16-byte aligned device pointer.  Code c of part p
+ *             (0 = query, 1 = key, 2 = value) stands for c * scale_p
+ *             (symmetric per-tensor quantization; every code -128..127 is
+ *             accepted).
+ *   scale_q, scale_k, scale_v   the three scales, host values.  scale_v must
+ *             lie in (0, 2^100] and scale_q * scale_k / sqrt(head_dim) in
+ *             [2^-100, 2^100], else SWIN_ERR_INVALID_ARG (NaN included).
+ *   rel_bias_table, out   as swin_wattn_fwd (out bf16, must not overlap qkv).
+ * The scores are the exact integer sums of code products (float32 holds
+ * them exactly) times scale_q * scale_k / sqrt(head_dim), plus bias and
+ * mask; softmax and value product as in swin_wattn_fwd, with the value
+ * codes taken exactly as bf16 and scale_v applied with the normaliser.
+ * Shapes, errors and guarantees otherwise as swin_wattn_fwd. */
+int swin_wattn_fwd_i8(const void* qkv, float scale_q, float scale_k, float scale_v,
+                      const float* rel_bias_table, void* out, int B, int H, int W, int heads,
+                      int head_dim, int window, int shift, void* stream);
+
 /* Backward of swin_wattn_fwd, for training (the NVIDIA talk, section 2,
  * fuses the window attention's backward too).  Given dout = dL/d(out), with
  * S = Q K^T / sqrt(d) + bias + mask, P = softmax(S) per window and head:

@@ -84,10 +84,11 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// 100*sqrt(d) as three bf16 pieces (each the top 8 significant bits of the
-// remainder); their sum is the fp32 value exactly, in any order
-void mask_pieces(int head_dim, float (&pieces)[3]) {
-  float rest = (float)(100.0 * sqrt((double)head_dim));
+// The mask value divided by the score scale (100 / scale), as three bf16
+// pieces (each the top 8 significant bits of the remainder); their sum is
+// the fp32 value exactly, in any order
+void mask_pieces(double value, float (&pieces)[3]) {
+  float rest = (float)value;
   for (int k = 0; k < 3; ++k) {
     uint32_t u;
     memcpy(&u, &rest, 4);
@@ -99,22 +100,40 @@ void mask_pieces(int head_dim, float (&pieces)[3]) {
   }
 }
 
+enum FwdKind { kFwdBf16, kFwdF32, kFwdI8 };
+
+// Scales of int8 codes: the score scale scale_q * scale_k / sqrt(head_dim)
+// must lie in [2^-100, 2^100] and scale_v in (0, 2^100], so that every
+// constant derived from them (the score scale, its inverse, the mask over
+// the score scale) is a normal fp32 number.
+bool i8_scales_ok(double sq, double sk, double sv, int head_dim) {
+  if (!(sq > 0.0) || !(sk > 0.0) || !(sv > 0.0) || !(sv <= 0x1p100)) return false;
+  const double sc = sq * sk / sqrt((double)head_dim);
+  return sc >= 0x1p-100 && sc <= 0x1p100;
+}
+
 int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int W, int heads,
-               int head_dim, int M, int s, void* stream, size_t elem, bool bf16) {
+               int head_dim, int M, int s, void* stream, FwdKind kind, float sq = 1.f,
+               float sk = 1.f, float sv = 1.f) {
   if (!qkv || !table || !out) return SWIN_ERR_INVALID_ARG;
   if (!aligned(qkv, 16) || !aligned(out, 16) || !aligned(table, 4)) return SWIN_ERR_INVALID_ARG;
   if (B < 0 || H <= 0 || W <= 0 || heads <= 0 || head_dim <= 0 || M <= 0) return SWIN_ERR_INVALID_ARG;
   if (H % M != 0 || W % M != 0 || s < 0 || s >= M) return SWIN_ERR_INVALID_ARG;
+  if (kind == kFwdI8 && !i8_scales_ok(sq, sk, sv, head_dim)) return SWIN_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || M > kMaxWindow) return SWIN_ERR_UNSUPPORTED;
-  // the fp32 kernel stages every head's bias table in LDS; the bf16 kernel
-  // stages one head group's when every head's would not fit
-  if (!bf16 && fwd_lds_bytes(M, heads) > (size_t)kMaxLds) return SWIN_ERR_UNSUPPORTED;
+  // the fp32 kernel stages every head's bias table in LDS; the persistent
+  // kernel stages one head group's when every head's would not fit
+  if (kind == kFwdF32 && fwd_lds_bytes(M, heads) > (size_t)kMaxLds) return SWIN_ERR_UNSUPPORTED;
+  const long long in_elem = kind == kFwdF32 ? 4 : kind == kFwdI8 ? 1 : 2;
+  const long long out_elem = kind == kFwdF32 ? 4 : 2;
   const long long nW = (long long)(H / M) * (W / M);
   const long long C = (long long)heads * head_dim;
-  const long long image_bytes = (long long)H * W * 3 * C * (long long)elem;
-  if (image_bytes > kMaxChunkBytes) return SWIN_ERR_UNSUPPORTED;
+  const long long image_bytes = (long long)H * W * 3 * C * in_elem;
+  const long long out_image_bytes = (long long)H * W * C * out_elem;
+  const long long max_image = image_bytes > out_image_bytes ? image_bytes : out_image_bytes;
+  if (max_image > kMaxChunkBytes) return SWIN_ERR_UNSUPPORTED;
   const long long tokens = (long long)B * H * W;
-  if (overlap(qkv, (size_t)(tokens * 3 * C) * elem, out, (size_t)(tokens * C) * elem))
+  if (overlap(qkv, (size_t)(tokens * 3 * C * in_elem), out, (size_t)(tokens * C * out_elem)))
     return SWIN_ERR_INVALID_ARG;
   if (B == 0) return SWIN_OK;
 
@@ -132,18 +151,22 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
   p.nWx = W / M;
   p.nW = (int)nW;
   const double sd = sqrt((double)head_dim);
-  p.score_scale = (float)(1.4426950408889634 / sd);
-  p.inv_scale = (float)sd;
+  // the score scale is 1/sqrt(d), times the query and key scales of int8 codes
+  const double sqk = kind == kFwdI8 ? (double)sq * (double)sk : 1.0;
+  p.score_scale = (float)(1.4426950408889634 * sqk / sd);
+  p.inv_scale = (float)(sd / sqk);
   p.mask_value = (float)(-100.0 * sd);
-  mask_pieces(head_dim, p.mask_pieces);
-  // bf16: the persistent LDS-staged kernel; fp32: the per-window kernel
+  mask_pieces(100.0 * sd / sqk, p.mask_pieces);
+  p.v_scale = kind == kFwdI8 ? sv : 1.f;
+  // bf16 and int8: the persistent LDS-staged kernel; fp32: the per-window kernel
   const int hg = head_group(heads, M);
-  const bool persistent = bf16;
+  const bool persistent = kind != kFwdF32;
   const int cus = persistent ? compute_units(dev) : 0;
   p.nhg = heads / hg;
-  // a unit's per-token slice is hg * 64 bytes: with odd hg and several head
-  // groups, neighbouring units of a window share 128-byte lines
-  p.xcd_ranges = (hg % 2 == 1 && p.nhg > 1) ? 1 : 0;
+  // a unit's per-token input slice is hg * 32 elements: with several head
+  // groups, neighbouring units of a window share 128-byte lines unless the
+  // slice is a whole number of lines
+  p.xcd_ranges = ((hg * kHeadDim * in_elem) % 128 != 0 && p.nhg > 1) ? 1 : 0;
   p.own_bias = 0;  // chosen per launch by the persistent kernel's launcher
   // fp32 kernel: heads are dealt round-robin to the waves of a workgroup,
   // preferably 2-3 heads per wave
@@ -155,7 +178,7 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
     }
   // images per launch: keeps every in-kernel byte offset below 2^31, and the
   // grid (windows of the launch) below 2^31
-  long long per = kMaxChunkBytes / image_bytes;
+  long long per = kMaxChunkBytes / max_image;
   if (per * nW * heads > 0x7fffffffLL) per = 0x7fffffffLL / (nW * heads);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const char* in = static_cast<const char*>(qkv);
@@ -163,12 +186,13 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
   for (long long b0 = 0; b0 < B; b0 += per) {
     const long long nb = B - b0 < per ? B - b0 : per;
     p.qkv = in + b0 * image_bytes;
-    p.out = o + b0 * (image_bytes / 3);
+    p.out = o + b0 * out_image_bytes;
     p.B = (int)nb;
     p.total_windows = (int)(nb * nW);
     p.units = (int)(nb * nW * p.nhg);
-    const hipError_t err = persistent ? launch_fwd_bf16_persistent(M, hg, p, dev, cus, st)
-                                      : launch_fwd_f32(M, p, waves, st);
+    const hipError_t err = kind == kFwdI8    ? launch_fwd_i8_persistent(M, hg, p, dev, cus, st)
+                           : kind == kFwdBf16 ? launch_fwd_bf16_persistent(M, hg, p, dev, cus, st)
+                                              : launch_fwd_f32(M, p, waves, st);
     if (err != hipSuccess) return SWIN_ERR_HIP;
   }
   return SWIN_OK;
@@ -236,14 +260,21 @@ int swin_wattn_precompute(int H, int W, int window, int shift, void* stream) {
 
 int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int B, int H, int W,
                    int heads, int head_dim, int window, int shift, void* stream) {
-  return fwd_common(qkv, rel_bias_table, out, B, H, W, heads, head_dim, window, shift, stream, 2,
-                    true);
+  return fwd_common(qkv, rel_bias_table, out, B, H, W, heads, head_dim, window, shift, stream,
+                    kFwdBf16);
+}
+
+int swin_wattn_fwd_i8(const void* qkv, float scale_q, float scale_k, float scale_v,
+                      const float* rel_bias_table, void* out, int B, int H, int W, int heads,
+                      int head_dim, int window, int shift, void* stream) {
+  return fwd_common(qkv, rel_bias_table, out, B, H, W, heads, head_dim, window, shift, stream,
+                    kFwdI8, scale_q, scale_k, scale_v);
 }
 
 int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out, int B, int H,
                        int W, int heads, int head_dim, int window, int shift, void* stream) {
-  return fwd_common(qkv, rel_bias_table, out, B, H, W, heads, head_dim, window, shift, stream, 4,
-                    false);
+  return fwd_common(qkv, rel_bias_table, out, B, H, W, heads, head_dim, window, shift, stream,
+                    kFwdF32);
 }
 
 int swin_linear_pack_weight(const void* weight, void* packed, int N, int K, void* stream) {
@@ -321,7 +352,7 @@ int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dou
   p.scale = (float)(1.0 / sd);
   p.score_scale = (float)(1.4426950408889634 / sd);
   p.inv_scale = (float)sd;
-  mask_pieces(head_dim, p.mask_pieces);
+  mask_pieces(100.0 * sd, p.mask_pieces);
   const int cus = compute_units(dev);
   // images per launch: in-kernel byte offsets stay below 2^31
   const long long per = kMaxChunkBytes / image_bytes;
@@ -440,7 +471,7 @@ int swin_ln_qkv_wattn_fwd(const void* x, const void* packed_qkv, const float* co
   const double sd = sqrt((double)head_dim);
   p.score_scale = (float)(1.4426950408889634 / sd);
   p.inv_scale = (float)sd;
-  mask_pieces(head_dim, p.mask_pieces);
+  mask_pieces(100.0 * sd, p.mask_pieces);
   const int cus = compute_units(dev);
   // images per launch: in-kernel byte offsets of x and out stay below 2^31
   const long long per = kMaxChunkBytes / image_bytes;

@@ -31,10 +31,12 @@ struct FwdParams {
   int xcd_ranges;           // persistent kernel: one contiguous unit range per XCD
   int own_bias;             // persistent kernel: 0 every head's tables, 1 the workgroup's head
                             // group's, 2 the current unit's head group's (restaged)
-  float score_scale;        // log2(e) / sqrt(head_dim)
-  float inv_scale;          // sqrt(head_dim): bias and mask are pre-divided by the scale
+  float score_scale;        // log2(e) * scale; scale = 1 / sqrt(head_dim) (times the query
+                            // and key scales for int8 codes)
+  float inv_scale;          // 1 / scale: bias and mask are pre-divided by the scale
   float mask_value;         // -100 * sqrt(head_dim)
-  float mask_pieces[3];     // bf16-exact parts summing to 100 * sqrt(head_dim) in fp32
+  float mask_pieces[3];     // bf16-exact parts summing to 100 * inv_scale in fp32
+  float v_scale;            // int8 forward: scale of the value codes
 };
 
 // Queues the precompute kernel.  rel_index [N*N], mask [nW*N*N],
@@ -56,5 +58,10 @@ size_t fwd_lds_bytes(int M, int nh);
 // device).
 hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
                                       hipStream_t stream);
+// The same kernel for int8 q, k, v codes (bf16 output); p.score_scale,
+// p.inv_scale and p.mask_pieces carry the query and key scales, p.v_scale the
+// value scale.
+hipError_t launch_fwd_i8_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
+                                    hipStream_t stream);
 
 }  // namespace swinattn

@@ -158,8 +158,30 @@ constexpr int fwd_minw() {
   return fwd_waves<M>() == 3 ? 3 : Unit<M, HG>::LEAN ? 5 : 1;
 }
 
-template <int M, int HG>
-__global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void wattn_fwd_bf16_persistent(FwdParams p) {
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// 8 int8 codes (two dwords, code k in byte k) as 8 bf16 values in the
+// 16-byte layout of a bf16 chunk.  bf16 holds every int8 value exactly.
+SWA_INLINE u32x4 widen_chunk(u32x2 v) {
+  bf16x8 r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    r[k] = (__bf16)(float)(int)(signed char)(v[k / 4] >> (8 * (k % 4)));
+  return __builtin_bit_cast(u32x4, r);
+}
+SWA_INLINE u32x4 widen_chunk(u32x4 v) { return v; }
+
+// The persistent forward.  I8: q, k and v arrive as int8 codes with one
+// scale per part.  A lane loads the 8 codes of its token part (8 bytes, in
+// place of 16 bytes of bf16) and writes them to LDS as bf16; from there the
+// math is the bf16 kernel's.  The score MFMA then sums 32 products of codes
+// (each at most 2^14 in magnitude) in fp32, which holds every such sum
+// exactly: it is the int32 accumulation of an int8 product.  The host folds
+// the query and key scales into the score scale (and so into the bias and
+// mask, which are pre-divided by it); the value scale multiplies the
+// normaliser.
+template <int M, int HG, bool I8>
+__global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void wattn_fwd_persistent(FwdParams p) {
   using S = Win<M>;
   using U = Unit<M, HG>;
   constexpr int NT = S::NT, NK = S::NK;
@@ -186,7 +208,9 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
   };
   const int g = lane >> 4, c = lane & 15;     // MFMA layout: lane group, token
   const int nh = p.nh;
-  const unsigned Cb = (unsigned)nh * kHeadDim * 2;  // bytes of one q (k, v, out) row
+  const unsigned Cb = (unsigned)nh * kHeadDim * 2;  // bytes of one bf16 q (k, v, out) row
+  constexpr unsigned EB = I8 ? 1 : 2;                // bytes of one input element
+  const unsigned Ci = (unsigned)nh * kHeadDim * EB;  // bytes of one input q (k, v) row
   const char* in = static_cast<const char*>(p.qkv);
   char* out = static_cast<char*>(p.out);
   const int units = p.units;
@@ -231,8 +255,10 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
     return q;
   };
 
-  // register-staged loads of one unit: slice s, tile wv + 4k of this wave
-  using Regs = u32x4[U::SLICES][U::TPW];  // raw 16-byte chunks
+  // register-staged loads of one unit: slice s, tile wv + 4k of this wave,
+  // raw chunks of 8 elements (16 bytes of bf16, 8 bytes of int8 codes)
+  using Chunk = std::conditional_t<I8, u32x2, u32x4>;
+  using Regs = Chunk[U::SLICES][U::TPW];
   auto issue_loads = [&](Regs& R, const Pos& q) {
 #pragma unroll
     for (int k = 0; k < U::TPW; ++k) {
@@ -242,10 +268,10 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
         tile_token<M>(t, cq, ty, tx);
         const bool ok = ty < M && tx < M;
         const unsigned pix = token_pixel(p, M, q.b, q.wy, q.wx, ty, tx, ok);
-        const char* src = in + pix * (3u * Cb) + (unsigned)q.hg * HG * kHeadDim * 2 + 16u * gq;
+        const char* src = in + pix * (3u * Ci) + (unsigned)q.hg * HG * kHeadDim * EB + 8u * EB * gq;
 #pragma unroll
         for (int s = 0; s < U::SLICES; ++s)
-          R[s][k] = *reinterpret_cast<const u32x4*>(src + (s / HG) * Cb + (s % HG) * kHeadDim * 2);
+          R[s][k] = *reinterpret_cast<const Chunk*>(src + (s / HG) * Ci + (s % HG) * kHeadDim * EB);
       }
     }
   };
@@ -277,7 +303,8 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
       if (t < NT) {
 #pragma unroll
         for (int s = 0; s < U::SLICES; ++s)
-          *reinterpret_cast<u32x4*>(s_unit + U::block(s, t) + uchunk(lane >> 2, lane & 3)) = R[s][k];
+          *reinterpret_cast<u32x4*>(s_unit + U::block(s, t) + uchunk(lane >> 2, lane & 3)) =
+              widen_chunk(R[s][k]);
       }
     }
   };
@@ -450,7 +477,7 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
         l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[kk], l4, 0, 0, 0);
       }
       if (ok) {
-        const float inv = fast_rcp(l4[0]);
+        const float inv = I8 ? fast_rcp(l4[0]) * p.v_scale : fast_rcp(l4[0]);
         bf16x8 ov;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -515,9 +542,9 @@ size_t lds_bytes_mh(int nh) {
   return ((bias + 15) & ~size_t(15)) + Unit<M, HG>::BYTES;
 }
 
-// workgroups of wattn_fwd_bf16_persistent<M, HG> resident per CU for `lds`
+// workgroups of wattn_fwd_persistent<M, HG, I8> resident per CU for `lds`
 // bytes of dynamic LDS; cached per device as (lds << 8 | blocks)
-template <int M, int HG>
+template <int M, int HG, bool I8>
 int blocks_per_cu(int dev, size_t lds, int slot) {
   static std::atomic<long long> cache[kMaxDevices][2];
   const bool cacheable = dev >= 0 && dev < kMaxDevices;
@@ -526,7 +553,7 @@ int blocks_per_cu(int dev, size_t lds, int slot) {
     if (c > 0 && (size_t)(c >> 8) == lds) return (int)(c & 255);
   }
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_fwd_bf16_persistent<M, HG>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wattn_fwd_persistent<M, HG, I8>,
                                                    Unit<M, HG>::kWaves * 64, lds) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -537,15 +564,15 @@ int blocks_per_cu(int dev, size_t lds, int slot) {
 
 // Grid for `lds` bytes per workgroup: CUs x resident workgroups, at most
 // one per unit, whole rounds of the 8 XCDs.
-template <int M, int HG>
+template <int M, int HG, bool I8>
 long long fwd_grid(const FwdParams& p, int dev, int cus, size_t lds, int slot) {
-  long long grid = (long long)cus * blocks_per_cu<M, HG>(dev, lds, slot);
+  long long grid = (long long)cus * blocks_per_cu<M, HG, I8>(dev, lds, slot);
   if (grid > p.units) grid = p.units;
   if (grid >= 8) grid &= ~7LL;  // whole XCD rounds (equal share per XCD)
   return grid;
 }
 
-template <int M, int HG>
+template <int M, int HG, bool I8>
 hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
   FwdParams p = p_in;
   p.own_bias = 0;
@@ -563,7 +590,7 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
     // ranges), so the grid is cut to a multiple of nhg (8 nhg): at most
     // 8 nhg - 8 workgroups fewer, e.g. 1008 instead of 1024 at 6 heads.
     if (p.nhg > 1) {
-      long long g = fwd_grid<M, HG>(p, dev, cus, small, 1);
+      long long g = fwd_grid<M, HG, I8>(p, dev, cus, small, 1);
       const bool xcd = p.xcd_ranges && g % 8 == 0;
       const long long q = xcd || Unit<M, HG>::LEAN ? 8LL * p.nhg : p.nhg;
       if (g >= q) g -= g % q;
@@ -572,13 +599,13 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
         lds = small;
         p.own_bias = 1;
       } else if (must_own) {
-        grid = fwd_grid<M, HG>(p, dev, cus, small, 1);
+        grid = fwd_grid<M, HG, I8>(p, dev, cus, small, 1);
         lds = small;
         p.own_bias = 2;
       }
     }
   }
-  if (grid < 0) grid = fwd_grid<M, HG>(p, dev, cus, lds, 0);
+  if (grid < 0) grid = fwd_grid<M, HG, I8>(p, dev, cus, lds, 0);
   // launches of at most two units per workgroup walk one contiguous range
   // per XCD (Swin-T stage 3: 10.6 -> 10.0 us); longer ones keep grid order,
   // which keeps the units in flight one compact stretch of the batch
@@ -587,21 +614,21 @@ hipError_t launch_mh(const FwdParams& p_in, int dev, int cus, hipStream_t st) {
   if (!p.xcd_ranges && p.nhg > 1 && grid % 8 == 0 && p.units <= 2 * grid &&
       (p.own_bias != 1 || (grid / 8) % p.nhg == 0))
     p.xcd_ranges = 1;
-  hipLaunchKernelGGL((wattn_fwd_bf16_persistent<M, HG>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((wattn_fwd_persistent<M, HG, I8>), dim3((unsigned)grid),
                      dim3(Unit<M, HG>::kWaves * 64), lds, st, p);
   return hipGetLastError();
 }
 
-template <int M>
+template <int M, bool I8>
 hipError_t launch_m(int HG, const FwdParams& p, int dev, int cus, hipStream_t st) {
   if constexpr (Win<M>::NT > 4) {  // larger windows: one head per unit
-    return HG == 1 ? launch_mh<M, 1>(p, dev, cus, st) : hipErrorInvalidValue;
+    return HG == 1 ? launch_mh<M, 1, I8>(p, dev, cus, st) : hipErrorInvalidValue;
   } else {
     switch (HG) {
-      case 1: return launch_mh<M, 1>(p, dev, cus, st);
-      case 2: return launch_mh<M, 2>(p, dev, cus, st);
-      case 3: return launch_mh<M, 3>(p, dev, cus, st);
-      case 4: return launch_mh<M, 4>(p, dev, cus, st);
+      case 1: return launch_mh<M, 1, I8>(p, dev, cus, st);
+      case 2: return launch_mh<M, 2, I8>(p, dev, cus, st);
+      case 3: return launch_mh<M, 3, I8>(p, dev, cus, st);
+      case 4: return launch_mh<M, 4, I8>(p, dev, cus, st);
       default: return hipErrorInvalidValue;
     }
   }
@@ -628,7 +655,15 @@ hipError_t launch_m(int HG, const FwdParams& p, int dev, int cus, hipStream_t st
 
 hipError_t launch_fwd_bf16_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
                                       hipStream_t stream) {
-#define SWA_LAUNCH(m) launch_m<m>(HG, p, dev, cus, stream)
+#define SWA_LAUNCH(m) launch_m<m, false>(HG, p, dev, cus, stream)
+  SWA_PERSISTENT_M(SWA_LAUNCH)
+#undef SWA_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_i8_persistent(int M, int HG, const FwdParams& p, int dev, int cus,
+                                    hipStream_t stream) {
+#define SWA_LAUNCH(m) launch_m<m, true>(HG, p, dev, cus, stream)
   SWA_PERSISTENT_M(SWA_LAUNCH)
 #undef SWA_LAUNCH
   return hipErrorInvalidValue;

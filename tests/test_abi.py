@@ -45,6 +45,14 @@ def test_status_strings():
 GOOD = dict(B=2, H=14, W=14, heads=2, head_dim=32, window=7, shift=3)
 
 
+def _fwd_i8(qkv, table, out, *rest):
+    """swin_wattn_fwd_i8 with valid scales, in the argument order of swin_wattn_fwd."""
+    return swa.swin_wattn_fwd_i8(qkv, 0.03, 0.03, 0.03, table, out, *rest)
+
+
+FWDS = [swa.swin_wattn_fwd, swa.swin_wattn_fwd_f32, _fwd_i8]
+
+
 def _fwd(fn=None, qkv=A16, table=A32, out=A48, **kw):
     a = dict(GOOD)
     a.update(kw)
@@ -53,7 +61,7 @@ def _fwd(fn=None, qkv=A16, table=A32, out=A48, **kw):
               a["shift"], 0)
 
 
-@pytest.mark.parametrize("fn", [swa.swin_wattn_fwd, swa.swin_wattn_fwd_f32])
+@pytest.mark.parametrize("fn", FWDS)
 def test_fwd_rejects_invalid_arguments(fn):
     E = swa.SWIN_ERR_INVALID_ARG
     assert _fwd(fn, qkv=0) == E
@@ -74,7 +82,7 @@ def test_fwd_rejects_invalid_arguments(fn):
     assert _fwd(fn, out=A16) == E              # out overlaps qkv
 
 
-@pytest.mark.parametrize("fn", [swa.swin_wattn_fwd, swa.swin_wattn_fwd_f32])
+@pytest.mark.parametrize("fn", FWDS)
 def test_fwd_reports_unsupported_configurations(fn):
     U = swa.SWIN_ERR_UNSUPPORTED
     assert _fwd(fn, head_dim=64) == U
@@ -92,9 +100,28 @@ def test_fp32_fwd_reports_bias_tables_beyond_lds():
     assert _fwd(swa.swin_wattn_fwd_f32, window=12, H=24, W=24, shift=0, heads=78) == U
 
 
-@pytest.mark.parametrize("fn", [swa.swin_wattn_fwd, swa.swin_wattn_fwd_f32])
+@pytest.mark.parametrize("fn", FWDS)
 def test_empty_batch_is_a_no_op(fn):
     assert _fwd(fn, B=0) == swa.SWIN_OK
+
+
+def test_fwd_i8_rejects_scales_out_of_range():
+    E = swa.SWIN_ERR_INVALID_ARG
+
+    def call(sq, sk, sv):
+        return swa.swin_wattn_fwd_i8(A16, sq, sk, sv, A32, A48, 2, 14, 14, 2, 32, 7, 3, 0)
+
+    nan, inf = float("nan"), float("inf")
+    for bad in [(0.0, 0.03, 0.03), (0.03, -0.03, 0.03), (0.03, 0.03, 0.0), (nan, 0.03, 0.03),
+                (0.03, nan, 0.03), (0.03, 0.03, nan), (inf, 0.03, 0.03), (0.03, 0.03, inf),
+                (1e-20, 1e-20, 1.0),     # score scale below 2^-100
+                (1e20, 1e20, 1.0),       # score scale above 2^100
+                (1.0, 1.0, 2.0 ** 101)]:
+        assert call(*bad) == E, bad
+    # near the range's ends: accepted (B = 0: nothing is queued)
+    lo, hi = 2.0 ** -48, 2.0 ** 50
+    assert swa.swin_wattn_fwd_i8(A16, lo, lo, 2.0 ** 100, A32, A48, 0, 14, 14, 2, 32, 7, 3, 0) == 0
+    assert swa.swin_wattn_fwd_i8(A16, hi, hi, 1.0, A32, A48, 0, 14, 14, 2, 32, 7, 3, 0) == 0
 
 
 def test_precompute_and_copies_reject_invalid_shapes():
