@@ -15,7 +15,8 @@ step is one swin_linear_fwd over its tokens instead, with a layer norm +
 QKV workload (lnqkv-l-s1, ...) one swin_ln_linear_fwd, and with a layer norm
 + attention workload (lnattn-l-s1, lnattn-t-s1) one swin_ln_qkv_wattn_fwd
 (the two-kernel chain is timed beside it).  With an INT8 attention workload
-(swin-l-s1-i8, ...) a step is one swin_wattn_fwd_i8 over the workload.
+(swin-l-s1-i8, ...) a step is one swin_wattn_fwd_i8 over the workload, and
+with an INT8 linear workload (qkv-l-s1-i8, ...) one swin_linear_i8_fwd.
 """
 from __future__ import annotations
 
@@ -33,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "shifted-window attn fwd GB/s & TFLOP/s (Swin-L stage1, bf16, B=64); % HBM peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
 MALL_BYTES = 256 * 2 ** 20
 CSRC = os.path.join(ROOT, "shifted_window_attention_swin_amd", "csrc")
 
@@ -218,6 +220,116 @@ def linear_kernel_name(K: int, N: int, residual: bool, layernorm: bool = False) 
     waves = 6 if ncb % 6 == 0 else 4 if ncb % 4 == 0 else 2
     mode = 2 if layernorm else 1 if residual else 0
     return f"linear_fwd_kernel<{K // 32}, {mode}, {waves}>"
+
+
+def linear_i8_kernel_name(K: int, N: int, residual: bool, out_i8: bool) -> str:
+    """The INT8 linear kernel the library launches: k-steps of 64 channels,
+    mode 3 bf16 output, 4 bf16 output + residual, 5 INT8 output."""
+    ncb = N // 32
+    waves = 6 if ncb % 6 == 0 else 4 if ncb % 4 == 0 else 2
+    mode = 5 if out_i8 else 4 if residual else 3
+    return f"linear_fwd_kernel<{(K + 63) // 64}, {mode}, {waves}>"
+
+
+def linear_i8_algorithmic(T, K, N, residual, out_i8):
+    """Bytes: x (int8) read once, y (int8 or bf16) written once, the bf16
+    residual read once.  FLOPs: one multiply-add per (token, input, output)."""
+    return T * K + T * N * (1 if out_i8 else 2) + (T * N * 2 if residual else 0), 2 * T * K * N
+
+
+def linear_i8_cpu_baseline(name: str, min_seconds: float = 10.0):
+    """The fp64 oracle of the INT8 linear layer on the first tokens of the
+    workload (grown until one call takes about `min_seconds` / 4)."""
+    import oracle
+    import synth
+    w = synth.LINEAR_I8_WORKLOADS[name]
+    n = 512
+    while True:
+        x, sx, wq, sw, b, r, so = synth.linear_i8_inputs(name, tokens=n)
+        t0 = time.perf_counter()
+        _, used = oracle.linear_i8(x, sx, wq, sw, b, residual=r, so=so, return_threads=True)
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds / 4 or n >= w["tokens"]:
+            break
+        n = min(w["tokens"], n * 4)
+    reps = 1
+    while time.perf_counter() - t0 < min_seconds and reps < 50:
+        oracle.linear_i8(x, sx, wq, sw, b, residual=r, so=so)
+        reps += 1
+    dt = time.perf_counter() - t0
+    nbytes, _ = linear_i8_algorithmic(n, w["K"], w["N"], w["residual"], w["out_i8"])
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{name}, first {n} of {w['tokens']} tokens x{reps} ({dt:.1f} s wall, "
+                      f"exact integer sums + fp64, {used} threads)"}
+
+
+def linear_i8_bench(args, torch, np) -> int:
+    """One swin_linear_i8_fwd per step over a whole INT8 linear workload."""
+    import shifted_window_attention_swin_amd as swa
+    import synth
+    w = synth.LINEAR_I8_WORKLOADS[args.workload]
+    T, K, N, res, out_i8 = w["tokens"], w["K"], w["N"], w["residual"], w["out_i8"]
+    dev = torch.device("cuda:0")
+    x_np, sx, w_np, sw_np, b_np, r_np, so_np = synth.linear_i8_inputs(args.workload)
+    x0 = torch.from_numpy(x_np).to(dev)
+    wq = torch.from_numpy(w_np).to(dev)
+    f32 = lambda a: None if a is None else torch.from_numpy(a).to(dev)
+    sw, bias, so = f32(sw_np), f32(b_np), f32(so_np)
+    r0 = torch.from_numpy(r_np.view(np.int16)).view(torch.bfloat16).to(dev) if res else None
+    del x_np, r_np
+    packed = torch.empty(N * ((K + 63) // 64) * 64, dtype=torch.int8, device=dev)
+    swa.check(swa.swin_linear_i8_pack_weight(wq, packed, N, K), "pack_i8")
+    nbytes, nflops = linear_i8_algorithmic(T, K, N, res, out_i8)
+    sets = 1 if args.hot else 2 * MALL_BYTES // nbytes + 1
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    rs = [r0] + [r0.clone() for _ in range(sets - 1)] if res else [None] * sets
+    ydt = torch.int8 if out_i8 else torch.bfloat16
+    ys = [torch.empty(T, N, dtype=ydt, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        k = i % sets
+        swa.check(swa.swin_linear_i8_fwd(xs[k], float(sx), packed, sw, bias, rs[k], so, ys[k], T, K, N,
+                                         stream), "linear_i8")
+
+    K_ = args.steps
+    total_ms, avg_launch_s, isolated_s = time_steps(torch, step, K_, args.warmup, stream, 1)
+    value = nbytes * K_ / (total_ms / 1e3) / 1e9
+    achieved = nbytes / avg_launch_s / 1e9
+    result = {
+        "metric": f"INT8 linear layer GB/s ({w['desc']}); % HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K_, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, int8 codes = rint(N(0, 32)) clipped to "
+                "+-127; x scale 1/32, weight row scales 0.02/32 x (1 + 0.1 z), bias ~ N(0,0.02)"
+                + (", output scales per q/k/v part" if out_i8 else ", bf16 residual ~ N(0,1)") + ")",
+        "config": {"workload": args.workload, "desc": w["desc"], "tokens": T, "K": K, "N": N,
+                   "residual": res, "out_dtype": "i8" if out_i8 else "bf16", "buffer_sets": sets,
+                   "cache": "hot" if args.hot else "cold"},
+        "tops": round(nflops * K_ / (total_ms / 1e3) / 1e12, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, "linear_fwd"),
+                     "kernel": linear_i8_kernel_name(K, N, res, out_i8),
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "isolated_launch_us": round(isolated_s * 1e6, 3),
+                     "alg_bytes_per_launch": nbytes, "alg_ops_per_launch": nflops,
+                     "mfma_tops": round(nflops / avg_launch_s / 1e12, 3),
+                     "mfma_peak_tops": INT8_PEAK_TOPS},
+        "cpu_baseline": None if args.no_cpu_baseline else linear_i8_cpu_baseline(args.workload),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def _linear_workload(name: str):
@@ -645,6 +757,8 @@ def main() -> int:
         return ln_attn_bench(args, torch, np)
     if args.workload in synth.I8_WORKLOADS:
         return i8_bench(args, torch, np)
+    if args.workload in synth.LINEAR_I8_WORKLOADS:
+        return linear_i8_bench(args, torch, np)
     if args.backward:
         return bwd_bench(args, torch, np)
     w = synth.WORKLOADS[args.workload]

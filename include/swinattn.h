@@ -167,6 +167,48 @@ int swin_linear_pack_weight(const void* weight, void* packed, int N, int K, void
 int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
                     const void* residual, void* y, long long T, int K, int N, void* stream);
 
+/* INT8 linear layer (NVIDIA talk, section 3, INT8 quantization: input and
+ * weight quantized to INT8, products accumulated in INT32 and the sums
+ * dequantized; bias, residual and layer norm stay in floating point; the
+ * INT8-output form, which the talk takes for Swin, quantizes the result
+ * again so that the next kernel reads INT8):
+ *   acc[t][j] = sum_c xq[t][c] * wq[j][c]                    (exact, int32)
+ *   bf16 output: y[t][j] = acc * (x_scale * w_scale[j]) + bias[j] (+ residual)
+ *                in float32, rounded to nearest-even bf16
+ *   int8 output: y[t][j] = clamp(rne(fma(acc, a_j, b_j)), -127, 127), with
+ *                a_j = x_scale * w_scale[j] / out_scale[j] and
+ *                b_j = bias[j] / out_scale[j] (float32 operations, each
+ *                rounded to nearest; rne = round half to even)
+ *
+ * swin_linear_i8_pack_weight: W [N][K] int8 codes (16-byte aligned device
+ * pointer) -> packed, N * ceil(K/64) * 64 bytes (zero where K is not a
+ * multiple of 64), caller-owned, 16-byte aligned, not overlapping W.  Once
+ * per weight; queued on `stream`.
+ *
+ * swin_linear_i8_fwd:
+ *   x          [T][K] int8 codes, contiguous, 16-byte aligned (device)
+ *   x_scale    scale of the x codes (host value, finite and > 0)
+ *   packed     the output of swin_linear_i8_pack_weight for this W
+ *   w_scale    [N] float32 scales of the rows of W (per output channel);
+ *              16-byte aligned device pointer, not NULL
+ *   bias       [N] float32, 16-byte aligned, or NULL (no bias)
+ *   residual   [T][N] bf16, 16-byte aligned, or NULL; bf16 output only; may
+ *              be y itself (in-place add), otherwise must not overlap y
+ *   out_scale  [N] float32 scales of the output columns (16-byte aligned;
+ *              finite and nonzero), or NULL for bf16 output; for the QKV
+ *              projection, columns [0,C) [C,2C) [2C,3C) carry the query,
+ *              key and value scales of swin_wattn_fwd_i8
+ *   y          [T][N] bf16, or int8 with out_scale; 16-byte aligned; must not
+ *              overlap x, packed, bias, w_scale or out_scale
+ * K and N must be positive multiples of 32 (else SWIN_ERR_INVALID_ARG);
+ * K <= 768 (else SWIN_ERR_UNSUPPORTED).  A residual with int8 output is
+ * SWIN_ERR_INVALID_ARG.  T == 0 queues nothing.  No allocation, no host
+ * synchronisation. */
+int swin_linear_i8_pack_weight(const void* weight, void* packed, int N, int K, void* stream);
+int swin_linear_i8_fwd(const void* x, float x_scale, const void* packed_weight,
+                       const float* w_scale, const float* bias, const void* residual,
+                       const float* out_scale, void* y, long long T, int K, int N, void* stream);
+
 /* Layer normalisation fused into the QKV projection:
  *   xn[t][c] = (x[t][c] - mean_t) / sqrt(var_t + eps) * gamma[c] + beta[c]
  *   y = xn W^T + bias

@@ -31,7 +31,8 @@ SWIN_ERR_HIP = -4
 EXPORTS = ("swin_wattn_precompute", "swin_wattn_fwd", "swin_wattn_fwd_f32", "swin_wattn_fwd_i8",
            "swin_wattn_bwd",
            "swin_wattn_copy_index", "swin_wattn_copy_mask", "swin_wattn_copy_region",
-           "swin_linear_pack_weight", "swin_linear_fwd", "swin_ln_linear_pack_weight",
+           "swin_linear_pack_weight", "swin_linear_fwd", "swin_linear_i8_pack_weight",
+           "swin_linear_i8_fwd", "swin_ln_linear_pack_weight",
            "swin_ln_linear_fwd", "swin_ln_qkv_wattn_fwd",
            "swin_wattn_release", "swin_wattn_status_string")
 
@@ -59,6 +60,8 @@ for _n in ("swin_wattn_copy_index", "swin_wattn_copy_mask", "swin_wattn_copy_reg
     getattr(_lib, _n).argtypes = [_I, _I, _I, _I, _P, _P]
 _lib.swin_linear_pack_weight.argtypes = [_P, _P, _I, _I, _P]
 _lib.swin_linear_fwd.argtypes = [_P, _P, _P, _P, _P, ctypes.c_longlong, _I, _I, _P]
+_lib.swin_linear_i8_pack_weight.argtypes = [_P, _P, _I, _I, _P]
+_lib.swin_linear_i8_fwd.argtypes = [_P, _F, _P, _P, _P, _P, _P, _P, ctypes.c_longlong, _I, _I, _P]
 _lib.swin_ln_linear_pack_weight.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _P]
 _lib.swin_ln_linear_fwd.argtypes = [_P, _P, _P, ctypes.c_float, _P, ctypes.c_longlong, _I, _I, _P]
 _lib.swin_ln_qkv_wattn_fwd.argtypes = [_P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _I, _I, _I, _I,
@@ -139,6 +142,17 @@ def swin_linear_fwd(x, packed_weight, bias, residual, y, T: int, K: int, N: int,
                     stream=None) -> int:
     return _lib.swin_linear_fwd(_addr(x), _addr(packed_weight), _addr(bias), _addr(residual),
                                 _addr(y), T, K, N, _stream(stream))
+
+
+def swin_linear_i8_pack_weight(weight, packed, N: int, K: int, stream=None) -> int:
+    return _lib.swin_linear_i8_pack_weight(_addr(weight), _addr(packed), N, K, _stream(stream))
+
+
+def swin_linear_i8_fwd(x, x_scale: float, packed_weight, w_scale, bias, residual, out_scale, y,
+                       T: int, K: int, N: int, stream=None) -> int:
+    return _lib.swin_linear_i8_fwd(_addr(x), x_scale, _addr(packed_weight), _addr(w_scale),
+                                   _addr(bias), _addr(residual), _addr(out_scale), _addr(y), T, K,
+                                   N, _stream(stream))
 
 
 def swin_ln_linear_pack_weight(weight, gamma, beta, bias, packed, consts, N: int, K: int,

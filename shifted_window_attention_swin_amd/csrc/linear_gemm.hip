@@ -37,8 +37,21 @@
 //              + residual (read as whole lines too), round to bf16,
 //              non-temporal 16-byte stores.  Halves of a line written by
 //              different waves cost a quarter more HBM write traffic.
+//
+// INT8 (same talk, section 3, INT8 quantization: input and weight in INT8,
+// products accumulated in INT32, the sums dequantized, bias and residual in
+// floating point; the INT8-output form quantizes the result again).  The
+// v_mfma_i32_16x16x64_i8 operands hold 16 bytes per lane at the byte
+// positions of the bf16 16x16x32 operands, so the kernel moves the same
+// bytes: a 64-byte k-step is 64 int8 input channels (K = 96 ends in half a
+// step: those lanes take zeros, and the packed weight is zero there).  The
+// int32 sums are converted to fp32 in the product layout: times x_scale *
+// w_scale[j], then bias (and residual) as above, rounded to bf16; or, for
+// INT8 output, the code clamp(rne(fma(sum, a_j, b_j)), -127, 127) with
+// a_j = x_scale * w_scale[j] / out_scale[j], b_j = bias[j] / out_scale[j].
 
 #include <atomic>
+#include <type_traits>
 
 #include "linear_internal.h"
 #include "wattn_common.h"
@@ -53,8 +66,18 @@ constexpr int kLinTiles = kLinRows / 16;
 // bytes per token of the fp32 output tile of a WAVES-wave workgroup (padded)
 constexpr int lin_out_stride(int waves) { return waves * 32 * 4 + 16; }
 
-// epilogue / prologue of the linear kernel
-enum LinMode { kLinPlain = 0, kLinResidual = 1, kLinLayerNorm = 2 };
+// epilogue / prologue of the linear kernel: bf16 x and weight (0-2); int8
+// x and weight with bf16 output (3, 4) or int8 output (5)
+enum LinMode {
+  kLinPlain = 0,
+  kLinResidual = 1,
+  kLinLayerNorm = 2,
+  kLinI8 = 3,
+  kLinI8Residual = 4,
+  kLinI8Out = 5
+};
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // sum over aligned groups of L = 4 or 8 lanes (DPP: lane ^ 1, lane ^ 2
 // within quads, then the mirror of each half row pairs the two quads)
@@ -77,7 +100,8 @@ constexpr size_t lin_ln_lds_bytes() { return kLinRows * 8; }
 // row of x (over its K channels) before the product.
 template <int KS, int MODE, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) {
-  constexpr bool RES = MODE == kLinResidual, LN = MODE == kLinLayerNorm;
+  constexpr bool RES = MODE == kLinResidual || MODE == kLinI8Residual, LN = MODE == kLinLayerNorm;
+  constexpr bool I8 = MODE >= kLinI8, I8OUT = MODE == kLinI8Out;
   constexpr int kLinWaves = WAVES;
   constexpr int kLinCols = 32 * WAVES;
   constexpr int kOutStride = lin_out_stride(WAVES);
@@ -102,8 +126,8 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   const char* xb = static_cast<const char*>(p.x);
   const char* rb = static_cast<const char*>(p.res);
   char* yb = static_cast<char*>(p.y);
-  const size_t xrow = (size_t)KS * 64;      // bytes of one x row
-  const size_t yrow = (size_t)p.N * 2;      // bytes of one y (residual) row
+  const size_t xrow = I8 ? (size_t)p.K : (size_t)KS * 64;  // bytes of one x row
+  const size_t yrow = (size_t)p.N * 2;      // bytes of one bf16 y (residual) row
 
   // This workgroup's column group and row blocks.  The grid is a multiple
   // of the column-group count, so a workgroup keeps one column group for the
@@ -140,13 +164,14 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   }
 
   // the wave's weight tiles stay in registers for the whole launch
-  bf16x8 a[KS][2];
+  using AOp = std::conditional_t<I8, i32x4, bf16x8>;
+  AOp a[KS][2];
   if (active) {
     const char* wcb = static_cast<const char*>(p.wp) + (size_t)cb * KS * 2048 + lane * 16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      a[ks][0] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2) * 1024);
-      a[ks][1] = *reinterpret_cast<const bf16x8*>(wcb + (ks * 2 + 1) * 1024);
+      a[ks][0] = *reinterpret_cast<const AOp*>(wcb + (ks * 2) * 1024);
+      a[ks][1] = *reinterpret_cast<const AOp*>(wcb + (ks * 2 + 1) * 1024);
     }
   }
   // the bias of the lane's 8 channels in each store slot j (zero without a
@@ -162,7 +187,35 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
     }
   };
   f32x4 bias[2][2];
-  if constexpr (!LN) load_bias(bias);
+  if constexpr (!LN && !I8OUT) load_bias(bias);
+  // int8: the dequantization constants of the 8 channels 8g + 4i + r of the
+  // wave's column block that lane (g, c) holds in the product layout:
+  // kq = x_scale * w_scale (bf16 output), or kq = x_scale * w_scale /
+  // out_scale and kb = bias / out_scale (int8 output)
+  f32x4 kq[I8 ? 2 : 1], kb[I8OUT ? 2 : 1];
+  if constexpr (I8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      kq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (I8OUT) kb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int ch = cb * 32 + 8 * g + 4 * i;
+      if (active && ch < p.N) {
+        const f32x4 sw = *reinterpret_cast<const f32x4*>(p.w_scale + ch);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kq[i][q] = p.x_scale * sw[q];
+        if constexpr (I8OUT) {
+          const f32x4 so = *reinterpret_cast<const f32x4*>(p.out_scale + ch);
+          f32x4 bi = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (p.bias) bi = *reinterpret_cast<const f32x4*>(p.bias + ch);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            kq[i][q] = kq[i][q] / so[q];  // correctly rounded fp32 division
+            kb[i][q] = bi[q] / so[q];
+          }
+        }
+      }
+    }
+  }
   // layer norm: the folded bias b'_j and row sum s_j of the 8 channels
   // 8g + 4i + r (i = 0, 1, r = 0..3) of the wave's column block that lane
   // (g, c) holds in the product layout, for the launch.  The epilogue is
@@ -255,7 +308,12 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
         const int tt = bi / KS, ks = bi - tt * KS;
         int tok = rr * kLinRows + tt * 16 + cq;
         if (tok >= T) tok = T - 1;
-        R[k] = *reinterpret_cast<const u32x4*>(xb + (size_t)tok * xrow + ks * 64 + 16 * gq);
+        // int8 rows of K = 64 KS - 32: the upper half of the last k-step
+        // lies past the row, and takes zeros (the packed weight is zero there)
+        if (I8 && ks == KS - 1 && p.half_step && gq >= 2)
+          R[k] = u32x4{0u, 0u, 0u, 0u};
+        else
+          R[k] = *reinterpret_cast<const u32x4*>(xb + (size_t)tok * xrow + ks * 64 + 16 * gq);
       }
     }
   };
@@ -288,19 +346,49 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
     if (r + step < r_end) issue(R, r + step);
     if (active) {
       f32x4 acc[kLinTiles][2];
+      if constexpr (I8) {
+        i32x4 iacc[kLinTiles][2];
 #pragma unroll
-      for (int tt = 0; tt < kLinTiles; ++tt) acc[tt][0] = acc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < kLinTiles; ++tt) iacc[tt][0] = iacc[tt][1] = i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        // keep each k-step's operand reads next to its products: hoisting
-        // every read of the row block would hold 8 * KS registers
-        __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < KS; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int tt = 0; tt < kLinTiles; ++tt) {
-          const bf16x8 b =
-              *reinterpret_cast<const bf16x8*>(s_x + (tt * KS + ks) * 1024 + uchunk(c, g));
-          acc[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][0], b, acc[tt][0], 0, 0, 0);
-          acc[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][1], b, acc[tt][1], 0, 0, 0);
+          for (int tt = 0; tt < kLinTiles; ++tt) {
+            const i32x4 b =
+                *reinterpret_cast<const i32x4*>(s_x + (tt * KS + ks) * 1024 + uchunk(c, g));
+            iacc[tt][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks][0], b, iacc[tt][0], 0, 0, 0);
+            iacc[tt][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks][1], b, iacc[tt][1], 0, 0, 0);
+          }
+        }
+        // dequantize in the product layout (int8 output: the code, as fp32)
+#pragma unroll
+        for (int tt = 0; tt < kLinTiles; ++tt)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float v = (float)iacc[tt][i][q];
+              if constexpr (I8OUT)
+                acc[tt][i][q] = fminf(fmaxf(__builtin_rintf(fmaf(v, kq[i][q], kb[i][q])), -127.f), 127.f);
+              else
+                acc[tt][i][q] = v * kq[i][q];
+            }
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < kLinTiles; ++tt) acc[tt][0] = acc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          // keep each k-step's operand reads next to its products: hoisting
+          // every read of the row block would hold 8 * KS registers
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int tt = 0; tt < kLinTiles; ++tt) {
+            const bf16x8 b =
+                *reinterpret_cast<const bf16x8*>(s_x + (tt * KS + ks) * 1024 + uchunk(c, g));
+            acc[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][0], b, acc[tt][0], 0, 0, 0);
+            acc[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][1], b, acc[tt][1], 0, 0, 0);
+          }
         }
       }
       if constexpr (LN) {
@@ -337,6 +425,17 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
         const char* o = s_o + srow[j] * kOutStride + (sch[j] - cg * kLinCols) * 4;
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(o);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(o + 16);
+        if constexpr (I8OUT) {
+          // 8 codes (exact integers in fp32), one byte each, 8-byte store
+          u32x2 packed = {0u, 0u};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            packed[0] |= ((unsigned)(int)v0[q] & 0xFFu) << (8 * q);
+            packed[1] |= ((unsigned)(int)v1[q] & 0xFFu) << (8 * q);
+          }
+          __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(yb + (size_t)tok * p.N + sch[j]));
+          continue;
+        }
         bf16x8 out;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -387,6 +486,27 @@ __global__ void linear_pack_kernel(const uint16_t* w, const float* gamma, uint16
     } else {
       *reinterpret_cast<u32x4*>(wp + e * 8) = src;
     }
+  }
+}
+
+// int8 weight [N][K]: packed[cb][ks][i][lane][s] = W[cb*32 + out_channel(i,
+// lane % 16)][ks*64 + 16*(lane/16) + s] for s < 16, zero past K (the bytes
+// of the bf16 packing with 64 int8 channels per k-step)
+__global__ void linear_pack_i8_kernel(const int8_t* w, int8_t* wp, int N, int K) {
+  const int KS = (K + 63) / 64;
+  const long long total = (long long)(N / 32) * KS * 2 * 64;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(e & 63);
+    const long long t = e >> 6;  // (cb * KS + ks) * 2 + i
+    const int i = (int)(t & 1);
+    const long long cks = t >> 1;
+    const int ks = (int)(cks % KS), cb = (int)(cks / KS);
+    const int row = cb * 32 + out_channel(i, lane % 16);
+    const int col = ks * 64 + 16 * (lane / 16);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (col < K) v = *reinterpret_cast<const u32x4*>(w + (size_t)row * K + col);
+    *reinterpret_cast<u32x4*>(wp + e * 16) = v;
   }
 }
 
@@ -460,6 +580,11 @@ hipError_t launch_linear_kr(const LinearParams& p, int dev, int cus, hipStream_t
 
 template <int KS>
 hipError_t launch_linear_ks(const LinearParams& p, int dev, int cus, hipStream_t st) {
+  if (p.w_scale) {
+    if (p.out_scale) return launch_linear_kr<KS, kLinI8Out>(p, dev, cus, st);
+    return p.res ? launch_linear_kr<KS, kLinI8Residual>(p, dev, cus, st)
+                 : launch_linear_kr<KS, kLinI8>(p, dev, cus, st);
+  }
   if (p.colsum) return launch_linear_kr<KS, kLinLayerNorm>(p, dev, cus, st);
   return p.res ? launch_linear_kr<KS, kLinResidual>(p, dev, cus, st)
                : launch_linear_kr<KS, kLinPlain>(p, dev, cus, st);
@@ -487,10 +612,23 @@ hipError_t launch_linear_pack(const void* w, const float* gamma, void* wp, int N
   return hipGetLastError();
 }
 
+hipError_t launch_linear_pack_i8(const void* w, void* wp, int N, int K, hipStream_t stream) {
+  const long long total = (long long)(N / 32) * ((K + 63) / 64) * 2 * 64;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(linear_pack_i8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const int8_t*>(w), static_cast<int8_t*>(wp), N, K);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(const LinearParams& q, int dev, int cus, hipStream_t stream) {
   LinearParams p = q;
   p.blocks = (int)((p.T + kLinRows - 1) / kLinRows);
-  switch (p.K / 32) {
+  // k-steps of 64 bytes: 32 bf16 channels, or 64 int8 channels (a last half
+  // step when K % 64 == 32)
+  p.half_step = p.w_scale && p.K % 64 != 0 ? 1 : 0;
+  switch (p.w_scale ? (p.K + 63) / 64 : p.K / 32) {
     case 1: return launch_linear_ks<1>(p, dev, cus, stream);
     case 2: return launch_linear_ks<2>(p, dev, cus, stream);
     case 3: return launch_linear_ks<3>(p, dev, cus, stream);

@@ -289,6 +289,17 @@ int swin_linear_pack_weight(const void* weight, void* packed, int N, int K, void
              : SWIN_ERR_HIP;
 }
 
+int swin_linear_i8_pack_weight(const void* weight, void* packed, int N, int K, void* stream) {
+  if (!weight || !packed || !aligned(weight, 16) || !aligned(packed, 16)) return SWIN_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return SWIN_ERR_INVALID_ARG;
+  if (K > kMaxLinearKI8) return SWIN_ERR_UNSUPPORTED;
+  if (overlap(weight, (size_t)N * K, packed, (size_t)N * ((K + 63) / 64) * 64))
+    return SWIN_ERR_INVALID_ARG;
+  return launch_linear_pack_i8(weight, packed, N, K, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SWIN_OK
+             : SWIN_ERR_HIP;
+}
+
 int swin_ln_linear_pack_weight(const void* weight, const float* gamma, const float* beta,
                                const float* bias, void* packed, float* consts, int N, int K,
                                void* stream) {
@@ -374,20 +385,32 @@ int swin_wattn_bwd(const void* qkv, const float* rel_bias_table, const void* dou
 
 namespace {
 
+// The linear layers.  bf16: w_scale null.  int8: x and the packed weight are
+// int8 codes, w_scale [N] the weight row scales; out_scale [N] (or null)
+// selects int8 output.
 int linear_common(const void* x, const float* colsum, float eps, const void* packed_weight,
                   const float* bias, const void* residual, void* y, long long T, int K, int N,
-                  void* stream) {
+                  void* stream, const float* w_scale = nullptr, float x_scale = 1.f,
+                  const float* out_scale = nullptr) {
+  const bool i8 = w_scale != nullptr;
   if (!x || !packed_weight || !y) return SWIN_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(packed_weight, 16) || !aligned(y, 16) ||
       (bias && !aligned(bias, 16)) || (residual && !aligned(residual, 16)))
     return SWIN_ERR_INVALID_ARG;
   if (colsum && (!aligned(colsum, 16) || !(eps >= 0.f))) return SWIN_ERR_INVALID_ARG;
+  if (i8 && (!aligned(w_scale, 16) || (out_scale && !aligned(out_scale, 16)) ||
+             !(x_scale > 0.f) || !(x_scale <= 3.0e38f) || (out_scale && residual)))
+    return SWIN_ERR_INVALID_ARG;
   if (T < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return SWIN_ERR_INVALID_ARG;
-  if (K > kMaxLinearK) return SWIN_ERR_UNSUPPORTED;
-  const size_t xb = (size_t)T * K * 2, yb = (size_t)T * N * 2, wb = (size_t)N * K * 2;
+  if (K > (i8 ? kMaxLinearKI8 : kMaxLinearK)) return SWIN_ERR_UNSUPPORTED;
+  const size_t xe = i8 ? 1 : 2, ye = out_scale ? 1 : 2;
+  const size_t xb = (size_t)T * K * xe, yb = (size_t)T * N * ye;
+  const size_t wb = i8 ? (size_t)N * ((K + 63) / 64) * 64 : (size_t)N * K * 2;
   if (overlap(y, yb, x, xb) || overlap(y, yb, packed_weight, wb) ||
       (bias && overlap(y, yb, bias, (size_t)N * 4)) ||
-      (colsum && overlap(y, yb, colsum, (size_t)N * 4)))
+      (colsum && overlap(y, yb, colsum, (size_t)N * 4)) ||
+      (w_scale && overlap(y, yb, w_scale, (size_t)N * 4)) ||
+      (out_scale && overlap(y, yb, out_scale, (size_t)N * 4)))
     return SWIN_ERR_INVALID_ARG;
   // the residual may be y itself (in-place residual add), or lie apart from it
   if (residual && residual != y && overlap(y, yb, residual, yb)) return SWIN_ERR_INVALID_ARG;
@@ -400,15 +423,18 @@ int linear_common(const void* x, const float* colsum, float eps, const void* pac
   p.bias = bias;
   p.colsum = colsum;
   p.eps = eps;
+  p.x_scale = x_scale;
+  p.w_scale = w_scale;
+  p.out_scale = out_scale;
   p.K = K;
   p.N = N;
   p.ncb = N / 32;
   // token indices inside the kernel are 32-bit: at most 2^30 tokens a launch
   for (long long t0 = 0; t0 < T; t0 += kMaxLinearTokens) {
     const long long n = T - t0 < kMaxLinearTokens ? T - t0 : kMaxLinearTokens;
-    p.x = static_cast<const char*>(x) + t0 * K * 2;
+    p.x = static_cast<const char*>(x) + t0 * K * (long long)xe;
     p.res = residual ? static_cast<const char*>(residual) + t0 * N * 2 : nullptr;
-    p.y = static_cast<char*>(y) + t0 * N * 2;
+    p.y = static_cast<char*>(y) + t0 * N * (long long)ye;
     p.T = n;
     if (launch_linear(p, dev, cus, static_cast<hipStream_t>(stream)) != hipSuccess)
       return SWIN_ERR_HIP;
@@ -421,6 +447,14 @@ int linear_common(const void* x, const float* colsum, float eps, const void* pac
 int swin_linear_fwd(const void* x, const void* packed_weight, const float* bias,
                     const void* residual, void* y, long long T, int K, int N, void* stream) {
   return linear_common(x, nullptr, 0.f, packed_weight, bias, residual, y, T, K, N, stream);
+}
+
+int swin_linear_i8_fwd(const void* x, float x_scale, const void* packed_weight,
+                       const float* w_scale, const float* bias, const void* residual,
+                       const float* out_scale, void* y, long long T, int K, int N, void* stream) {
+  if (!w_scale) return SWIN_ERR_INVALID_ARG;
+  return linear_common(x, nullptr, 0.f, packed_weight, bias, residual, y, T, K, N, stream, w_scale,
+                       x_scale, out_scale);
 }
 
 int swin_ln_linear_fwd(const void* x, const void* packed_weight, const float* consts, float eps,

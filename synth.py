@@ -274,3 +274,47 @@ def i8_inputs(name: str, batch: int | None = None):
     a = WORKLOADS[I8_WORKLOADS[name]["attn"]]
     B = a["B"] if batch is None else batch
     return make_i8_inputs(B, a["H"], a["W"], a["heads"], a["head_dim"], a["window"], a["seed"])
+
+
+# INT8 linear layers: x codes (scale 1/32, so x is about N(0, 1)), weight
+# codes with per-row scales (W about N(0, 0.02)), bias ~ N(0, 0.02).  The
+# QKV projections write INT8 with one output scale per part (query, key,
+# value: about 4 output spreads over 127, the scales swin_wattn_fwd_i8
+# reads); the output projection writes bf16 and adds a bf16 residual.
+LINEAR_I8_WORKLOADS = {
+    "qkv-l-s1-i8": dict(tokens=64 * 56 * 56, K=192, N=576, residual=False, out_i8=True, seed=2101,
+                        desc="Swin-L stage 1 QKV projection, B=64, 56x56, C=192, INT8 in and out"),
+    "qkv-t-s1-i8": dict(tokens=32 * 56 * 56, K=96, N=288, residual=False, out_i8=True, seed=2102,
+                        desc="Swin-T stage 1 QKV projection, B=32, 56x56, C=96, INT8 in and out"),
+    "proj-l-s1-i8": dict(tokens=64 * 56 * 56, K=192, N=192, residual=True, out_i8=False, seed=2103,
+                         desc="Swin-L stage 1 output projection + residual, B=64, 56x56, C=192, "
+                              "INT8 in, bf16 out"),
+}
+I8_QKV_PART_SCALES = (1.0, 0.9, 1.1)  # relative output scales of query, key, value
+
+
+def make_linear_i8_inputs(T: int, K: int, N: int, seed: int, residual: bool, out_i8: bool):
+    """Returns ``(x [T,K] int8, x_scale float32, w [N,K] int8, w_scale [N]
+    float32, bias [N] float32, res [T,N] bf16 patterns or None, out_scale [N]
+    float32 or None)``.  A smaller T gives a prefix of the tokens of a larger one."""
+    x = int8_codes(stream_key(seed, 0), T * K).reshape(T, K)
+    w = int8_codes(stream_key(seed, 1), N * K).reshape(N, K)
+    x_scale = np.float32(1.0 / 32.0)
+    spread = np.clip(normal(stream_key(seed, 2), N, 0.1) + np.float32(1.0), 0.5, 1.5)
+    w_scale = (spread * np.float32(0.02 / 32.0)).astype(np.float32)
+    bias = normal(stream_key(seed, 3), N, 0.02)
+    res = bf16_bits(normal(stream_key(seed, 4), T * N, 1.0)).reshape(T, N) if residual else None
+    out_scale = None
+    if out_i8:
+        base = np.float32(4.0 * 0.02 * np.sqrt(K) / 127.0)
+        part = np.repeat(np.array(I8_QKV_PART_SCALES, dtype=np.float32), N // 3) if N % 3 == 0 else \
+            np.ones(N, dtype=np.float32)
+        out_scale = (base * part).astype(np.float32)
+    return x, x_scale, w, w_scale, bias, res, out_scale
+
+
+def linear_i8_inputs(name: str, tokens: int | None = None):
+    """Inputs of a named INT8 linear workload (optionally its first tokens)."""
+    w = LINEAR_I8_WORKLOADS[name]
+    T = w["tokens"] if tokens is None else tokens
+    return make_linear_i8_inputs(T, w["K"], w["N"], w["seed"], w["residual"], w["out_i8"])

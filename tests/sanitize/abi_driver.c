@@ -57,6 +57,13 @@ int main(void) {
   expect(swin_wattn_fwd_f32(NULL, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I, "fwd fp32 null");
   expect(swin_wattn_fwd_i8(NULL, 0.03f, 0.03f, 0.03f, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I,
          "fwd int8 null");
+  expect(swin_linear_i8_fwd(A, 0.03f, Bp, NULL, NULL, NULL, NULL, C, 64, 192, 576, NULL), I,
+         "linear int8 no weight scales");
+  expect(swin_linear_i8_fwd(A, 0.03f, Bp, (const float*)C, NULL, A, (const float*)C, Bp, 64, 192,
+                            576, NULL), I, "linear int8 residual with int8 output");
+  expect(swin_linear_i8_fwd(A, 0.03f, Bp, (const float*)C, NULL, NULL, NULL, Bp, 64, 800, 576,
+                            NULL), U, "linear int8 K");
+  expect(swin_linear_i8_pack_weight(A, A, 576, 192, NULL), I, "linear int8 pack overlap");
   expect(swin_wattn_fwd_i8(A, 0.03f, 0.03f, 0.03f, C, A, 2, 14, 14, 2, 32, 7, 3, NULL), I,
          "fwd int8 overlap");
   expect(swin_wattn_fwd_i8(A, 0.0f, 0.03f, 0.03f, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I,

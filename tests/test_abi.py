@@ -159,6 +159,41 @@ def test_linear_rejects_invalid_arguments():
     assert swa.swin_linear_pack_weight(a, b, 576, 416) == U
 
 
+def test_linear_i8_rejects_invalid_arguments():
+    E, U = swa.SWIN_ERR_INVALID_ARG, swa.SWIN_ERR_UNSUPPORTED
+    a, b, c, ws, os_ = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20  # aligned, never dereferenced
+
+    def call(x=a, sx=0.03, wp=b, sw=ws, bias=None, res=None, so=None, y=c, T=64, K=192, N=576):
+        return swa.swin_linear_i8_fwd(x, sx, wp, sw, bias, res, so, y, T, K, N)
+
+    assert call(x=0) == E
+    assert call(wp=0) == E
+    assert call(sw=0) == E                  # the weight scales are required
+    assert call(y=0) == E
+    assert call(x=a + 8) == E               # misaligned
+    assert call(sw=ws + 4) == E
+    assert call(so=os_ + 8) == E
+    assert call(bias=a + 4) == E
+    assert call(sx=0.0) == E                # x scale must be finite and > 0
+    assert call(sx=-1.0) == E
+    assert call(sx=float("nan")) == E
+    assert call(sx=float("inf")) == E
+    assert call(res=c, so=os_) == E         # no residual with int8 output
+    assert call(T=-1) == E
+    assert call(K=100) == E                 # K % 32
+    assert call(N=500) == E                 # N % 32
+    assert call(K=800) == U                 # K > 768
+    assert call(y=a) == E                   # y overlaps x
+    assert call(y=ws - 64, T=1, N=64) == E  # y overlaps the weight scales
+    assert call(T=0) == swa.SWIN_OK
+    assert call(T=0, so=os_, K=96) == swa.SWIN_OK
+    assert swa.swin_linear_i8_pack_weight(0, b, 576, 192) == E
+    assert swa.swin_linear_i8_pack_weight(a, b, 576, 100) == E
+    assert swa.swin_linear_i8_pack_weight(a, b, 500, 192) == E
+    assert swa.swin_linear_i8_pack_weight(a, a, 576, 192) == E   # packed overlaps W
+    assert swa.swin_linear_i8_pack_weight(a, b, 576, 800) == U
+
+
 def test_linear_empty_is_a_no_op():
     assert swa.swin_linear_fwd(1 << 20, 2 << 20, None, None, 3 << 20, 0, 192, 576) == swa.SWIN_OK
     # in-place residual (residual == y) is accepted
