@@ -105,6 +105,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   constexpr int kLinWaves = WAVES;
   constexpr int kLinCols = 32 * WAVES;
   constexpr int kOutStride = lin_out_stride(WAVES);
+  constexpr int kOut8Stride = kLinCols + 16;  // bytes per token of the int8 output tile
   constexpr int NB = kLinTiles * KS;                      // LDS blocks per row block
   constexpr int BPW = (NB + kLinWaves - 1) / kLinWaves;   // blocks loaded per wave
   constexpr int CPT = kLinCols / 8;                       // 16-byte chunks per token
@@ -152,11 +153,19 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
   const bool active = cb < p.ncb;
   // store phase: the output tile is kLinRows * CPT chunks of 16 bytes (8
   // channels); wave wv stores chunks 128 wv + 64 j + lane, j = 0, 1, in
-  // token-major order, so consecutive lanes cover whole lines of a token
+  // token-major order, so consecutive lanes cover whole lines of a token.
+  // int8 output: chunks of 16 channels (16 bytes), chunk 64 wv + lane
   int srow[2], sch[2];
   bool s_active[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    if constexpr (I8OUT) {
+      const int q = 64 * wv + lane;
+      srow[j] = q / (kLinCols / 16);
+      sch[j] = cg * kLinCols + 16 * (q - srow[j] * (kLinCols / 16));
+      s_active[j] = j == 0 && sch[j] < p.N;
+      continue;
+    }
     const int q = 128 * wv + 64 * j + lane;
     srow[j] = q / CPT;
     sch[j] = cg * kLinCols + 8 * (q - srow[j] * CPT);
@@ -361,19 +370,37 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
             iacc[tt][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks][1], b, iacc[tt][1], 0, 0, 0);
           }
         }
-        // dequantize in the product layout (int8 output: the code, as fp32)
+        if constexpr (I8OUT) {
+          // the code of every output: one fma, a clamp to +-127, then round
+          // half to even (adding 1.5 * 2^23 rounds to an integer and leaves
+          // it, in two's complement, in the low byte; the same code as
+          // rounding first and clamping after); lane (g, c) packs its 8
+          // consecutive channels into the int8 output tile
 #pragma unroll
-        for (int tt = 0; tt < kLinTiles; ++tt)
+          for (int tt = 0; tt < kLinTiles; ++tt) {
+            u32x2 w;
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i) {
+              unsigned word = 0u;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float v = (float)iacc[tt][i][q];
-              if constexpr (I8OUT)
-                acc[tt][i][q] = fminf(fmaxf(__builtin_rintf(fmaf(v, kq[i][q], kb[i][q])), -127.f), 127.f);
-              else
-                acc[tt][i][q] = v * kq[i][q];
+              for (int q = 0; q < 4; ++q) {
+                const float y = __builtin_amdgcn_fmed3f(
+                    fmaf((float)iacc[tt][i][q], kq[i][q], kb[i][q]), -127.f, 127.f);
+                word |= (__float_as_uint(y + 12582912.f) & 0xFFu) << (8 * q);
+              }
+              w[i] = word;
             }
+            *reinterpret_cast<u32x2*>(s_o + (tt * 16 + c) * kOut8Stride + wv * 32 + 8 * g) = w;
+          }
+        } else {
+          // dequantize in the product layout
+#pragma unroll
+          for (int tt = 0; tt < kLinTiles; ++tt)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[tt][i][q] = (float)iacc[tt][i][q] * kq[i][q];
+        }
       } else {
 #pragma unroll
         for (int tt = 0; tt < kLinTiles; ++tt) acc[tt][0] = acc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -407,11 +434,13 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
       }
       // lane (g, c) holds channels 8g + 4i + q of the wave's block for
       // token c of each tile: 8 consecutive floats of the output tile
+      if constexpr (!I8OUT) {
 #pragma unroll
-      for (int tt = 0; tt < kLinTiles; ++tt) {
-        char* o = s_o + (tt * 16 + c) * kOutStride + (wv * 32 + 8 * g) * 4;
-        *reinterpret_cast<f32x4*>(o) = acc[tt][0];
-        *reinterpret_cast<f32x4*>(o + 16) = acc[tt][1];
+        for (int tt = 0; tt < kLinTiles; ++tt) {
+          char* o = s_o + (tt * 16 + c) * kOutStride + (wv * 32 + 8 * g) * 4;
+          *reinterpret_cast<f32x4*>(o) = acc[tt][0];
+          *reinterpret_cast<f32x4*>(o + 16) = acc[tt][1];
+        }
       }
     } else if constexpr (LN) {
       ln_stats();
@@ -422,20 +451,23 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
     for (int j = 0; j < 2; ++j) {
       const int tok = tok0 + srow[j];
       if (s_active[j] && tok < T) {
+        if constexpr (I8OUT) {
+          // 16 codes, 16-byte store.  A workgroup of 4 or 6 waves writes
+          // whole 128-byte lines of a token, which the output never re-reads
+          // (non-temporal); narrower groups write parts of lines that other
+          // workgroups complete, which plain stores let meet in L2 (Swin-L
+          // stage 1 QKV: 46.2 against 58.6 us with plain stores; Swin-T
+          // stage 1, 2 waves: 19.8 against 22.2 us with non-temporal ones)
+          const u32x4 w = *reinterpret_cast<const u32x4*>(s_o + srow[j] * kOut8Stride + sch[j] -
+                                                          cg * kLinCols);
+          u32x4* dst = reinterpret_cast<u32x4*>(yb + (size_t)tok * p.N + sch[j]);
+          if constexpr (kLinCols >= 128) __builtin_nontemporal_store(w, dst);
+          else *dst = w;
+          continue;
+        }
         const char* o = s_o + srow[j] * kOutStride + (sch[j] - cg * kLinCols) * 4;
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(o);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(o + 16);
-        if constexpr (I8OUT) {
-          // 8 codes (exact integers in fp32), one byte each, 8-byte store
-          u32x2 packed = {0u, 0u};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            packed[0] |= ((unsigned)(int)v0[q] & 0xFFu) << (8 * q);
-            packed[1] |= ((unsigned)(int)v1[q] & 0xFFu) << (8 * q);
-          }
-          __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(yb + (size_t)tok * p.N + sch[j]));
-          continue;
-        }
         bf16x8 out;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
