@@ -94,8 +94,9 @@ SWA_INLINE float group_sum(float v) {
 // the row block's tokens
 constexpr size_t lin_ln_lds_bytes() { return kLinRows * 8; }
 
-// WAVES waves per workgroup, one 32-column block each: the workgroup's
-// WAVES * 32 channels are WAVES / 2 whole 128-byte lines of every token.
+// WAVES waves per workgroup, one 32-column block each: with an even WAVES
+// the workgroup's WAVES * 32 channels are WAVES / 2 whole 128-byte lines of
+// every bf16 token.
 // MODE kLinResidual adds a residual; kLinLayerNorm normalises every token
 // row of x (over its K channels) before the product.
 template <int KS, int MODE, int WAVES>
@@ -559,9 +560,16 @@ __global__ void linear_ln_consts_kernel(const uint16_t* w, const float* gamma, c
   }
 }
 
-// waves per workgroup for N / 32 column blocks: the widest whole-line
-// group that divides them (fewer re-reads of x), else 2
-int linear_waves(int ncb) { return ncb % 6 == 0 ? 6 : ncb % 4 == 0 ? 4 : 2; }
+// waves per workgroup for N / 32 column blocks: the widest group of 6, 4 or
+// 3 that divides them (fewer re-reads of x), else 2.  int8 layers take 9
+// before 4 and 3: a group then covers rows of 288 bytes whole (Swin-T stage
+// 1 QKV, 9 blocks: 15.4 us against 16.7 with 3 waves and 19.8 with 2; the
+// bf16 layer there: 16.5 us with 3 waves, 19.3 with 9, 17.8 with 2)
+int linear_waves(int ncb, bool i8) {
+  if (ncb % 6 == 0) return 6;
+  if (i8 && ncb % 9 == 0) return 9;
+  return ncb % 4 == 0 ? 4 : ncb % 3 == 0 ? 3 : 2;
+}
 
 size_t linear_lds_waves(int K, int waves) {
   return (size_t)kLinTiles * (K / 32) * 1024 + (size_t)kLinRows * lin_out_stride(waves) +
@@ -603,7 +611,11 @@ hipError_t launch_linear_krw(LinearParams p, int dev, int cus, hipStream_t st) {
 
 template <int KS, int MODE>
 hipError_t launch_linear_kr(const LinearParams& p, int dev, int cus, hipStream_t st) {
-  switch (linear_waves(p.ncb)) {
+  switch (linear_waves(p.ncb, MODE >= kLinI8)) {
+    case 9:
+      if constexpr (MODE >= kLinI8) return launch_linear_krw<KS, MODE, 9>(p, dev, cus, st);
+      return hipErrorInvalidValue;
+    case 3: return launch_linear_krw<KS, MODE, 3>(p, dev, cus, st);
     case 6: return launch_linear_krw<KS, MODE, 6>(p, dev, cus, st);
     case 4: return launch_linear_krw<KS, MODE, 4>(p, dev, cus, st);
     default: return launch_linear_krw<KS, MODE, 2>(p, dev, cus, st);
