@@ -81,6 +81,25 @@ def bwd_algorithmic(B, H, W, heads, head_dim, window, elem=2):
     return 7 * C * T * elem, 10 * N * C * T
 
 
+def bwd_kernel_name(B: int, H: int, W: int, heads: int, window: int, cus: int) -> str:
+    """Name of the backward kernel the library launches.  Mirrors its plan:
+    head pairs for windows of 4 tiles with an even head count, unless their
+    grid would leave CUs idle (runs of at least 8 windows per workgroup, two
+    8-wave pair workgroups per CU), else one head per workgroup."""
+    q = (window + 3) // 4
+    hp = 1
+    if q * q == 4 and heads % 2 == 0:
+        groups = heads // 2
+        windows = B * (H // window) * (W // window)
+        runs = min(2 * cus // groups, windows, windows // 8)
+        runs = max(runs, 1)
+        if runs >= 8:
+            runs -= runs % 8
+        if runs * groups >= cus:
+            hp = 2
+    return f"wattn_bwd_bf16_kernel<{window}, {hp}>"
+
+
 def fwd_kernel_name(window: int, heads: int, i8: bool = False) -> str:
     """Name of the bf16 (int8) forward kernel the library launches.  Mirrors
     its dispatch: head groups of 2, else 3, else 1 for windows of up to 4
@@ -635,7 +654,8 @@ def bwd_bench(args, torch, np) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload, "wattn_bwd_bf16"),
-                     "kernel": f"wattn_bwd_bf16_kernel<{M}, {2 if (M + 3) // 4 == 2 and nh % 2 == 0 else 1}>",
+                     "kernel": bwd_kernel_name(B, H, W, nh, M,
+                                               torch.cuda.get_device_properties(0).multi_processor_count),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "isolated_launch_us": round(isolated_s * 1e6, 3),
                      "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
