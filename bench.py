@@ -691,7 +691,7 @@ def i8_bench(args, torch, np) -> int:
 
     def step(i):
         k = i % sets
-        swa.check(swa.swin_wattn_fwd_i8(qs[k], sq, sk, sv, table, outs[k], B, H, W, nh, d, M, s,
+        swa.check(swa.swin_wattn_fwd_i8(qs[k], sq, sk, sv, 0.0, table, outs[k], B, H, W, nh, d, M, s,
                                         stream), "fwd_i8")
 
     K = args.steps

@@ -106,15 +106,22 @@ int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out
  *   scale_q, scale_k, scale_v   the three scales, host values.  scale_v must
  *             lie in (0, 2^100] and scale_q * scale_k / sqrt(head_dim) in
  *             [2^-100, 2^100], else SWIN_ERR_INVALID_ARG (NaN included).
- *   rel_bias_table, out   as swin_wattn_fwd (out bf16, must not overlap qkv).
+ *   out_scale 0: out is bf16, as swin_wattn_fwd.  > 0: out is int8 codes
+ *             [B][H][W][heads*head_dim], code = clamp(rne(o / out_scale),
+ *             -127, 127) (rne = round half to even) of the float32 output
+ *             o, for an INT8 output projection to read; scale_v / out_scale
+ *             must lie in [2^-100, 2^100].  Negative or NaN:
+ *             SWIN_ERR_INVALID_ARG.
+ *   rel_bias_table, out   as swin_wattn_fwd (out must not overlap qkv).
  * The scores are the exact integer sums of code products (float32 holds
  * them exactly) times scale_q * scale_k / sqrt(head_dim), plus bias and
  * mask; softmax and value product as in swin_wattn_fwd, with the value
- * codes taken exactly as bf16 and scale_v applied with the normaliser.
- * Shapes, errors and guarantees otherwise as swin_wattn_fwd. */
+ * codes taken exactly as bf16 and scale_v (scale_v / out_scale) applied
+ * with the normaliser.  Shapes, errors and guarantees otherwise as
+ * swin_wattn_fwd. */
 int swin_wattn_fwd_i8(const void* qkv, float scale_q, float scale_k, float scale_v,
-                      const float* rel_bias_table, void* out, int B, int H, int W, int heads,
-                      int head_dim, int window, int shift, void* stream);
+                      float out_scale, const float* rel_bias_table, void* out, int B, int H,
+                      int W, int heads, int head_dim, int window, int shift, void* stream);
 
 /* Backward of swin_wattn_fwd, for training (the NVIDIA talk, section 2,
  * fuses the window attention's backward too).  Given dout = dL/d(out), with

@@ -54,7 +54,7 @@ _lib.swin_wattn_precompute.argtypes = [_I, _I, _I, _I, _P]
 _lib.swin_wattn_fwd.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]
 _lib.swin_wattn_fwd_f32.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]
 _F = ctypes.c_float
-_lib.swin_wattn_fwd_i8.argtypes = [_P, _F, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]
+_lib.swin_wattn_fwd_i8.argtypes = [_P, _F, _F, _F, _F, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]
 _lib.swin_wattn_bwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]
 for _n in ("swin_wattn_copy_index", "swin_wattn_copy_mask", "swin_wattn_copy_region"):
     getattr(_lib, _n).argtypes = [_I, _I, _I, _I, _P, _P]
@@ -107,12 +107,12 @@ def swin_wattn_fwd_f32(qkv, rel_bias_table, out, B: int, H: int, W: int, heads: 
                                    head_dim, window, shift, _stream(stream))
 
 
-def swin_wattn_fwd_i8(qkv, scale_q: float, scale_k: float, scale_v: float, rel_bias_table, out,
-                      B: int, H: int, W: int, heads: int, head_dim: int, window: int, shift: int,
-                      stream=None) -> int:
-    return _lib.swin_wattn_fwd_i8(_addr(qkv), scale_q, scale_k, scale_v, _addr(rel_bias_table),
-                                  _addr(out), B, H, W, heads, head_dim, window, shift,
-                                  _stream(stream))
+def swin_wattn_fwd_i8(qkv, scale_q: float, scale_k: float, scale_v: float, out_scale: float,
+                      rel_bias_table, out, B: int, H: int, W: int, heads: int, head_dim: int,
+                      window: int, shift: int, stream=None) -> int:
+    return _lib.swin_wattn_fwd_i8(_addr(qkv), scale_q, scale_k, scale_v, out_scale,
+                                  _addr(rel_bias_table), _addr(out), B, H, W, heads, head_dim,
+                                  window, shift, _stream(stream))
 
 
 def swin_wattn_bwd(qkv, rel_bias_table, dout, dqkv, dtable, B: int, H: int, W: int, heads: int,

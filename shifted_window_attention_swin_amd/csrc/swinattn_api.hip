@@ -105,27 +105,30 @@ enum FwdKind { kFwdBf16, kFwdF32, kFwdI8 };
 // Scales of int8 codes: the score scale scale_q * scale_k / sqrt(head_dim)
 // must lie in [2^-100, 2^100] and scale_v in (0, 2^100], so that every
 // constant derived from them (the score scale, its inverse, the mask over
-// the score scale) is a normal fp32 number.
-bool i8_scales_ok(double sq, double sk, double sv, int head_dim) {
+// the score scale) is a normal fp32 number; an int8 output scale (so > 0)
+// must keep scale_v / so in [2^-100, 2^100].
+bool i8_scales_ok(double sq, double sk, double sv, double so, int head_dim) {
   if (!(sq > 0.0) || !(sk > 0.0) || !(sv > 0.0) || !(sv <= 0x1p100)) return false;
+  if (!(so >= 0.0)) return false;
+  if (so > 0.0 && !(sv / so >= 0x1p-100 && sv / so <= 0x1p100)) return false;
   const double sc = sq * sk / sqrt((double)head_dim);
   return sc >= 0x1p-100 && sc <= 0x1p100;
 }
 
 int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int W, int heads,
                int head_dim, int M, int s, void* stream, FwdKind kind, float sq = 1.f,
-               float sk = 1.f, float sv = 1.f) {
+               float sk = 1.f, float sv = 1.f, float so = 0.f) {
   if (!qkv || !table || !out) return SWIN_ERR_INVALID_ARG;
   if (!aligned(qkv, 16) || !aligned(out, 16) || !aligned(table, 4)) return SWIN_ERR_INVALID_ARG;
   if (B < 0 || H <= 0 || W <= 0 || heads <= 0 || head_dim <= 0 || M <= 0) return SWIN_ERR_INVALID_ARG;
   if (H % M != 0 || W % M != 0 || s < 0 || s >= M) return SWIN_ERR_INVALID_ARG;
-  if (kind == kFwdI8 && !i8_scales_ok(sq, sk, sv, head_dim)) return SWIN_ERR_INVALID_ARG;
+  if (kind == kFwdI8 && !i8_scales_ok(sq, sk, sv, so, head_dim)) return SWIN_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || M > kMaxWindow) return SWIN_ERR_UNSUPPORTED;
   // the fp32 kernel stages every head's bias table in LDS; the persistent
   // kernel stages one head group's when every head's would not fit
   if (kind == kFwdF32 && fwd_lds_bytes(M, heads) > (size_t)kMaxLds) return SWIN_ERR_UNSUPPORTED;
   const long long in_elem = kind == kFwdF32 ? 4 : kind == kFwdI8 ? 1 : 2;
-  const long long out_elem = kind == kFwdF32 ? 4 : 2;
+  const long long out_elem = kind == kFwdF32 ? 4 : (kind == kFwdI8 && so > 0.f) ? 1 : 2;
   const long long nW = (long long)(H / M) * (W / M);
   const long long C = (long long)heads * head_dim;
   const long long image_bytes = (long long)H * W * 3 * C * in_elem;
@@ -157,7 +160,8 @@ int fwd_common(const void* qkv, const float* table, void* out, int B, int H, int
   p.inv_scale = (float)(sd / sqk);
   p.mask_value = (float)(-100.0 * sd);
   mask_pieces(100.0 * sd / sqk, p.mask_pieces);
-  p.v_scale = kind == kFwdI8 ? sv : 1.f;
+  p.out_i8 = kind == kFwdI8 && so > 0.f ? 1 : 0;
+  p.v_scale = kind != kFwdI8 ? 1.f : p.out_i8 ? (float)((double)sv / (double)so) : sv;
   // bf16 and int8: the persistent LDS-staged kernel; fp32: the per-window kernel
   const int hg = head_group(heads, M);
   const bool persistent = kind != kFwdF32;
@@ -265,10 +269,10 @@ int swin_wattn_fwd(const void* qkv, const float* rel_bias_table, void* out, int 
 }
 
 int swin_wattn_fwd_i8(const void* qkv, float scale_q, float scale_k, float scale_v,
-                      const float* rel_bias_table, void* out, int B, int H, int W, int heads,
-                      int head_dim, int window, int shift, void* stream) {
+                      float out_scale, const float* rel_bias_table, void* out, int B, int H,
+                      int W, int heads, int head_dim, int window, int shift, void* stream) {
   return fwd_common(qkv, rel_bias_table, out, B, H, W, heads, head_dim, window, shift, stream,
-                    kFwdI8, scale_q, scale_k, scale_v);
+                    kFwdI8, scale_q, scale_k, scale_v, out_scale);
 }
 
 int swin_wattn_fwd_f32(const float* qkv, const float* rel_bias_table, float* out, int B, int H,

@@ -36,7 +36,9 @@ struct FwdParams {
   float inv_scale;          // 1 / scale: bias and mask are pre-divided by the scale
   float mask_value;         // -100 * sqrt(head_dim)
   float mask_pieces[3];     // bf16-exact parts summing to 100 * inv_scale in fp32
-  float v_scale;            // int8 forward: scale of the value codes
+  float v_scale;            // int8 forward: scale of the value codes (over the output scale
+                            // for int8 output)
+  int out_i8;               // int8 forward: int8 output codes instead of bf16
 };
 
 // Queues the precompute kernel.  rel_index [N*N], mask [nW*N*N],

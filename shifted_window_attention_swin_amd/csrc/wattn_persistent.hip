@@ -172,7 +172,7 @@ SWA_INLINE u32x4 widen_chunk(u32x2 v) {
 SWA_INLINE u32x4 widen_chunk(u32x4 v) { return v; }
 
 // The persistent forward.  I8: q, k and v arrive as int8 codes with one
-// scale per part.  A lane loads the 8 codes of its token part (8 bytes, in
+// scale per part, and the output is bf16, or int8 codes (out_i8).  A lane loads the 8 codes of its token part (8 bytes, in
 // place of 16 bytes of bf16) and writes them to LDS as bf16; from there the
 // math is the bf16 kernel's.  The score MFMA then sums 32 products of codes
 // (each at most 2^14 in magnitude) in fp32, which holds every such sum
@@ -478,6 +478,26 @@ __global__ __launch_bounds__(fwd_waves<M>() * 64, (fwd_minw<M, HG>())) void watt
       }
       if (ok) {
         const float inv = I8 ? fast_rcp(l4[0]) * p.v_scale : fast_rcp(l4[0]);
+        if constexpr (I8) {
+          if (p.out_i8) {
+            // int8 output: v_scale is the value scale over the output
+            // scale; the code is clamp(rne(o), -127, 127) (adding 1.5 * 2^23
+            // rounds half to even and leaves the code in the low byte), 8
+            // codes of the lane's 8 channels in one 8-byte store
+            u32x2 w = {0u, 0u};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float y0 = __builtin_amdgcn_fmed3f(o0[r] * inv, -127.f, 127.f) + 12582912.f;
+              const float y1 = __builtin_amdgcn_fmed3f(o1[r] * inv, -127.f, 127.f) + 12582912.f;
+              w[0] |= (__float_as_uint(y0) & 0xFFu) << (8 * r);
+              w[1] |= (__float_as_uint(y1) & 0xFFu) << (8 * r);
+            }
+            const unsigned pix = token_pixel(p, M, b, wy, wx, ty, tx, true);
+            __builtin_nontemporal_store(
+                w, reinterpret_cast<u32x2*>(out + pix * (Cb / 2) + h * kHeadDim + 8 * g));
+            continue;
+          }
+        }
         bf16x8 ov;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

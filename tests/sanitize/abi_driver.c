@@ -55,7 +55,7 @@ int main(void) {
   expect(swin_wattn_fwd(A, C, Bp, 0, 14, 14, 2, 32, 7, 3, NULL), SWIN_OK, "fwd B=0");
   expect(swin_wattn_fwd_f32(A, C, Bp, 2, 24, 24, 78, 32, 12, 0, NULL), U, "fwd fp32 tables");
   expect(swin_wattn_fwd_f32(NULL, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I, "fwd fp32 null");
-  expect(swin_wattn_fwd_i8(NULL, 0.03f, 0.03f, 0.03f, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I,
+  expect(swin_wattn_fwd_i8(NULL, 0.03f, 0.03f, 0.03f, 0.f, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I,
          "fwd int8 null");
   expect(swin_linear_i8_fwd(A, 0.03f, Bp, NULL, NULL, NULL, NULL, C, 64, 192, 576, NULL), I,
          "linear int8 no weight scales");
@@ -64,15 +64,15 @@ int main(void) {
   expect(swin_linear_i8_fwd(A, 0.03f, Bp, (const float*)C, NULL, NULL, NULL, Bp, 64, 800, 576,
                             NULL), U, "linear int8 K");
   expect(swin_linear_i8_pack_weight(A, A, 576, 192, NULL), I, "linear int8 pack overlap");
-  expect(swin_wattn_fwd_i8(A, 0.03f, 0.03f, 0.03f, C, A, 2, 14, 14, 2, 32, 7, 3, NULL), I,
+  expect(swin_wattn_fwd_i8(A, 0.03f, 0.03f, 0.03f, 0.f, C, A, 2, 14, 14, 2, 32, 7, 3, NULL), I,
          "fwd int8 overlap");
-  expect(swin_wattn_fwd_i8(A, 0.0f, 0.03f, 0.03f, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I,
+  expect(swin_wattn_fwd_i8(A, 0.0f, 0.03f, 0.03f, 0.f, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I,
          "fwd int8 zero scale");
-  expect(swin_wattn_fwd_i8(A, 1e-20f, 1e-20f, 1.f, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I,
+  expect(swin_wattn_fwd_i8(A, 1e-20f, 1e-20f, 1.f, 0.f, C, Bp, 2, 14, 14, 2, 32, 7, 3, NULL), I,
          "fwd int8 score scale");
-  expect(swin_wattn_fwd_i8(A, 0.03f, 0.03f, 0.03f, C, Bp, 2, 14, 14, 2, 64, 7, 3, NULL), U,
+  expect(swin_wattn_fwd_i8(A, 0.03f, 0.03f, 0.03f, 0.f, C, Bp, 2, 14, 14, 2, 64, 7, 3, NULL), U,
          "fwd int8 head_dim");
-  expect(swin_wattn_fwd_i8(A, 0.03f, 0.03f, 0.03f, C, Bp, 0, 14, 14, 2, 32, 7, 3, NULL), SWIN_OK,
+  expect(swin_wattn_fwd_i8(A, 0.03f, 0.03f, 0.03f, 0.f, C, Bp, 0, 14, 14, 2, 32, 7, 3, NULL), SWIN_OK,
          "fwd int8 B=0");
   /* backward */
   expect(swin_wattn_bwd(A, C, D, NULL, E, 2, 14, 14, 2, 32, 7, 3, NULL), I, "bwd null dqkv");

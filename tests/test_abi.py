@@ -47,7 +47,7 @@ GOOD = dict(B=2, H=14, W=14, heads=2, head_dim=32, window=7, shift=3)
 
 def _fwd_i8(qkv, table, out, *rest):
     """swin_wattn_fwd_i8 with valid scales, in the argument order of swin_wattn_fwd."""
-    return swa.swin_wattn_fwd_i8(qkv, 0.03, 0.03, 0.03, table, out, *rest)
+    return swa.swin_wattn_fwd_i8(qkv, 0.03, 0.03, 0.03, 0.0, table, out, *rest)
 
 
 FWDS = [swa.swin_wattn_fwd, swa.swin_wattn_fwd_f32, _fwd_i8]
@@ -108,20 +108,24 @@ def test_empty_batch_is_a_no_op(fn):
 def test_fwd_i8_rejects_scales_out_of_range():
     E = swa.SWIN_ERR_INVALID_ARG
 
-    def call(sq, sk, sv):
-        return swa.swin_wattn_fwd_i8(A16, sq, sk, sv, A32, A48, 2, 14, 14, 2, 32, 7, 3, 0)
+    def call(sq, sk, sv, so=0.0):
+        return swa.swin_wattn_fwd_i8(A16, sq, sk, sv, so, A32, A48, 2, 14, 14, 2, 32, 7, 3, 0)
 
     nan, inf = float("nan"), float("inf")
     for bad in [(0.0, 0.03, 0.03), (0.03, -0.03, 0.03), (0.03, 0.03, 0.0), (nan, 0.03, 0.03),
                 (0.03, nan, 0.03), (0.03, 0.03, nan), (inf, 0.03, 0.03), (0.03, 0.03, inf),
                 (1e-20, 1e-20, 1.0),     # score scale below 2^-100
                 (1e20, 1e20, 1.0),       # score scale above 2^100
-                (1.0, 1.0, 2.0 ** 101)]:
+                (1.0, 1.0, 2.0 ** 101),
+                (0.03, 0.03, 0.03, -1.0),      # negative output scale
+                (0.03, 0.03, 0.03, nan),
+                (0.03, 0.03, 1e20, 1e-20)]:    # scale_v / out_scale above 2^100
         assert call(*bad) == E, bad
     # near the range's ends: accepted (B = 0: nothing is queued)
     lo, hi = 2.0 ** -48, 2.0 ** 50
-    assert swa.swin_wattn_fwd_i8(A16, lo, lo, 2.0 ** 100, A32, A48, 0, 14, 14, 2, 32, 7, 3, 0) == 0
-    assert swa.swin_wattn_fwd_i8(A16, hi, hi, 1.0, A32, A48, 0, 14, 14, 2, 32, 7, 3, 0) == 0
+    assert swa.swin_wattn_fwd_i8(A16, lo, lo, 2.0 ** 100, 0.0, A32, A48, 0, 14, 14, 2, 32, 7, 3, 0) == 0
+    assert swa.swin_wattn_fwd_i8(A16, hi, hi, 1.0, 0.0, A32, A48, 0, 14, 14, 2, 32, 7, 3, 0) == 0
+    assert swa.swin_wattn_fwd_i8(A16, 0.03, 0.03, 0.03, 0.01, A32, A48, 0, 14, 14, 2, 32, 7, 3, 0) == 0
 
 
 def test_precompute_and_copies_reject_invalid_shapes():

@@ -29,13 +29,17 @@ def _dev():
     return torch.device("cuda:0")
 
 
-def _run_i8(codes, scales, table, M, s, codes_dev=None):
+def _run_i8(codes, scales, table, M, s, codes_dev=None, out_scale=0.0):
     B, H, W, _, nh, d = codes.shape
     q = codes_dev if codes_dev is not None else torch.from_numpy(np.ascontiguousarray(codes)).to(_dev())
     t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.float32)).to(_dev())
-    out = torch.full((B, H, W, nh * d), float("nan"), dtype=torch.bfloat16, device=_dev())
+    if out_scale > 0:  # -128 is no code: any left is a position never written
+        out = torch.full((B, H, W, nh * d), -128, dtype=torch.int8, device=_dev())
+    else:
+        out = torch.full((B, H, W, nh * d), float("nan"), dtype=torch.bfloat16, device=_dev())
     sq, sk, sv = (float(x) for x in scales)
-    swa.check(swa.swin_wattn_fwd_i8(q, sq, sk, sv, t, out, B, H, W, nh, d, M, s), "fwd_i8")
+    swa.check(swa.swin_wattn_fwd_i8(q, sq, sk, sv, float(out_scale), t, out, B, H, W, nh, d, M, s),
+              "fwd_i8")
     torch.cuda.synchronize()
     return out
 
@@ -188,3 +192,85 @@ def test_i8_batch_split_over_2gib():
             k += 1
     del q, out
     torch.cuda.empty_cache()
+
+
+def _check_out_codes(got, o64, so, what, min_equal=0.97):
+    # int8 output: the code rounds the fp32 output, whose error against the
+    # fp64 value is the bf16 path's (weights rounded to bf16) without the
+    # output rounding.  Every code must be within 1 of the fp64 value's
+    # code (round half to even, clamped), nearly all equal to it, and codes
+    # far beyond the range saturate
+    exact = np.clip(np.rint(o64 / so), -127, 127)
+    d = np.abs(got.astype(np.float64) - exact)
+    eq = float(np.mean(d == 0))
+    print(f"    {what}: max code diff {d.max():.0f}, equal {eq:.4f}, saturated "
+          f"{np.mean(np.abs(exact) == 127):.4f}", flush=True)
+    assert d.max() <= 1 and eq >= min_equal, what
+    far = np.abs(o64 / so) > 128
+    assert np.array_equal(got[far], 127 * np.sign(o64[far])), what
+
+
+@pytest.mark.parametrize("B,H,W,nh,M,s", [(4, 56, 56, 6, 7, 3), (2, 24, 24, 3, 12, 6), (2, 14, 14, 7, 7, 3)])
+def test_i8_int8_output(B, H, W, nh, M, s):
+    _say(f"i8 int8 output B={B} H={H} W={W} nh={nh} M={M} s={s}")
+    codes, scales, table = synth.make_i8_inputs(B, H, W, nh, 32, M, seed=660 + M + nh)
+    o64 = oracle.swin_wattn_fwd_i8(codes, scales, table, M, s)
+    so = float(np.float32(np.abs(o64).max() / 127.0))
+    out = _run_i8(codes, scales, table, M, s, out_scale=so)
+    got = out.cpu().numpy()
+    assert (got != -128).all(), "some output position was never written"
+    _check_out_codes(got, o64, so, "codes")
+
+
+def test_i8_int8_output_saturates():
+    _say("i8 int8 output saturation")
+    codes, scales, table = synth.make_i8_inputs(2, 14, 14, 6, 32, 7, seed=671)
+    o64 = oracle.swin_wattn_fwd_i8(codes, scales, table, 7, 3)
+    so = float(np.float32(np.quantile(np.abs(o64), 0.7) / 127.0))  # about 30% beyond +-127
+    got = _run_i8(codes, scales, table, 7, 3, out_scale=so).cpu().numpy()
+    _check_out_codes(got, o64, so, "saturating codes", min_equal=0.9)
+    assert np.mean(np.abs(got) == 127) > 0.1 and got.min() >= -127
+
+
+def test_int8_block_chain():
+    # QKV projection (INT8 out) -> attention (INT8 in, INT8 out) -> output
+    # projection (INT8 in, bf16 out, + bias + residual): each stage against
+    # the oracle on the codes the previous GPU stage wrote
+    spec = synth.LINEAR_I8_WORKLOADS["qkv-l-s1-i8"]
+    a = synth.WORKLOADS["swin-l-s1"]
+    B = 2
+    H, W, nh, M, s = a["H"], a["W"], a["heads"], a["window"], a["shifts"][0]
+    C = nh * 32
+    T = B * H * W
+    _say(f"INT8 block chain, Swin-L stage 1 shape, B={B}")
+    x, sx, w, sw, bias, _, so = synth.linear_i8_inputs("qkv-l-s1-i8", tokens=T)
+    dev = _dev()
+    f32 = lambda v: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev)
+    packed = torch.zeros(3 * C * ((C + 63) // 64) * 64, dtype=torch.int8, device=dev)
+    swa.check(swa.swin_linear_i8_pack_weight(torch.from_numpy(w).to(dev), packed, 3 * C, C), "pack")
+    qkv = torch.full((T, 3 * C), -128, dtype=torch.int8, device=dev)
+    swa.check(swa.swin_linear_i8_fwd(torch.from_numpy(x).to(dev), float(sx), packed, f32(sw), f32(bias),
+                                     None, f32(so), qkv, T, C, 3 * C), "qkv")
+    scales = np.array([so[0], so[C], so[2 * C]], dtype=np.float32)
+    table = synth.attention_table(a["seed"], nh, M)
+    qkv_codes = qkv.cpu().numpy()
+    _, _, ref_qkv = oracle.linear_i8(x, sx, w, sw, bias, so=so)
+    assert np.array_equal(qkv_codes, ref_qkv)
+    o64 = oracle.swin_wattn_fwd_i8(qkv_codes.reshape(B, H, W, 3, nh, 32), scales, table, M, s)
+    so_attn = float(np.float32(np.abs(o64).max() / 127.0))
+    att = _run_i8(qkv_codes.reshape(B, H, W, 3, nh, 32), scales, table, M, s, codes_dev=qkv,
+                  out_scale=so_attn)
+    att_codes = att.cpu().numpy()
+    _check_out_codes(att_codes, o64, so_attn, "attention codes")
+    # the output projection on the attention's codes
+    _, _, w2, sw2, b2, res, _ = synth.make_linear_i8_inputs(T, C, C, 2103, True, False)
+    packed2 = torch.zeros(C * ((C + 63) // 64) * 64, dtype=torch.int8, device=dev)
+    swa.check(swa.swin_linear_i8_pack_weight(torch.from_numpy(w2).to(dev), packed2, C, C), "pack2")
+    y = torch.from_numpy(res.view(np.int16)).view(torch.bfloat16).to(dev).clone()
+    swa.check(swa.swin_linear_i8_fwd(att.view(T, C), so_attn, packed2, f32(sw2), f32(b2), y, None, y,
+                                     T, C, C), "proj")
+    torch.cuda.synchronize()
+    _, ref, _ = oracle.linear_i8(att_codes.reshape(T, C), so_attn, w2, sw2, b2, residual=res)
+    got = y.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    assert (err <= 2.0 ** -7 * np.abs(ref) + 1e-3).all(), float(err.max())

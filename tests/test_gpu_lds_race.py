@@ -187,3 +187,59 @@ def test_ln_attn_independent_of_stale_lds():
     print(f"    max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
 
+
+
+@pytest.mark.parametrize("B,H,W,nh,M,s", [
+    (4, 56, 56, 6, 7, 3),    # two-head units
+    (2, 96, 96, 6, 12, 6),   # window 12, one head's bias
+])
+def test_forward_i8_independent_of_stale_lds(B, H, W, nh, M, s):
+    _say(f"lds race fwd i8 B={B} H={H} W={W} nh={nh} M={M} s={s}")
+    codes, scales, table = synth.make_i8_inputs(B, H, W, nh, 32, M, seed=950 + M + nh)
+    q = torch.from_numpy(codes).to(_dev())
+    t = torch.from_numpy(table).to(_dev())
+    out = torch.empty(B, H, W, nh * 32, dtype=torch.bfloat16, device=_dev())
+
+    def run():
+        out.fill_(float("nan"))
+        swa.check(swa.swin_wattn_fwd_i8(q, *(float(v) for v in scales), 0.0, t, out, B, H, W, nh, 32,
+                                        M, s), "fwd_i8")
+        return [out]
+
+    (a,), (c,) = _twice(run)
+    assert torch.equal(a, c), "INT8 forward output depends on the LDS contents before the launch"
+    err = np.abs(a.float().cpu().numpy().astype(np.float64)
+                 - oracle.swin_wattn_fwd_i8(codes, scales, table, M, s))
+    print(f"    max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+@pytest.mark.parametrize("K,N,mode", [(192, 576, "i8"), (96, 288, "i8"), (192, 192, "res")])
+def test_linear_i8_independent_of_stale_lds(K, N, mode):
+    T = 3 * 1024 + 40
+    _say(f"lds race linear i8 T={T} K={K} N={N} mode={mode}")
+    x, sx, w, sw, bias, res, so = synth.make_linear_i8_inputs(T, K, N, 980 + K, mode == "res",
+                                                              mode == "i8")
+    f32 = lambda a: None if a is None else torch.from_numpy(a).to(_dev())
+    xd, wd, swd, bd, sod = torch.from_numpy(x).to(_dev()), torch.from_numpy(w).to(_dev()), f32(sw), \
+        f32(bias), f32(so)
+    rd = _bf16_dev(res) if res is not None else None
+    packed = torch.zeros(N * ((K + 63) // 64) * 64, dtype=torch.int8, device=_dev())
+    swa.check(swa.swin_linear_i8_pack_weight(wd, packed, N, K), "pack_i8")
+    y = torch.empty(T, N, dtype=torch.int8 if mode == "i8" else torch.bfloat16, device=_dev())
+
+    def run():
+        y.fill_(-128 if mode == "i8" else float("nan"))
+        swa.check(swa.swin_linear_i8_fwd(xd, float(sx), packed, swd, bd, rd, sod, y, T, K, N),
+                  "linear_i8")
+        return [y]
+
+    (a,), (c,) = _twice(run)
+    assert torch.equal(a, c), "INT8 linear output depends on the LDS contents before the launch"
+    _, ref, codes = oracle.linear_i8(x, sx, w, sw, bias, residual=res, so=so)
+    if mode == "i8":
+        assert np.array_equal(a.cpu().numpy(), codes)
+    else:
+        got = a.float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        assert (err <= 2.0**-7 * np.abs(ref) + 2.0**-7 * (np.abs(ref) + 1.0)).all()

@@ -179,7 +179,7 @@ def test_qkv_i8_then_attention_i8():
     assert np.array_equal(so, np.repeat(scales, C))
     table = synth.attention_table(a["seed"], nh, M)
     out = torch.full((B, a["H"], a["W"], C), float("nan"), dtype=torch.bfloat16, device=_dev())
-    swa.check(swa.swin_wattn_fwd_i8(qkv, *(float(v) for v in scales), _f32_dev(table), out, B, a["H"],
+    swa.check(swa.swin_wattn_fwd_i8(qkv, *(float(v) for v in scales), 0.0, _f32_dev(table), out, B, a["H"],
                                     a["W"], nh, 32, M, s), "attention")
     torch.cuda.synchronize()
     _, _, codes = oracle.linear_i8(x, sx, w, sw, bias, so=so)
