@@ -243,10 +243,10 @@ def linear_kernel_name(K: int, N: int, residual: bool, layernorm: bool = False) 
 
 def linear_i8_kernel_name(K: int, N: int, residual: bool, out_i8: bool) -> str:
     """The INT8 linear kernel the library launches: k-steps of 64 channels,
-    mode 3 bf16 output, 4 bf16 output + residual, 5 INT8 output; 6, 9, 4, 3 or
+    mode 3 bf16 output, 4 bf16 output + residual, 5 INT8 output; 9, 6, 4, 3 or
     2 waves, the first that divides N / 32)."""
     ncb = N // 32
-    waves = (6 if ncb % 6 == 0 else 9 if ncb % 9 == 0 else 4 if ncb % 4 == 0 else
+    waves = (9 if ncb % 9 == 0 else 6 if ncb % 6 == 0 else 4 if ncb % 4 == 0 else
              3 if ncb % 3 == 0 else 2)
     mode = 5 if out_i8 else 4 if residual else 3
     return f"linear_fwd_kernel<{(K + 63) // 64}, {mode}, {waves}>"

@@ -562,12 +562,13 @@ __global__ void linear_ln_consts_kernel(const uint16_t* w, const float* gamma, c
 
 // waves per workgroup for N / 32 column blocks: the widest group of 6, 4 or
 // 3 that divides them (fewer re-reads of x), else 2.  int8 layers take 9
-// before 4 and 3: a group then covers rows of 288 bytes whole (Swin-T stage
-// 1 QKV, 9 blocks: 15.4 us against 16.7 with 3 waves and 19.8 with 2; the
-// bf16 layer there: 16.5 us with 3 waves, 19.3 with 9, 17.8 with 2)
+// first: a group then covers 288-byte spans of a row (Swin-T stage 1 QKV,
+// 9 blocks: 15.4 us against 16.7 with 3 waves and 19.8 with 2; Swin-L stage
+// 1 QKV, 18 blocks: 44.9-45.4 against 47.0-47.6 us with 6 waves; the bf16
+// Swin-T QKV: 16.5 us with 3 waves, 19.3 with 9, 17.8 with 2)
 int linear_waves(int ncb, bool i8) {
-  if (ncb % 6 == 0) return 6;
   if (i8 && ncb % 9 == 0) return 9;
+  if (ncb % 6 == 0) return 6;
   return ncb % 4 == 0 ? 4 : ncb % 3 == 0 ? 3 : 2;
 }
 
