@@ -343,7 +343,7 @@ __global__ __launch_bounds__(WAVES * 64) void linear_fwd_kernel(LinearParams p) 
     // bf16 layers without a residual issue the next row block's loads
     // before the barrier, while the other waves still write (Swin-L stage 1
     // QKV 65.7 -> 64.8 us, with the layer norm 77.5 -> 76.3 us; the int8
-    // QKV was 1.6% slower so)
+    // QKV was 1.6% slower that way)
     if (kEarly && r + step < r_end) issue(R, r + step);
     __syncthreads();  // row block visible to every wave
     const int tok0 = r * kLinRows;

@@ -173,9 +173,10 @@ SWA_INLINE u32x4 widen_chunk(u32x2 v) {
 SWA_INLINE u32x4 widen_chunk(u32x4 v) { return v; }
 
 // The persistent forward.  I8: q, k and v arrive as int8 codes with one
-// scale per part, and the output is bf16, or int8 codes (out_i8).  A lane loads the 8 codes of its token part (8 bytes, in
-// place of 16 bytes of bf16) and writes them to LDS as bf16; from there the
-// math is the bf16 kernel's.  The score MFMA then sums 32 products of codes
+// scale per part, and the output is bf16, or int8 codes (out_i8).  A lane
+// loads the 8 codes of its token part (8 bytes, in place of 16 bytes of
+// bf16) and writes them to LDS as bf16; from there the math is the bf16
+// kernel's.  The score MFMA then sums 32 products of codes
 // (each at most 2^14 in magnitude) in fp32, which holds every such sum
 // exactly: it is the int32 accumulation of an int8 product.  The host folds
 // the query and key scales into the score scale (and so into the bias and
