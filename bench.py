@@ -753,7 +753,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the forward shards by batch with no "
+        print("bench.py: measures one GPU only; the forward shards by batch with no "
               "communication, so there is no multi-GPU run to make (--gpus must be 1)", file=sys.stderr)
         return 2
 

@@ -24,8 +24,10 @@
  *  - Baidu AIAK-Training talk (jxzklqfsx.com article 743345), section 2,
  *    WindowAttention fusion case: two matrix products and a softmax.
  * The formula figure of the WindowAttention case did not survive extraction;
- * the oracle takes softmax(Q K^T / sqrt(d) + bias + mask) V, and every other
- * reading where the pages are silent is listed in the design doc.
+ * the oracle takes softmax(Q K^T / sqrt(d) + bias + mask) V.  Where the
+ * pages are silent (shift direction, mask value -100, relative index as
+ * query minus key, scale 1/sqrt(d)) it takes the plainest reading that the
+ * rest of the pages supports, stated at each function below.
  *
  * Conventions (all arrays dense, row-major, no padding):
  *   image tensors  [B][H][W][Cx]

@@ -55,7 +55,7 @@ def test_c_abi_host_code_under_address_and_undefined_sanitizers(tmp_path):
     cmd = swa_build.command(str(lib), extra=host_san)
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
     assert res.returncode == 0, res.stderr[-3000:]
-    # the driver is built by the same clang, whose sanitizer runtime the
+    # the ABI test program is built by the same clang, whose sanitizer runtime the
     # library's instrumentation expects (it is linked into the executable)
     clang = os.path.join(os.path.dirname(os.path.realpath(hipcc)), "..", "llvm", "bin", "clang")
     if not os.path.exists(clang):
