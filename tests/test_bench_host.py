@@ -131,3 +131,21 @@ def test_more_than_one_gpu_exits_with_a_message(argv, env):
     assert res.returncode == 2
     assert "one GPU only" in res.stderr
     assert res.stdout == ""
+
+
+def test_reported_kernel_names_match_the_traces():
+    # each committed rocprofv3 summary names, in its title, the kernel that
+    # bench.py reported for the run, and lists the kernels the trace saw:
+    # the mirrors of the dispatch rules must name a kernel that really ran
+    import glob
+    import re
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+    assert len(paths) >= 10
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        reported = re.search(r"rocprofv3 summary: (.+?), (backward of )?workload", text).group(1)
+        traced = [re.sub(r"^void |swinattn::\(anonymous namespace\)::|\(swinattn::\w+\)$", "", n)
+                  for n in re.findall(r"\| `([^`]+)` \|", text)]
+        traced = [n.replace("swinattn::(anonymous namespace)::", "") for n in traced]
+        assert reported in traced, (os.path.basename(path), reported, traced)
