@@ -1,6 +1,6 @@
 """Seeded sweep of random shapes: the bf16 forward, the INT8 forward, the
-backward and the linear layers (bf16 and INT8) against the fp64 oracle, at
-shapes drawn from a fixed seed.
+backward, the linear layers (bf16 and INT8) and the fused layer norm + QKV
++ attention against the fp64 oracle, at shapes drawn from a fixed seed.
 
 The draws cover windows 1-12, 1-16 heads, every shift, 1-3 images and
 1-3 windows per axis (H != W included), so the launch plans of the
@@ -148,3 +148,36 @@ def test_sweep_linear_i8(T, K, N, mode):
         mag = (np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T) * (float(sx) * sw) + np.abs(b) \
             + np.abs(synth.bf16_to_f32(r))
         assert (np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 2.0 ** -20 * mag).all()
+
+
+def _ln_attn_shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(5, 9))
+        s = int(rng.integers(0, M))
+        nh = int(rng.integers(1, 7))  # C = 32 .. 192
+        B = int(rng.integers(1, 3))
+        H, W = M * int(rng.integers(1, 4)), M * int(rng.integers(1, 4))
+        out.append((B, H, W, nh, M, s))
+    return out
+
+
+@pytest.mark.parametrize("B,H,W,nh,M,s", _ln_attn_shapes(2029, 24))
+def test_sweep_ln_attn(B, H, W, nh, M, s):
+    print(f"[case] sweep ln_qkv_wattn B={B} H={H} W={W} nh={nh} M={M} s={s}", flush=True)
+    x, g, be, w, b, t = synth.make_ln_attn_inputs(B, H, W, nh, M, seed=9000 + B * 97 + H * 13 + nh)
+    C = nh * 32
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(_dev())
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(_dev())
+    wd = bf(w)
+    packed = torch.empty_like(wd)
+    consts = torch.empty(2, 3 * C, dtype=torch.float32, device=_dev())
+    swa.check(swa.swin_ln_linear_pack_weight(wd, f32(g), f32(be), f32(b), packed, consts, 3 * C, C),
+              "pack")
+    out = torch.full((B, H, W, C), float("nan"), dtype=torch.bfloat16, device=_dev())
+    swa.check(swa.swin_ln_qkv_wattn_fwd(bf(x), packed, consts, 1e-5, f32(t), out, B, H, W, nh, 32, M, s),
+              "ln_qkv_wattn")
+    torch.cuda.synchronize()
+    qkv = oracle.linear(oracle.layernorm(x, g, be, 1e-5), w, b).reshape(B, H, W, 3, nh, 32)
+    _check(out.float().cpu().numpy().astype(np.float64), oracle.swin_wattn_fwd(qkv, t, M, s), "ln_attn")
