@@ -1,6 +1,7 @@
-"""Seeded sweep of random shapes: the bf16 forward, the INT8 forward, the
-backward, the linear layers (bf16 and INT8) and the fused layer norm + QKV
-+ attention against the fp64 oracle, at shapes drawn from a fixed seed.
+"""Seeded sweep of random shapes: the bf16 forward, the INT8 forward (bf16
+and int8 output), the backward, the linear layers (bf16 and INT8) and the
+fused layer norm + QKV + attention against the fp64 oracle, at shapes drawn
+from a fixed seed.
 
 The draws cover windows 1-12, 1-16 heads, every shift, 1-3 images and
 1-3 windows per axis (H != W included), so the launch plans of the
@@ -148,6 +149,27 @@ def test_sweep_linear_i8(T, K, N, mode):
         mag = (np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T) * (float(sx) * sw) + np.abs(b) \
             + np.abs(synth.bf16_to_f32(r))
         assert (np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 2.0 ** -20 * mag).all()
+
+
+@pytest.mark.parametrize("B,H,W,nh,M,s", _shapes(2030, 24))
+def test_sweep_i8_forward_int8_out(B, H, W, nh, M, s):
+    # int8 output codes (out_scale = max |o| / 127): each code within 1 of
+    # the fp64 output's code (round half to even, clamped to +-127), nearly
+    # all equal to it, never -128 (the fill value: a position never written)
+    print(f"[case] sweep i8 fwd int8 out B={B} H={H} W={W} nh={nh} M={M} s={s}", flush=True)
+    codes, scales, table = synth.make_i8_inputs(B, H, W, nh, 32, M, seed=5500 + B * 97 + H * 13 + nh)
+    o64 = oracle.swin_wattn_fwd_i8(codes, scales, table, M, s)
+    so = float(np.float32(np.abs(o64).max() / 127.0))
+    out = torch.full((B, H, W, nh * 32), -128, dtype=torch.int8, device=_dev())
+    swa.check(swa.swin_wattn_fwd_i8(torch.from_numpy(codes).to(_dev()), *(float(v) for v in scales), so,
+                                    torch.from_numpy(table).to(_dev()), out, B, H, W, nh, 32, M, s),
+              "fwd_i8 int8 out")
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    exact = np.clip(np.rint(o64 / so), -127, 127)
+    d = np.abs(got - exact)
+    print(f"    codes: max diff {d.max():.0f}, equal {np.mean(d == 0):.4f}", flush=True)
+    assert got.min() >= -127 and d.max() <= 1 and np.mean(d == 0) >= 0.97
 
 
 def _ln_attn_shapes(seed, n):
