@@ -125,52 +125,78 @@ def measured_traffic(workload: str, family: str = "wattn_fwd_bf16"):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50):
+def cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50,
+                 gpu_out=None):
     """The fp64 oracle on the first `sample_batch` images of the workload, on
     every host core, repeated until about `min_seconds` of wall time; reported
-    in the metric's unit (GB/s of algorithmic bytes)."""
+    in the metric's unit (GB/s of algorithmic bytes).  With `gpu_out` (the
+    library's output for the same images and the workload's first shift, as
+    float64) the oracle's output is also compared with it, element by
+    element, against the bf16 bars (max-abs 2e-2, mean-abs 2e-3)."""
     import oracle
     import synth
     w = synth.WORKLOADS[name]
     qkv, table = synth.workload_inputs(name, batch=sample_batch)
-    reps, used = 0, 0
+    reps, used, ref = 0, 0, None
     t0 = time.perf_counter()
     while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
-        _, used = oracle.swin_wattn_fwd(qkv, table, w["window"], w["shifts"][0], return_threads=True)
+        ref, used = oracle.swin_wattn_fwd(qkv, table, w["window"], w["shifts"][0], return_threads=True)
         reps += 1
     dt = time.perf_counter() - t0
     nbytes, _ = algorithmic(sample_batch, w["H"], w["W"], w["heads"], w["head_dim"], w["window"])
-    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle",
-            "sample": f"{name}, first {sample_batch} of {w['B']} images, whole forward x{reps} "
-                      f"({dt:.1f} s wall, fp64, {used} threads)"}
+    res = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+           "kind": "oracle",
+           "sample": f"{name}, first {sample_batch} of {w['B']} images, whole forward x{reps} "
+                     f"({dt:.1f} s wall, fp64, {used} threads)"}
+    if gpu_out is not None:
+        res["parity"] = _parity(gpu_out, ref)
+    return res
 
 
-def i8_cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50):
+def _parity(got, ref):
+    """Element-by-element comparison of the library's bf16 forward output with
+    the oracle's, against the bf16 bars (max-abs 2e-2, mean-abs 2e-3)."""
+    err = abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    return {"max_abs": mx, "mean_abs": mean, "bar_max_abs": 2e-2, "bar_mean_abs": 2e-3,
+            "elements": int(err.size), "ok": bool(mx <= 2e-2 and mean <= 2e-3)}
+
+
+def i8_cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50,
+                    gpu_out=None):
     """The fp64 oracle (dequantize, then the forward) on the first
-    `sample_batch` images of an INT8 workload, as cpu_baseline does."""
+    `sample_batch` images of an INT8 workload, as cpu_baseline does (with
+    `gpu_out`, the same comparison and bars)."""
     import oracle
     import synth
     a = synth.WORKLOADS[synth.I8_WORKLOADS[name]["attn"]]
     codes, scales, table = synth.i8_inputs(name, batch=sample_batch)
-    reps, used = 0, 0
+    reps, used, ref = 0, 0, None
     t0 = time.perf_counter()
     while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
-        _, used = oracle.swin_wattn_fwd_i8(codes, scales, table, a["window"], a["shifts"][0],
-                                           return_threads=True)
+        ref, used = oracle.swin_wattn_fwd_i8(codes, scales, table, a["window"], a["shifts"][0],
+                                             return_threads=True)
         reps += 1
     dt = time.perf_counter() - t0
     nbytes, _ = algorithmic(sample_batch, a["H"], a["W"], a["heads"], a["head_dim"], a["window"],
                             elem=1, out_elem=2)
-    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle",
-            "sample": f"{name}, first {sample_batch} of {a['B']} images, whole forward x{reps} "
-                      f"({dt:.1f} s wall, fp64, {used} threads)"}
+    res = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+           "kind": "oracle",
+           "sample": f"{name}, first {sample_batch} of {a['B']} images, whole forward x{reps} "
+                     f"({dt:.1f} s wall, fp64, {used} threads)"}
+    if gpu_out is not None:
+        res["parity"] = _parity(gpu_out, ref)
+    return res
 
 
-def bwd_cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50):
+def bwd_cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, max_reps: int = 50,
+                     gpu_dqkv=None):
     """The fp64 oracle backward on the first `sample_batch` images, as
-    cpu_baseline does for the forward."""
+    cpu_baseline does for the forward.  With `gpu_dqkv` (the library's dq,
+    dk, dv of the same images, float64) they are compared element by element
+    against the backward's bars, per part: max error <= 2^-6 max |ref| and
+    mean error <= 2^-8 mean |ref| (the table gradient sums over the whole
+    batch and is not compared on a sample)."""
     import oracle
     import synth
     w = synth.WORKLOADS[name]
@@ -179,18 +205,30 @@ def bwd_cpu_baseline(name: str, sample_batch: int, min_seconds: float = 10.0, ma
     n = sample_batch * w["H"] * w["W"] * C
     dout = synth.bf16_bits(synth.normal(synth.stream_key(w["seed"], 7), n, 1.0))
     dout = dout.reshape(sample_batch, w["H"], w["W"], C)
-    reps, cores = 0, 0
+    reps, cores, ref = 0, 0, None
     t0 = time.perf_counter()
     while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
-        _, _, cores = oracle.swin_wattn_bwd(qkv, table, dout, w["window"], w["shifts"][0],
-                                            return_threads=True)
+        ref, _, cores = oracle.swin_wattn_bwd(qkv, table, dout, w["window"], w["shifts"][0],
+                                              return_threads=True)
         reps += 1
     dt = time.perf_counter() - t0
     nbytes, _ = bwd_algorithmic(sample_batch, w["H"], w["W"], w["heads"], w["head_dim"], w["window"])
-    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{name}, first {sample_batch} of {w['B']} images, whole backward x{reps} "
-                      f"({dt:.1f} s wall, fp64, {cores} threads)"}
+    res = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"{name}, first {sample_batch} of {w['B']} images, whole backward x{reps} "
+                     f"({dt:.1f} s wall, fp64, {cores} threads)"}
+    if gpu_dqkv is not None:
+        err = abs(gpu_dqkv - ref)
+        worst_max = worst_mean = 0.0
+        for part in range(3):  # dq, dk, dv
+            e, r = err[:, :, :, part], abs(ref[:, :, :, part])
+            worst_max = max(worst_max, float(e.max()) / (2.0 ** -6 * float(r.max()) + 1e-6))
+            worst_mean = max(worst_mean, float(e.mean()) / (2.0 ** -8 * float(r.mean()) + 1e-7))
+        res["parity"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                         "worst_max_over_bar": round(worst_max, 4),
+                         "worst_mean_over_bar": round(worst_mean, 4), "elements": int(err.size),
+                         "ok": bool(worst_max <= 1.0 and worst_mean <= 1.0)}
+    return res
 
 
 def time_steps(torch, step, K: int, warmup: int, stream, launches_per_step: int):
@@ -661,9 +699,16 @@ def bwd_bench(args, torch, np) -> int:
                      "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
                      "mfma_tflops": round(nflops / avg_launch_s / 1e12, 3),
                      "mfma_peak_tflops": BF16_PEAK_TFLOPS},
-        "cpu_baseline": None if args.no_cpu_baseline else
-        bwd_cpu_baseline(args.workload, min(args.cpu_sample_batch, B, 8)),
+        "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        # one more launch (untimed): its dq, dk, dv of the sampled images are
+        # compared with the oracle's
+        sb = min(args.cpu_sample_batch, B, 8)
+        swa.check(swa.swin_wattn_bwd(qs[0], table, gs[0], dqs[0], dt, B, H, W, nh, d, M, s, stream), "bwd")
+        torch.cuda.synchronize()
+        got = dqs[0][:sb].float().cpu().numpy().astype(np.float64).reshape(sb, H, W, 3, nh, d)
+        result["cpu_baseline"] = bwd_cpu_baseline(args.workload, sb, gpu_dqkv=got)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -728,9 +773,17 @@ def i8_bench(args, torch, np) -> int:
                      "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
                      "mfma_tflops": round(nflops / avg_launch_s / 1e12, 3),
                      "mfma_peak_tflops": BF16_PEAK_TFLOPS},
-        "cpu_baseline": None if args.no_cpu_baseline else
-        i8_cpu_baseline(args.workload, min(args.cpu_sample_batch, B)),
+        "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        # one more launch (untimed): its output on the sampled images is
+        # compared with the oracle's
+        sb = min(args.cpu_sample_batch, B)
+        swa.check(swa.swin_wattn_fwd_i8(qs[0], sq, sk, sv, 0.0, table, outs[0], B, H, W, nh, d, M, s,
+                                        stream), "fwd_i8")
+        torch.cuda.synchronize()
+        got = outs[0][:sb].float().cpu().numpy().astype(np.float64)
+        result["cpu_baseline"] = i8_cpu_baseline(args.workload, sb, gpu_out=got)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -847,7 +900,13 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample_batch, B))
+        # one more launch (untimed) with the workload's first shift: its
+        # output on the sampled images is compared with the oracle's
+        sb = min(args.cpu_sample_batch, B)
+        swa.check(swa.swin_wattn_fwd(qs[0], table, outs[0], B, H, W, nh, d, M, shifts[0], stream), "fwd")
+        torch.cuda.synchronize()
+        got = outs[0][:sb].float().cpu().numpy().astype(np.float64)
+        result["cpu_baseline"] = cpu_baseline(args.workload, sb, gpu_out=got)
     print(json.dumps(result), flush=True)
     return 0
 
