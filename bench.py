@@ -296,9 +296,14 @@ def linear_i8_algorithmic(T, K, N, residual, out_i8):
     return T * K + T * N * (1 if out_i8 else 2) + (T * N * 2 if residual else 0), 2 * T * K * N
 
 
-def linear_i8_cpu_baseline(name: str, min_seconds: float = 10.0):
+def linear_i8_cpu_baseline(name: str, min_seconds: float = 10.0, gpu_rows=None):
     """The fp64 oracle of the INT8 linear layer on the first tokens of the
-    workload (grown until one call takes about `min_seconds` / 4)."""
+    workload (grown until one call takes about `min_seconds` / 4).  With
+    `gpu_rows` (n -> the library's first n output rows) the outputs are
+    compared: INT8 codes must be equal (both sides decide them by the same
+    fp32 operations); bf16 output against |y - ref| <= 2^-7 |ref| + 2^-20
+    (sum_c |x_c w_jc| x_scale w_scale_j + |b_j| + |r_j|)."""
+    import numpy as np
     import oracle
     import synth
     w = synth.LINEAR_I8_WORKLOADS[name]
@@ -306,7 +311,7 @@ def linear_i8_cpu_baseline(name: str, min_seconds: float = 10.0):
     while True:
         x, sx, wq, sw, b, r, so = synth.linear_i8_inputs(name, tokens=n)
         t0 = time.perf_counter()
-        _, used = oracle.linear_i8(x, sx, wq, sw, b, residual=r, so=so, return_threads=True)
+        (_, ref, codes), used = oracle.linear_i8(x, sx, wq, sw, b, residual=r, so=so, return_threads=True)
         dt = time.perf_counter() - t0
         if dt >= min_seconds / 4 or n >= w["tokens"]:
             break
@@ -317,10 +322,22 @@ def linear_i8_cpu_baseline(name: str, min_seconds: float = 10.0):
         reps += 1
     dt = time.perf_counter() - t0
     nbytes, _ = linear_i8_algorithmic(n, w["K"], w["N"], w["residual"], w["out_i8"])
-    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle",
-            "sample": f"{name}, first {n} of {w['tokens']} tokens x{reps} ({dt:.1f} s wall, "
-                      f"exact integer sums + fp64, {used} threads)"}
+    res = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+           "kind": "oracle",
+           "sample": f"{name}, first {n} of {w['tokens']} tokens x{reps} ({dt:.1f} s wall, "
+                     f"exact integer sums + fp64, {used} threads)"}
+    if gpu_rows is not None:
+        got = gpu_rows(n)
+        if w["out_i8"]:
+            diff = int(np.count_nonzero(got != codes))
+            res["parity"] = {"codes_differing": diff, "elements": int(codes.size), "ok": diff == 0}
+        else:
+            mag = ((np.abs(x.astype(np.float64)) @ np.abs(wq.astype(np.float64)).T) * (float(sx) * sw)
+                   + np.abs(b.astype(np.float64)))
+            if r is not None:
+                mag = mag + np.abs(synth.bf16_to_f32(r).astype(np.float64))
+            res["parity"] = _bound_parity(got, ref, mag * 2.0 ** -20)
+    return res
 
 
 def linear_i8_bench(args, torch, np) -> int:
@@ -385,8 +402,14 @@ def linear_i8_bench(args, torch, np) -> int:
                      "alg_bytes_per_launch": nbytes, "alg_ops_per_launch": nflops,
                      "mfma_tops": round(nflops / avg_launch_s / 1e12, 3),
                      "mfma_peak_tops": INT8_PEAK_TOPS},
-        "cpu_baseline": None if args.no_cpu_baseline else linear_i8_cpu_baseline(args.workload),
+        "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        step(0)  # one more launch (untimed) on the first buffer set, compared with the oracle
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = linear_i8_cpu_baseline(
+            args.workload, gpu_rows=lambda n: (lambda t: t.cpu().numpy() if t.dtype == torch.int8 else
+                        t.float().cpu().numpy().astype(np.float64))(ys[0][:n]))
     print(json.dumps(result), flush=True)
     return 0
 
@@ -399,9 +422,15 @@ def _linear_workload(name: str):
     return synth.LINEAR_WORKLOADS[name], False
 
 
-def linear_cpu_baseline(name: str, min_seconds: float = 10.0):
+def linear_cpu_baseline(name: str, min_seconds: float = 10.0, gpu_rows=None):
     """The fp64 oracle on the first tokens of the workload (grown until one
-    call takes about `min_seconds`), reported in GB/s of algorithmic bytes."""
+    call takes about `min_seconds`), reported in GB/s of algorithmic bytes.
+    With `gpu_rows` (n -> the library's first n output rows, float64) the
+    oracle's rows are compared with them element by element against the
+    linear layer's bound: |y - ref| <= 2^-7 |ref| + 2^-20 (sum_c |x_c w_jc|
+    + |b_j| + |r_j|); with the layer norm, 2^-7 |ref| + 2^-7 sum_c (|xn_c| +
+    |beta_c|) |w_jc| + 2^-20 |b_j| (gamma o W rounded to bf16)."""
+    import numpy as np
     import oracle
     import synth
     w, ln = _linear_workload(name)
@@ -409,15 +438,16 @@ def linear_cpu_baseline(name: str, min_seconds: float = 10.0):
     def run(n):
         if ln:
             x, g, be, wt, b = synth.ln_linear_inputs(name, tokens=n)
-            return lambda: oracle.linear(oracle.layernorm(x, g, be), wt, b, return_threads=True)
+            return (lambda: oracle.linear(oracle.layernorm(x, g, be), wt, b, return_threads=True),
+                    (x, g, be, wt, b))
         x, wt, b, r = synth.linear_inputs(name, tokens=n)
-        return lambda: oracle.linear(x, wt, b, r, return_threads=True)
+        return lambda: oracle.linear(x, wt, b, r, return_threads=True), (x, wt, b, r)
 
     n = 512
     while True:
-        call = run(n)
+        call, inputs = run(n)
         t0 = time.perf_counter()
-        _, used = call()
+        ref, used = call()
         dt = time.perf_counter() - t0
         if dt >= min_seconds / 4 or n >= w["tokens"]:
             break
@@ -428,10 +458,35 @@ def linear_cpu_baseline(name: str, min_seconds: float = 10.0):
         reps += 1
     dt = time.perf_counter() - t0
     nbytes, _ = linear_algorithmic(n, w["K"], w["N"], w["residual"])
-    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle",
-            "sample": f"{name}, first {n} of {w['tokens']} tokens x{reps} ({dt:.1f} s wall, fp64, "
-                      f"{used} threads)"}
+    res = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": used,
+           "kind": "oracle",
+           "sample": f"{name}, first {n} of {w['tokens']} tokens x{reps} ({dt:.1f} s wall, fp64, "
+                     f"{used} threads)"}
+    if gpu_rows is not None:
+        got = gpu_rows(n)
+        f64 = lambda bits: synth.bf16_to_f32(bits).astype(np.float64)
+        if ln:
+            x, g, be, wt, b = inputs
+            xn = oracle.layernorm(x, g, be)
+            extra = ((np.abs(xn) + np.abs(be.astype(np.float64))) @ np.abs(f64(wt)).T * 2.0 ** -7
+                     + np.abs(b.astype(np.float64)) * 2.0 ** -20)
+        else:
+            x, wt, b, r = inputs
+            mag = np.abs(f64(x)) @ np.abs(f64(wt)).T + np.abs(b.astype(np.float64))
+            if r is not None:
+                mag = mag + np.abs(f64(r))
+            extra = mag * 2.0 ** -20
+        res["parity"] = _bound_parity(got, ref, extra)
+    return res
+
+
+def _bound_parity(got, ref, extra):
+    """Element-by-element comparison against the per-element bound
+    2^-7 |ref| + extra: the worst ratio of error to bound, <= 1 passes."""
+    err = abs(got - ref)
+    worst = float((err / (2.0 ** -7 * abs(ref) + extra)).max())
+    return {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+            "worst_err_over_bound": round(worst, 4), "elements": int(err.size), "ok": bool(worst <= 1.0)}
 
 
 def linear_bench(args, torch, np) -> int:
@@ -505,8 +560,14 @@ def linear_bench(args, torch, np) -> int:
                      "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": nflops,
                      "mfma_tflops": round(nflops / avg_launch_s / 1e12, 3),
                      "mfma_peak_tflops": BF16_PEAK_TFLOPS},
-        "cpu_baseline": None if args.no_cpu_baseline else linear_cpu_baseline(args.workload),
+        "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        step(0)  # one more launch (untimed) on the first buffer set, compared with the oracle
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = linear_cpu_baseline(
+            args.workload, gpu_rows=lambda n: (lambda t: t.cpu().numpy() if t.dtype == torch.int8 else
+                        t.float().cpu().numpy().astype(np.float64))(ys[0][:n]))
     print(json.dumps(result), flush=True)
     return 0
 
@@ -520,9 +581,11 @@ def ln_attn_algorithmic(B, H, W, heads, head_dim, window):
     return 4 * C * T, 2 * T * C * 3 * C + 4 * window * window * C * T
 
 
-def ln_attn_cpu_baseline(name: str, min_seconds: float = 10.0, max_reps: int = 50):
+def ln_attn_cpu_baseline(name: str, min_seconds: float = 10.0, max_reps: int = 50, gpu_out=None):
     """The fp64 oracle chain (layer norm, linear, attention) on the first
-    images of the workload, repeated for about `min_seconds`."""
+    images of the workload, repeated for about `min_seconds`.  With `gpu_out`
+    (the library's output of those images, float64) compared as
+    cpu_baseline does."""
     import oracle
     import synth
     spec = synth.LN_ATTN_WORKLOADS[name]
@@ -531,19 +594,22 @@ def ln_attn_cpu_baseline(name: str, min_seconds: float = 10.0, max_reps: int = 5
     nb = 2
     x, g, be, w, b, t = synth.ln_attn_inputs(name, batch=nb)
     B, H, W, C = x.shape
-    reps, cores = 0, 0
+    reps, cores, ref = 0, 0, None
     t0 = time.perf_counter()
     while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
         xn = oracle.layernorm(x, g, be)
         qkv, cores = oracle.linear(xn, w, b, return_threads=True)
-        oracle.swin_wattn_fwd(qkv.reshape(B, H, W, 3, C // 32, 32), t, M, s)
+        ref = oracle.swin_wattn_fwd(qkv.reshape(B, H, W, 3, C // 32, 32), t, M, s)
         reps += 1
     dt = time.perf_counter() - t0
     nbytes, _ = ln_attn_algorithmic(nb, H, W, C // 32, 32, M)
-    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{name}, first {nb} of {a['B']} images, layer norm + linear + attention "
-                      f"x{reps} ({dt:.1f} s wall, fp64, {cores} threads)"}
+    res = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"{name}, first {nb} of {a['B']} images, layer norm + linear + attention "
+                     f"x{reps} ({dt:.1f} s wall, fp64, {cores} threads)"}
+    if gpu_out is not None:
+        res["parity"] = _parity(gpu_out[:nb], ref)
+    return res
 
 
 def ln_attn_bench(args, torch, np) -> int:
@@ -632,8 +698,13 @@ def ln_attn_bench(args, torch, np) -> int:
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "two_kernel_chain_us": round(chain_ms / K * 1e3, 3),
         "roofline": roof,
-        "cpu_baseline": None if args.no_cpu_baseline else ln_attn_cpu_baseline(args.workload),
+        "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        step(0)  # one more launch (untimed) of the fused call, compared with the oracle chain
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = ln_attn_cpu_baseline(
+            args.workload, gpu_out=outs[0][:2].float().cpu().numpy().astype(np.float64))
     print(json.dumps(result), flush=True)
     return 0
 
