@@ -262,6 +262,20 @@ def test_uniform_attention_shifted_is_region_mean(oracle_lib):
             assert np.max(np.abs(out[y, x] - mean)) < 1e-12
 
 
+def test_region_labels_hand_worked(oracle_lib):
+    # labels of the shifted frame, worked out by hand from the band rule
+    # (per axis [0, L-M), [L-M, L-s), [L-s, L); label = 3 band_y + band_x):
+    # 4x4 image, window 2, shift 1 (the frame of the region-mean test), and a
+    # 6-row, 4-column image, window 2, shift 1, where the rows' bands are
+    # 0 0 0 0 1 2 and the columns' 0 0 1 2
+    square = np.array([[0, 0, 1, 2], [0, 0, 1, 2], [3, 3, 4, 5], [6, 6, 7, 8]])
+    tall = np.array([[0, 0, 1, 2]] * 4 + [[3, 3, 4, 5], [6, 6, 7, 8]])
+    assert np.array_equal(oracle.region_labels(4, 4, 2, 1), square)
+    assert np.array_equal(oracle.region_labels(6, 4, 2, 1), tall)
+    # no shift: one region
+    assert not oracle.region_labels(6, 4, 2, 0).any()
+
+
 def test_one_hot_bias_sign(oracle_lib):
     # bias +50 only for offset (dy, dx) = (+1, 0) (query one row below the key):
     # every query not in its window's first row copies the value one row above

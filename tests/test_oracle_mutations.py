@@ -1,10 +1,11 @@
 """The oracle's pins catch plausible mistakes.
 
 Each case plants one mistake in a temporary copy of oracle/swin_oracle.c (a
-reversed shift, a flipped relative index, a dropped scale or mask, a
-transposed operand, a wrong rounding rule, ...), builds it with gcc, and
-runs tests/test_oracle.py against the mutant (SWIN_ORACLE_LIB names the
-build): the pins must fail.  The mistakes are planted on the CPU only; the
+reversed shift or unshift, a flipped relative index, a dropped or wrong
+scale, mask, bias, residual or epsilon, a transposed operand or index map, a
+wrong rounding rule, a backward term from the wrong matrix, ...), builds
+it with gcc, and runs tests/test_oracle.py against the mutant
+(SWIN_ORACLE_LIB names the build): the pins must fail.  The mistakes are planted on the CPU only; the
 oracle itself is untouched.  Each snippet must occur exactly once in the
 oracle source, so a change of the oracle that moves a snippet fails here
 loudly instead of testing nothing."""
@@ -62,6 +63,39 @@ MUTATIONS = {
     "backward dS with the sign flipped":
         ("dP[i * N + j] = S[i * N + j] * (dP[i * N + j] - Dr[i]);",
          "dP[i * N + j] = S[i * N + j] * (Dr[i] - dP[i * N + j]);"),
+    "unshift rolled the same way as the shift":
+        ("oracle_roll(o, B, H, W, (int)C, s, s, out);", "oracle_roll(o, B, H, W, (int)C, -s, -s, out);"),
+    "window reverse in column-major order":
+        ("            long n = (b * nWy + wy) * nWx + wx, t = ty * M + tx;\n"
+         "            double* dst = x + ((b * H + wy * M + ty) * W + wx * M + tx) * (long)C;",
+         "            long n = (b * nWy + wy) * nWx + wx, t = tx * M + ty;\n"
+         "            double* dst = x + ((b * H + wy * M + ty) * W + wx * M + tx) * (long)C;"),
+    "score scale 1/d instead of 1/sqrt(d)":
+        ("  const double scale = 1.0 / sqrt((double)d);\n  const double* base",
+         "  const double scale = 1.0 / (double)d;\n  const double* base"),
+    "padded keys scored 0 instead of -inf":
+        ("          S[i * Np + j] = -INFINITY;", "          S[i * Np + j] = 0.0;"),
+    "region label axes swapped":
+        ("3 * band(y, H, M, s) + band(x, W, M, s)", "3 * band(x, W, M, s) + band(y, H, M, s)"),
+    "linear residual dropped":
+        ("      if (J->r) acc += load_elem(J->r, J->rdtype, t * J->N + j);\n", ""),
+    "layer norm without eps":
+        ("    const double r = 1.0 / sqrt(var + eps);", "    const double r = 1.0 / sqrt(var);"),
+    "layer norm without beta":
+        (" * (double)gamma[c] + (double)beta[c];", " * (double)gamma[c];"),
+    "backward dV from P untransposed":
+        ("            av += S[u * N + t] * G_(u, e);", "            av += S[t * N + u] * G_(u, e);"),
+    "backward D without P":
+        ("          Di += S[i * N + j] * acc;", "          Di += acc;"),
+    "backward dQ without the scale":
+        ("          dx[(long)t * 3 * C + h * d + e] = aq * scale;",
+         "          dx[(long)t * 3 * C + h * d + e] = aq;"),
+    "backward bias gradient from P instead of dS":
+        ("          J->dtable[(long)J->rel[i * N + j] * nh + h] += dP[i * N + j];",
+         "          J->dtable[(long)J->rel[i * N + j] * nh + h] += S[i * N + j];"),
+    "int8 linear bias not divided by the output scale":
+        ("const float shift = (J->bias ? J->bias[j] : 0.0f) / J->so[j];",
+         "const float shift = (J->bias ? J->bias[j] : 0.0f);"),
 }
 
 
